@@ -1,0 +1,347 @@
+"""Generators for the five workloads (Tiny, lockstep B=16, B=128, long context, multi-query).
+
+Recipe common to every paged case (``numpy.random.default_rng(seed)``; draws in this order):
+  1. context lengths n_b (tokens cached before the step), unless fixed;
+  2. the physical block order ``rng.permutation(num_blocks)``; rows take blocks in logical order,
+     the last id of the permutation is the poison block (NaN-filled, never handed out) and every
+     unused block-table entry points at it;
+  3. history keys/values per row, ``standard_normal`` fp32 rounded to the storage dtype, stored at
+     the row's token slots; every other slot of the pool holds NaN;
+  4. the step's query, new key and new value, N(0, 1) in the same way.
+The step appends at position n_b (kv_len = n_b + 1 afterwards) and then attends.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from paged_kv_cache_177_amd.blocks import BLOCK_SIZE
+
+POISON_F32 = np.uint32(0x7FC00000)
+POISON_BF16 = np.uint16(0x7FC0)
+
+
+def poison_value(dtype: str):
+    return np.float32(np.nan) if dtype == "f32" else POISON_BF16
+
+
+def storage_np_dtype(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+def to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 draws -> storage dtype (bf16 through torch's CPU round-to-nearest-even conversion)."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "f32":
+        return x32
+    t = torch.from_numpy(x32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def fp32_scale(head_dim: int) -> float:
+    """Softmax scale handed to both sides: 1/sqrt(D) rounded to fp32."""
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+@dataclass
+class PagedCase:
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    poison_block: int
+    rope_theta: float            # 0.0 means no RoPE table
+    rope_max_pos: int
+    n_ctx: np.ndarray            # int32[B] tokens cached before the step
+    positions: np.ndarray        # int32[B] RoPE position of the step's token (= n_ctx)
+    dest: np.ndarray             # int32[B] token index the step's K/V is written to (= n_ctx)
+    kv_lens: np.ndarray          # int32[B] valid tokens after the append (= n_ctx + 1)
+    block_tables: np.ndarray     # int32[B][bt_stride]
+    k_pool: np.ndarray           # [num_blocks][H_kv][16][D] storage, before the append
+    v_pool: np.ndarray
+    k_new: np.ndarray            # [B][H_kv][D] storage (pre-RoPE key)
+    v_new: np.ndarray
+    q: np.ndarray                # [B][H_q][D] storage (pre-RoPE when there is a table)
+    scale: float
+    seed: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return len(self.kv_lens)
+
+    @property
+    def bt_stride(self) -> int:
+        return self.block_tables.shape[1]
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.kv_lens.max(initial=0))
+
+    def kv_bytes(self) -> int:
+        """K and V bytes one decode step reads: sum(kv_len) * H_kv * D * 2 * sizeof(storage)."""
+        el = 4 if self.dtype == "f32" else 2
+        return int(self.kv_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * el
+
+
+def make_paged_case(name, seed, n_ctx, num_q_heads, num_kv_heads, head_dim, dtype,
+                    rope_theta=0.0, rope_max_pos=None, num_blocks=None, pool_factor=1.25,
+                    rng=None, bt_stride=None) -> PagedCase:
+    """Build one append-then-decode step over a shuffled paged pool (see the module recipe)."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    n_ctx = np.asarray(n_ctx, dtype=np.int32)
+    B = len(n_ctx)
+    kv_lens = n_ctx + 1
+    nblk = (kv_lens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    needed = int(nblk.sum())
+    if num_blocks is None:
+        num_blocks = int(math.ceil(pool_factor * needed)) + 1
+    if num_blocks < needed + 1:
+        raise ValueError("pool too small for the case plus its poison block")
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    poison = int(perm[-1])
+    stride = int(bt_stride if bt_stride is not None else max(1, int(nblk.max(initial=1))))
+    bt = np.full((B, stride), poison, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    sd = storage_np_dtype(dtype)
+    shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
+    k_pool = np.full(shape, poison_value(dtype), dtype=sd)
+    v_pool = np.full(shape, poison_value(dtype), dtype=sd)
+    for b in range(B):
+        n = int(n_ctx[b])
+        kh = to_storage(rng.standard_normal((n, num_kv_heads, head_dim), dtype=np.float32), dtype)
+        vh = to_storage(rng.standard_normal((n, num_kv_heads, head_dim), dtype=np.float32), dtype)
+        t = np.arange(n)
+        blk = bt[b, t // BLOCK_SIZE]
+        k_pool[blk, :, t % BLOCK_SIZE, :] = kh
+        v_pool[blk, :, t % BLOCK_SIZE, :] = vh
+    q = to_storage(rng.standard_normal((B, num_q_heads, head_dim), dtype=np.float32), dtype)
+    k_new = to_storage(rng.standard_normal((B, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    v_new = to_storage(rng.standard_normal((B, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    if rope_max_pos is None:
+        rope_max_pos = int(kv_lens.max(initial=1)) if rope_theta else 0
+    return PagedCase(name=name, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                     head_dim=head_dim, num_blocks=num_blocks, poison_block=poison,
+                     rope_theta=float(rope_theta), rope_max_pos=int(rope_max_pos), n_ctx=n_ctx,
+                     positions=n_ctx.copy(), dest=n_ctx.copy(), kv_lens=kv_lens.astype(np.int32),
+                     block_tables=bt, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
+                     q=q, scale=fp32_scale(head_dim), seed=seed)
+
+
+# --------------------------------------------------------------------------------------------
+# The workloads
+# --------------------------------------------------------------------------------------------
+def tiny(reading: str = "A", seed: int = 0) -> PagedCase:
+    """B=3, 4 query / 2 KV heads, D=64, fp32, 16-block shuffled pool, RoPE theta=1e4.
+
+    Reading "A": the context lengths 5, 17, 33 are the tokens cached before the step (kv_len 6, 18,
+    34 afterwards). Reading "B": they already count the step's token (kv_len 5, 17, 33)."""
+    n = [5, 17, 33] if reading == "A" else [4, 16, 32]
+    return make_paged_case(f"tiny-{reading}", seed, n, 4, 2, 64, "f32", rope_theta=1e4,
+                           num_blocks=16)
+
+
+def tiny_edges(seed: int = 0, dtype: str = "f32") -> PagedCase:
+    """Tiny geometry with contexts on the block edges: 0, 1, 15, 16, 31, 32."""
+    return make_paged_case(f"tiny-edges-{dtype}", seed, [0, 1, 15, 16, 31, 32], 4, 2, 64, dtype,
+                           rope_theta=1e4, num_blocks=16)
+
+
+def b128(seed: int = 2) -> PagedCase:
+    """B=128 throughput step: contexts uniform in [512, 8192], 32 query / 8 KV heads, D=64, bf16,
+    shuffled pool sized 1.25x the needed blocks, no RoPE table (q and k are post-RoPE draws)."""
+    rng = np.random.default_rng(seed)
+    n = rng.integers(512, 8192, 128, endpoint=True)
+    return make_paged_case("b128", seed, n, 32, 8, 64, "bf16", rng=rng)
+
+
+def long_context(seed: int = 3) -> PagedCase:
+    """B=4 long rows: contexts uniform in [32768, 131072], 32 query / 8 KV heads, D=128, bf16."""
+    rng = np.random.default_rng(seed)
+    n = rng.integers(32768, 131072, 4, endpoint=True)
+    return make_paged_case("long", seed, n, 32, 8, 128, "bf16", rng=rng)
+
+
+# --------------------------------------------------------------------------------------------
+# Lockstep B=16 protocol
+# --------------------------------------------------------------------------------------------
+@dataclass
+class LockstepPlan:
+    """32 lockstep decode steps over 16 rows; at ``join_step`` two rows leave and two new sequences
+    (ids 16, 17) take their slots. Per-step draws come from ``default_rng([seed, seq_id, step])``
+    and histories from ``default_rng([seed, seq_id, 10**6])``, so a row's inputs do not depend on
+    which other rows share its batch."""
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    rope_theta: float
+    steps: int
+    join_step: int
+    n_ctx0: np.ndarray           # contexts of sequences 0..15 (slot b holds sequence b at start)
+    leave_slots: np.ndarray      # two slots whose sequences leave at join_step
+    join_ctx: np.ndarray         # contexts of the joining sequences 16, 17
+    num_blocks: int
+    perm: np.ndarray             # physical block order
+    rope_max_pos: int
+
+    @property
+    def scale(self) -> float:
+        return fp32_scale(self.head_dim)
+
+    def seq_ctx(self, seq_id: int) -> int:
+        return int(self.n_ctx0[seq_id]) if seq_id < 16 else int(self.join_ctx[seq_id - 16])
+
+    def history(self, seq_id: int):
+        """(K, V) history of a sequence, each (n, H_kv, D) in storage dtype (post-RoPE draws)."""
+        rng = np.random.default_rng([self.seed, seq_id, 10**6])
+        n = self.seq_ctx(seq_id)
+        shape = (n, self.num_kv_heads, self.head_dim)
+        k = to_storage(rng.standard_normal(shape, dtype=np.float32), self.dtype)
+        v = to_storage(rng.standard_normal(shape, dtype=np.float32), self.dtype)
+        return k, v
+
+    def step_inputs(self, seq_id: int, step: int):
+        """(q (H_q, D), k (H_kv, D), v (H_kv, D)) of one sequence at one step, pre-RoPE q and k."""
+        rng = np.random.default_rng([self.seed, seq_id, step])
+        q = to_storage(rng.standard_normal((self.num_q_heads, self.head_dim), dtype=np.float32),
+                       self.dtype)
+        k = to_storage(rng.standard_normal((self.num_kv_heads, self.head_dim), dtype=np.float32),
+                       self.dtype)
+        v = to_storage(rng.standard_normal((self.num_kv_heads, self.head_dim), dtype=np.float32),
+                       self.dtype)
+        return q, k, v
+
+    def schedule(self):
+        """Per step: the list of (slot, seq_id, position) of the 16 active rows."""
+        out = []
+        seqs = list(range(16))
+        joins = [16, 17]
+        for s in range(self.steps):
+            if s == self.join_step:
+                for slot, sid in zip(sorted(self.leave_slots.tolist()), joins):
+                    seqs[slot] = sid
+            rows = []
+            for slot, sid in enumerate(seqs):
+                start = 0 if sid < 16 else self.join_step
+                rows.append((slot, sid, self.seq_ctx(sid) + (s - start)))
+            out.append(rows)
+        return out
+
+
+def b16_plan(seed: int = 1, steps: int = 32, join_step: int = 16) -> LockstepPlan:
+    """B=16 ragged lockstep decode: contexts uniform in [64, 2048], 32 query / 8 KV heads, D=64,
+    bf16, RoPE theta=1e6, shuffled pool sized 1.25x the blocks every sequence needs over the run."""
+    rng = np.random.default_rng(seed)
+    n0 = rng.integers(64, 2048, 16, endpoint=True).astype(np.int32)
+    join_ctx = rng.integers(64, 2048, 2, endpoint=True).astype(np.int32)
+    leave = np.sort(rng.choice(16, 2, replace=False)).astype(np.int32)
+    final = []
+    for sid in range(16):
+        runs = join_step if sid in leave.tolist() else steps
+        final.append(int(n0[sid]) + runs)
+    for j in range(2):
+        final.append(int(join_ctx[j]) + steps - join_step)
+    needed = sum((f + BLOCK_SIZE - 1) // BLOCK_SIZE for f in final)
+    nb = int(math.ceil(1.25 * needed)) + 1
+    perm = rng.permutation(nb).astype(np.int32)
+    return LockstepPlan(seed=seed, num_q_heads=32, num_kv_heads=8, head_dim=64, dtype="bf16",
+                        rope_theta=1e6, steps=steps, join_step=join_step, n_ctx0=n0,
+                        leave_slots=leave, join_ctx=join_ctx, num_blocks=nb, perm=perm,
+                        rope_max_pos=max(final) + 1)
+
+
+# --------------------------------------------------------------------------------------------
+# Multi-query ragged cross-attention (Perceiver-style)
+# --------------------------------------------------------------------------------------------
+@dataclass
+class MQCase:
+    name: str
+    dtype: str
+    num_heads: int
+    head_dim: int
+    n_q: int
+    num_blocks: int
+    poison_block: int
+    kv_lens: np.ndarray          # int32[B] spike tokens per sample
+    block_tables: np.ndarray
+    k_pool: np.ndarray           # [num_blocks][H][16][dh] storage
+    v_pool: np.ndarray
+    q: np.ndarray                # [n_q][H][dh] storage, shared by every sample
+    scale: float
+    seed: int = 0
+
+    @property
+    def batch(self) -> int:
+        return len(self.kv_lens)
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.kv_lens.max(initial=0))
+
+
+def mq(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 137,
+       n_bins: int = 120, rate: float = 0.05, model_dim: int = 256, num_heads: int = 8,
+       q_gain: float = 1.0, kv_gain: float = 1.0) -> MQCase:
+    """Perceiver-style cross-attention inputs.
+
+    Spike counts c ~ Poisson(rate) per (neuron, time bin) cell; every spike is one token
+    (neuron, bin, value = min(c, 4)), tokens ordered by bin then neuron, E_b = sum of counts.
+    Token embedding = n_emb[neuron] + t_emb[bin] + v_emb[value - 1] with N(0, 0.02) tables; keys and
+    values are that embedding times N(0, 1/model_dim) projections, split into heads of
+    model_dim / num_heads. The latent queries (N(0, 0.02), projected the same way) are shared by
+    all samples. ``q_gain``/``kv_gain`` scale the projected queries/keys (1.0 is the workload;
+    larger values sharpen the softmax for stress tests)."""
+    rng = np.random.default_rng(seed)
+    counts = rng.poisson(rate, (batch, n_neurons, n_bins))
+    n_emb = rng.normal(0.0, 0.02, (n_neurons, model_dim)).astype(np.float32)
+    t_emb = rng.normal(0.0, 0.02, (n_bins, model_dim)).astype(np.float32)
+    v_emb = rng.normal(0.0, 0.02, (4, model_dim)).astype(np.float32)
+    w_q = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    w_k = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    w_v = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    latents = rng.normal(0.0, 0.02, (n_latents, model_dim)).astype(np.float32)
+    dh = model_dim // num_heads
+    dtype = "bf16"
+    q = to_storage((q_gain * (latents @ w_q)).reshape(n_latents, num_heads, dh), dtype)
+
+    kv_lens = counts.reshape(batch, -1).sum(axis=1).astype(np.int32)
+    nblk = (kv_lens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    num_blocks = int(math.ceil(1.25 * int(nblk.sum()))) + 1
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    poison = int(perm[-1])
+    stride = max(1, int(nblk.max(initial=1)))
+    bt = np.full((batch, stride), poison, dtype=np.int32)
+    shape = (num_blocks, num_heads, BLOCK_SIZE, dh)
+    k_pool = np.full(shape, POISON_BF16, dtype=np.uint16)
+    v_pool = np.full(shape, POISON_BF16, dtype=np.uint16)
+    off = 0
+    for b in range(batch):
+        bt[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+        c = counts[b].T  # (bins, neurons): order tokens by bin, then neuron
+        bins, neurons = np.nonzero(c)
+        reps = c[bins, neurons]
+        bins = np.repeat(bins, reps)
+        neurons = np.repeat(neurons, reps)
+        vals = np.minimum(np.repeat(reps, reps), 4)
+        x = n_emb[neurons] + t_emb[bins] + v_emb[vals - 1]
+        kk = to_storage((kv_gain * (x @ w_k)).reshape(-1, num_heads, dh), dtype)
+        vv = to_storage((x @ w_v).reshape(-1, num_heads, dh), dtype)
+        t = np.arange(len(x))
+        blk = bt[b, t // BLOCK_SIZE]
+        k_pool[blk, :, t % BLOCK_SIZE, :] = kk
+        v_pool[blk, :, t % BLOCK_SIZE, :] = vv
+    return MQCase(name="mq", dtype=dtype, num_heads=num_heads, head_dim=dh, n_q=n_latents,
+                  num_blocks=num_blocks, poison_block=poison, kv_lens=kv_lens, block_tables=bt,
+                  k_pool=k_pool, v_pool=v_pool, q=q, scale=fp32_scale(dh), seed=seed)
