@@ -1,0 +1,166 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged decode-attention library (libpa.so).
+ *
+ * The operations, and the passages of the pages they follow:
+ *   - a pre-allocated pool of fixed 16-token K/V blocks, reached through per-sequence block tables
+ *     ("NeuroGrid releases", v0.7.0 "Paged KV Cache"; "cortex-engine write-up", serving section:
+ *     a pre-allocated page pool with a fixed page size);
+ *   - appending each row's new key and value at its own position, the key rotated (RoPE,
+ *     rotate-half) at that row's logical position before it is stored ("helexa PR #121", commit
+ *     "slice 1": per-row RoPE positions; keys stored post-RoPE, so padding is position-inert);
+ *   - batched single-token decode attention over the paged cache with GQA and an online softmax
+ *     ("NeuroGrid releases", v0.7.0 and v0.6.0 "Flash Decode Attention Kernel"); with several
+ *     queries per row it is the ragged multi-query cross-attention of the "cortex-engine
+ *     write-up", kernels section (block-sparse cross-attention);
+ *   - the lockstep form over right-padded per-row KV with one padding gap per row
+ *     ("helexa PR #121", commit "slice 1": assemble_batch, batch_decode_mask).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns every buffer; the library
+ *     allocates nothing, keeps no global state and never synchronises (except pa_alloc_pool, which
+ *     waits for its own table upload). Work is enqueued on `stream` and returns at once.
+ *   - Validation of host-side arguments happens before any HIP call; a failed check returns an
+ *     error code and launches nothing. A failed launch returns PA_ERR_HIP. No C++ exception
+ *     crosses the ABI.
+ *   - Device-side contents (lengths, positions, block ids) are preconditions and are not checked
+ *     for errors; to keep every access inside the caller's buffers the kernels clamp them (see each
+ *     call), which can only turn a broken precondition into a wrong result, never a fault.
+ *   - Scores and outputs are computed in fp32. `out` is fp32; `lse` is the natural-log
+ *     log-sum-exp of the scaled scores. A row with no valid key yields out = 0 and lse = -inf.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* inconsistent sizes (negative, not divisible, bound too large, ...) */
+  PA_ERR_UNSUPPORTED = 3, /* a valid but unsupported configuration (dtype, head_dim, block size) */
+  PA_ERR_CAPACITY = 4,    /* a caller buffer (pool buffer, workspace) is too small */
+  PA_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum { PA_PAGED = 0, PA_PADDED = 1 } pa_layout;
+
+/* (host) Shape of a pool. */
+typedef struct {
+  int32_t layout;        /* pa_layout */
+  int32_t dtype;         /* pa_dtype: storage type of K, V and of the queries used with the pool */
+  int32_t num_kv_heads;  /* H_kv >= 1 */
+  int32_t head_dim;      /* D in {32, 64, 128} */
+  int32_t block_size;    /* must be 16 */
+  int32_t num_blocks;    /* PA_PAGED: physical blocks (>= 1); ignored for PA_PADDED */
+  int32_t batch_cap;     /* PA_PADDED: rows; ignored for PA_PAGED */
+  int32_t seq_cap;       /* PA_PADDED: columns per row; ignored for PA_PAGED */
+  int32_t rope_max_pos;  /* rows of the RoPE tables; 0 = no RoPE (keys and queries stored as given) */
+  double rope_theta;     /* RoPE base theta (> 0 when rope_max_pos > 0) */
+} pa_pool_desc;
+
+/* (host) Plain view of a pool carved from caller memory; needs no destructor.
+ *   PA_PAGED : k, v are [num_blocks][H_kv][16][D]; token t of a row with block table bt lives at
+ *              block bt[t / 16], slot t % 16.
+ *   PA_PADDED: k, v are [batch_cap][H_kv][seq_cap][D]; row b's column c lives at [b][.][c].
+ *   rope_cos, rope_sin: [rope_max_pos][D / 2] fp32, or NULL without RoPE. */
+typedef struct {
+  pa_pool_desc desc;
+  void* k;
+  void* v;
+  float* rope_cos;
+  float* rope_sin;
+  size_t bytes; /* bytes of dev_buf the pool occupies */
+} pa_pool;
+
+/* Carve a pool out of one caller-owned device buffer, and fill its RoPE tables.
+ *
+ * Size query: with dev_buf == NULL, writes the bytes needed to *bytes_needed and returns PA_OK.
+ * Otherwise dev_buf (256-byte aligned, dev_buf_bytes long) is split into K, V and the two tables,
+ * *out is filled, and the tables are uploaded on `stream`, which the call then synchronises.
+ * Table entry [p][i] is cos/sin(p * theta^(-2i/D)), evaluated in fp64 on the host and rounded once
+ * to fp32. K/V contents are left as they are (the caller fills or poisons them).
+ * Errors: NULL desc / out / bytes_needed -> PA_ERR_NULL; block_size != 16, head_dim not in
+ * {32, 64, 128}, unknown dtype or layout -> PA_ERR_UNSUPPORTED; non-positive sizes or theta with a
+ * table -> PA_ERR_SHAPE; dev_buf_bytes too small or dev_buf misaligned -> PA_ERR_CAPACITY. */
+pa_status pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size_t dev_buf_bytes,
+                        size_t* bytes_needed /* host */, pa_pool* out /* host */,
+                        hipStream_t stream);
+
+/* Append one token per row.
+ *
+ * Row b (b < batch): the key k_new[b] ([H_kv][D], pool dtype) is rotated at position positions[b]
+ * when the pool has RoPE tables -- rotate-half, pairs (i, i + D/2):
+ *   r[i] = x[i]*c[i] - x[i+D/2]*s[i],  r[i+D/2] = x[i+D/2]*c[i] + x[i]*s[i]
+ * with every product and sum a separate round-to-nearest fp32 operation -- then rounded to the pool
+ * dtype (round-to-nearest-even) and written with v_new[b] (copied unchanged) at token index dest[b]:
+ * PA_PAGED block block_tables[b * bt_stride + dest[b] / 16], slot dest[b] % 16; PA_PADDED row b,
+ * column dest[b]. dest == NULL means dest = positions. q_in/q_out ([batch][num_q_heads][D], pool
+ * dtype; both NULL or both set) rotate the queries at the same positions (copied when the pool has
+ * no tables). Results are bit-exact and independent of the launch geometry.
+ * Preconditions (clamped, not checked): 0 <= positions[b] < rope_max_pos, dest[b] inside the row
+ * (< bt_stride*16, or < seq_cap), block ids < num_blocks, b < batch_cap for PA_PADDED.
+ * Errors: PA_ERR_NULL for a missing pointer (block_tables is required for PA_PAGED, positions
+ * always); PA_ERR_SHAPE for batch < 0, bt_stride < 1, num_q_heads not a positive multiple of H_kv,
+ * batch > batch_cap (PA_PADDED). batch == 0 is a no-op. */
+pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* positions, const int32_t* dest, const void* k_new,
+                       const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
+                       int32_t batch, hipStream_t stream);
+
+/* Paged decode attention.
+ *
+ * q: [batch][n_q][num_q_heads][D] in the pool dtype; row b starts at element b * q_row_stride
+ * (q_row_stride = 0 shares one [n_q][H_q][D] block of queries between all rows). Query head h reads
+ * KV head h / G, G = num_q_heads / H_kv. Row b attends over its first kv_lens[b] tokens, gathered
+ * through block_tables[b * bt_stride ...]; score = scale * <q, k>; exact softmax, computed online.
+ * out: [batch][n_q][num_q_heads][D] fp32. lse: [batch][n_q][num_q_heads] fp32 or NULL.
+ * n_q == 1 is the decode path (vector units; one workgroup per (row, KV head, split); long rows are
+ * split into chunks whose partial results a second kernel merges by log-sum-exp). n_q > 1 is the
+ * multi-query path (matrix cores). The split of a row depends on its own kv_len only, so a row's
+ * result does not depend on the rest of the batch.
+ * Workspace: with workspace_needed != NULL the call only writes the bytes it needs for these
+ * arguments there and launches nothing; otherwise workspace must hold that many bytes (it may be
+ * NULL when none are needed). max_kv_len is a host upper bound of kv_lens (<= bt_stride * 16).
+ * Preconditions (clamped, not checked): 0 <= kv_lens[b] <= max_kv_len; block ids < num_blocks.
+ * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0, n_q < 1,
+ * num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, layout not
+ * PA_PAGED); PA_ERR_UNSUPPORTED (n_q == 1 with G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace
+ * too small). batch == 0 is a no-op. */
+pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
+                              int32_t n_q, int32_t num_q_heads, const int32_t* block_tables,
+                              int32_t bt_stride, const int32_t* kv_lens, int32_t batch,
+                              int32_t max_kv_len, float scale, void* workspace,
+                              size_t workspace_bytes, size_t* workspace_needed /* host */,
+                              float* out, float* lse, hipStream_t stream);
+
+/* Lockstep decode over right-padded KV (PA_PADDED pool).
+ *
+ * q: [batch][num_q_heads][D] in the pool dtype. Row b's valid columns are
+ * [0, gap_start[b]) and [gap_end[b], kv_cols); the gap in between is skipped (never read), which
+ * equals an additive -inf mask on it. gap_start == gap_end means no gap. out/lse as for
+ * pa_decode_attention; the same split rule applies to the row's count of valid columns.
+ * Workspace as for pa_decode_attention.
+ * Preconditions (clamped, not checked): 0 <= gap_start[b] <= gap_end[b] <= kv_cols.
+ * Errors: PA_ERR_NULL (pool, q, gap_start, gap_end, out); PA_ERR_SHAPE (batch < 0 or > batch_cap,
+ * kv_cols < 0 or > seq_cap, num_q_heads not a positive multiple of H_kv, layout not PA_PADDED);
+ * PA_ERR_UNSUPPORTED (G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace too small). */
+pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
+                                     int32_t num_q_heads, int32_t batch, const int32_t* gap_start,
+                                     const int32_t* gap_end, int32_t kv_cols, float scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     size_t* workspace_needed /* host */, float* out, float* lse,
+                                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,281 @@
+// C-ABI layer of libpa.so: host-side validation, pool carving, RoPE tables, launch dispatch.
+// Every check runs before the first HIP call, so the error paths work without a GPU.
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int elem_size(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+pa_status check_desc(const pa_pool_desc* d) {
+  if (d == nullptr) return PA_ERR_NULL;
+  if (d->layout != PA_PAGED && d->layout != PA_PADDED) return PA_ERR_UNSUPPORTED;
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (d->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->num_kv_heads < 1) return PA_ERR_SHAPE;
+  if (d->layout == PA_PAGED && d->num_blocks < 1) return PA_ERR_SHAPE;
+  if (d->layout == PA_PADDED && (d->batch_cap < 1 || d->seq_cap < 1)) return PA_ERR_SHAPE;
+  if (d->rope_max_pos < 0) return PA_ERR_SHAPE;
+  if (d->rope_max_pos > 0 && !(d->rope_theta > 0.0)) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+size_t kv_bytes(const pa_pool_desc* d) {
+  const size_t per_token = (size_t)d->num_kv_heads * (size_t)d->head_dim * elem_size(d->dtype);
+  const size_t tokens = d->layout == PA_PAGED ? (size_t)d->num_blocks * pa::kBlock
+                                              : (size_t)d->batch_cap * (size_t)d->seq_cap;
+  return align256(tokens * per_token);
+}
+
+size_t table_bytes(const pa_pool_desc* d) {
+  return align256((size_t)d->rope_max_pos * (size_t)(d->head_dim / 2) * sizeof(float));
+}
+
+// A pool handed back by the caller must still describe a consistent, carved pool.
+pa_status check_pool(const pa_pool* p) {
+  if (p == nullptr) return PA_ERR_NULL;
+  pa_status s = check_desc(&p->desc);
+  if (s != PA_OK) return s;
+  if (p->k == nullptr || p->v == nullptr) return PA_ERR_NULL;
+  if (p->desc.rope_max_pos > 0 && (p->rope_cos == nullptr || p->rope_sin == nullptr))
+    return PA_ERR_NULL;
+  return PA_OK;
+}
+
+// q rows must keep the kernels' 16-byte vector loads aligned.
+bool q_aligned(const void* q, long long row_stride, int dtype) {
+  const long long per16 = 16 / elem_size(dtype);
+  return ((uintptr_t)q % 16) == 0 && (row_stride % per16) == 0;
+}
+
+// cos/sin are called through volatile pointers so that the compiler cannot fuse them into a
+// sincos call or fold them: every entry is the host libm's own cos(a), sin(a).
+double (*volatile g_cos)(double) = std::cos;
+double (*volatile g_sin)(double) = std::sin;
+double (*volatile g_pow)(double, double) = std::pow;
+
+pa_status map_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" pa_status pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size_t dev_buf_bytes,
+                                   size_t* bytes_needed, pa_pool* out, hipStream_t stream) {
+  if (desc == nullptr) return PA_ERR_NULL;
+  pa_status s = check_desc(desc);
+  if (s != PA_OK) return s;
+  const size_t kvb = kv_bytes(desc);
+  const size_t tb = table_bytes(desc);
+  const size_t need = 2 * kvb + 2 * tb;
+  if (dev_buf == nullptr) {
+    if (bytes_needed == nullptr) return PA_ERR_NULL;
+    *bytes_needed = need;
+    return PA_OK;
+  }
+  if (out == nullptr) return PA_ERR_NULL;
+  if (dev_buf_bytes < need || ((uintptr_t)dev_buf % 256) != 0) return PA_ERR_CAPACITY;
+  if (bytes_needed != nullptr) *bytes_needed = need;
+
+  pa_pool p;
+  std::memset(&p, 0, sizeof(p));
+  p.desc = *desc;
+  char* base = static_cast<char*>(dev_buf);
+  p.k = base;
+  p.v = base + kvb;
+  p.rope_cos = desc->rope_max_pos > 0 ? reinterpret_cast<float*>(base + 2 * kvb) : nullptr;
+  p.rope_sin = desc->rope_max_pos > 0 ? reinterpret_cast<float*>(base + 2 * kvb + tb) : nullptr;
+  p.bytes = need;
+
+  if (desc->rope_max_pos > 0) {
+    // Entry [pos][i] = cos/sin(pos * theta^(-2i/D)); frequency and angle in fp64, one rounding to
+    // fp32 (helexa PR #121, commit "slice 1": cos/sin gathered per position, rotate-half halves).
+    const int half = desc->head_dim / 2;
+    const size_t n = (size_t)desc->rope_max_pos * half;
+    std::vector<float> cs(n), sn(n);
+    for (int i = 0; i < half; ++i) {
+      const double inv = g_pow(desc->rope_theta, -2.0 * i / desc->head_dim);
+      for (int pos = 0; pos < desc->rope_max_pos; ++pos) {
+        const double ang = (double)pos * inv;
+        cs[(size_t)pos * half + i] = (float)g_cos(ang);
+        sn[(size_t)pos * half + i] = (float)g_sin(ang);
+      }
+    }
+    hipError_t e = hipMemcpyAsync(p.rope_cos, cs.data(), n * sizeof(float),
+                                  hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(p.rope_sin, sn.data(), n * sizeof(float), hipMemcpyHostToDevice,
+                         stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  *out = p;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables,
+                                  int32_t bt_stride, const int32_t* positions, const int32_t* dest,
+                                  const void* k_new, const void* v_new, const void* q_in,
+                                  void* q_out, int32_t num_q_heads, int32_t batch,
+                                  hipStream_t stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  const pa_pool_desc& d = pool->desc;
+  if (positions == nullptr || k_new == nullptr || v_new == nullptr) return PA_ERR_NULL;
+  if ((q_in == nullptr) != (q_out == nullptr)) return PA_ERR_NULL;
+  if (d.layout == PA_PAGED && block_tables == nullptr) return PA_ERR_NULL;
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (d.layout == PA_PAGED && bt_stride < 1) return PA_ERR_SHAPE;
+  if (d.layout == PA_PADDED && batch > d.batch_cap) return PA_ERR_SHAPE;
+  if (q_in != nullptr && (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0))
+    return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+
+  pa::AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.layout = d.layout;
+  a.dtype = d.dtype;
+  a.H_kv = d.num_kv_heads;
+  a.H_q = q_in != nullptr ? num_q_heads : 0;
+  a.D = d.head_dim;
+  a.num_blocks = d.num_blocks;
+  a.batch_cap = d.batch_cap;
+  a.seq_cap = d.seq_cap;
+  a.rope_max_pos = d.rope_max_pos;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.cos = d.rope_max_pos > 0 ? pool->rope_cos : nullptr;
+  a.sin = d.rope_max_pos > 0 ? pool->rope_sin : nullptr;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.positions = positions;
+  a.dest = dest;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.q_in = q_in;
+  a.q_out = q_out;
+  a.batch = batch;
+  return map_hip(pa::launch_append(a, stream));
+}
+
+extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
+                                         int32_t n_q, int32_t num_q_heads,
+                                         const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* kv_lens, int32_t batch,
+                                         int32_t max_kv_len, float scale, void* workspace,
+                                         size_t workspace_bytes, size_t* workspace_needed,
+                                         float* out, float* lse, hipStream_t stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  const pa_pool_desc& d = pool->desc;
+  if (d.layout != PA_PAGED) return PA_ERR_SHAPE;
+  if (q == nullptr || block_tables == nullptr || kv_lens == nullptr || out == nullptr)
+    return PA_ERR_NULL;
+  if (batch < 0 || n_q < 1 || bt_stride < 1 || max_kv_len < 0 || q_row_stride < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_kv_len > (int64_t)bt_stride * pa::kBlock) return PA_ERR_SHAPE;
+  const int G = num_q_heads / d.num_kv_heads;
+  if (n_q == 1 && G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (!q_aligned(q, q_row_stride, d.dtype)) return PA_ERR_SHAPE;
+
+  const int s_max = n_q == 1 ? pa::num_splits(max_kv_len, pa::chunk_tokens(d.head_dim)) : 1;
+  const size_t need = pa::decode_workspace_bytes(batch, n_q, num_q_heads, d.head_dim, s_max);
+  if (workspace_needed != nullptr) {
+    *workspace_needed = need;
+    return PA_OK;
+  }
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_CAPACITY;
+  if (batch == 0) return PA_OK;
+
+  pa::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.layout = PA_PAGED;
+  a.dtype = d.dtype;
+  a.H_kv = d.num_kv_heads;
+  a.H_q = num_q_heads;
+  a.D = d.head_dim;
+  a.n_q = n_q;
+  a.num_blocks = d.num_blocks;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.q = q;
+  a.q_row_stride = q_row_stride;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.kv_lens = kv_lens;
+  a.batch = batch;
+  a.max_kv_len = max_kv_len;
+  a.s_max = s_max;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  if (need > 0)
+    pa::carve_workspace(workspace, batch, n_q, num_q_heads, d.head_dim, s_max, &a.part_o,
+                        &a.part_lse);
+  hipError_t e = n_q == 1 ? pa::launch_decode_vector(a, stream) : pa::launch_decode_mq(a, stream);
+  if (e == hipSuccess && s_max > 1) e = pa::launch_lse_reduce(a, stream);
+  return map_hip(e);
+}
+
+extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
+                                                int32_t num_q_heads, int32_t batch,
+                                                const int32_t* gap_start, const int32_t* gap_end,
+                                                int32_t kv_cols, float scale, void* workspace,
+                                                size_t workspace_bytes, size_t* workspace_needed,
+                                                float* out, float* lse, hipStream_t stream) {
+  pa_status s = check_pool(padded_pool);
+  if (s != PA_OK) return s;
+  const pa_pool_desc& d = padded_pool->desc;
+  if (d.layout != PA_PADDED) return PA_ERR_SHAPE;
+  if (q == nullptr || gap_start == nullptr || gap_end == nullptr || out == nullptr)
+    return PA_ERR_NULL;
+  if (batch < 0 || batch > d.batch_cap || kv_cols < 0 || kv_cols > d.seq_cap) return PA_ERR_SHAPE;
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int G = num_q_heads / d.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  const long long row_stride = (long long)num_q_heads * d.head_dim;
+  if (!q_aligned(q, row_stride, d.dtype)) return PA_ERR_SHAPE;
+
+  const int s_max = pa::num_splits(kv_cols, pa::chunk_tokens(d.head_dim));
+  const size_t need = pa::decode_workspace_bytes(batch, 1, num_q_heads, d.head_dim, s_max);
+  if (workspace_needed != nullptr) {
+    *workspace_needed = need;
+    return PA_OK;
+  }
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_CAPACITY;
+  if (batch == 0) return PA_OK;
+
+  pa::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.layout = PA_PADDED;
+  a.dtype = d.dtype;
+  a.H_kv = d.num_kv_heads;
+  a.H_q = num_q_heads;
+  a.D = d.head_dim;
+  a.n_q = 1;
+  a.seq_cap = d.seq_cap;
+  a.k = padded_pool->k;
+  a.v = padded_pool->v;
+  a.q = q;
+  a.q_row_stride = row_stride;
+  a.gap_start = gap_start;
+  a.gap_end = gap_end;
+  a.kv_cols = kv_cols;
+  a.batch = batch;
+  a.max_kv_len = kv_cols;
+  a.s_max = s_max;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  if (need > 0)
+    pa::carve_workspace(workspace, batch, 1, num_q_heads, d.head_dim, s_max, &a.part_o,
+                        &a.part_lse);
+  hipError_t e = pa::launch_decode_vector(a, stream);
+  if (e == hipSuccess && s_max > 1) e = pa::launch_lse_reduce(a, stream);
+  return map_hip(e);
+}

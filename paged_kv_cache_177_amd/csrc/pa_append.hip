@@ -1,0 +1,131 @@
+// append_kv for gfx950: write each row's new key (rotated at its own position) and value into the
+// pool, and optionally rotate the queries at the same positions.
+//
+// helexa PR #121, commit "slice 1": cos/sin are gathered at arbitrary per-row positions and applied
+// rotate-half (element i pairs with i + D/2); keys are stored post-RoPE, so where a key sits (its
+// slot or padded column) never changes its scores. NeuroGrid releases, v0.7.0 "Paged KV Cache": the
+// slot is found through the row's block table.
+//
+// One thread per (row, head, i < D/2) handles the pair (i, i + D/2). The rotation is done in fp32
+// with every product and sum rounded on its own (contraction into fused multiply-adds is switched
+// off), and the result is rounded to the pool dtype by the hardware fp32 -> bf16 conversion (round
+// to nearest even), so the stored bits do not depend on the launch geometry.
+#include <type_traits>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
+
+// Raw storage bits of T: copies move bits, never values (no NaN canonicalisation).
+template <typename T>
+using Bits = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
+
+template <typename T>
+__device__ __forceinline__ void copy_pair(const T* src, T* dst, int i, int half) {
+  const Bits<T>* s = reinterpret_cast<const Bits<T>*>(src);
+  Bits<T>* d = reinterpret_cast<Bits<T>*>(dst);
+  d[i] = s[i];
+  d[i + half] = s[i + half];
+}
+
+// r_lo = x_lo*c - x_hi*s ; r_hi = x_hi*c + x_lo*s, each operation rounded separately.
+__device__ __forceinline__ void rotate_pair(float x_lo, float x_hi, float c, float s, float* r_lo,
+                                            float* r_hi) {
+#pragma clang fp contract(off)
+  const float a = x_lo * c;
+  const float b = x_hi * s;
+  const float d = x_hi * c;
+  const float e = x_lo * s;
+  *r_lo = a - b;
+  *r_hi = d + e;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  const int half = a.D / 2;
+  const int heads = 2 * a.H_kv + (a.q_in != nullptr ? a.H_q : 0);
+  const long long total = (long long)a.batch * heads * half;
+  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int i = (int)(tid % half);
+  const int hh = (int)((tid / half) % heads);
+  const int b = (int)(tid / ((long long)half * heads));
+
+  const bool rope = a.cos != nullptr;
+  int pos = a.positions[b];
+  if (rope) pos = clampi(pos, 0, a.rope_max_pos - 1);
+
+  if (hh >= 2 * a.H_kv) {  // query head: rotate into q_out
+    const int h = hh - 2 * a.H_kv;
+    const size_t base = ((size_t)b * a.H_q + h) * a.D;
+    const T* src = reinterpret_cast<const T*>(a.q_in) + base;
+    T* dst = reinterpret_cast<T*>(a.q_out) + base;
+    if (rope) {
+      float r_lo, r_hi;
+      rotate_pair(to_f32(src[i]), to_f32(src[i + half]), a.cos[(size_t)pos * half + i],
+                  a.sin[(size_t)pos * half + i], &r_lo, &r_hi);
+      dst[i] = from_f32<T>(r_lo);
+      dst[i + half] = from_f32<T>(r_hi);
+    } else {
+      copy_pair(src, dst, i, half);
+    }
+    return;
+  }
+
+  const bool is_v = hh >= a.H_kv;
+  const int h = is_v ? hh - a.H_kv : hh;
+  int t = a.dest != nullptr ? a.dest[b] : a.positions[b];
+  size_t slot_base;  // element offset of [.., h, slot/column, 0]
+  if (a.layout == PA_PAGED) {
+    t = clampi(t, 0, a.bt_stride * kBlock - 1);
+    int blk = a.block_tables[(size_t)b * a.bt_stride + t / kBlock];
+    blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+    slot_base = (((size_t)blk * a.H_kv + h) * kBlock + (t % kBlock)) * a.D;
+  } else {
+    t = clampi(t, 0, a.seq_cap - 1);
+    slot_base = (((size_t)b * a.H_kv + h) * a.seq_cap + t) * a.D;
+  }
+  const size_t src_base = ((size_t)b * a.H_kv + h) * a.D;
+  if (is_v) {
+    const T* src = reinterpret_cast<const T*>(a.v_new) + src_base;
+    T* dst = reinterpret_cast<T*>(a.v) + slot_base;
+    copy_pair(src, dst, i, half);
+    return;
+  }
+  const T* src = reinterpret_cast<const T*>(a.k_new) + src_base;
+  T* dst = reinterpret_cast<T*>(a.k) + slot_base;
+  if (rope) {
+    float r_lo, r_hi;
+    rotate_pair(to_f32(src[i]), to_f32(src[i + half]), a.cos[(size_t)pos * half + i],
+                a.sin[(size_t)pos * half + i], &r_lo, &r_hi);
+    dst[i] = from_f32<T>(r_lo);
+    dst[i + half] = from_f32<T>(r_hi);
+  } else {
+    copy_pair(src, dst, i, half);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  const int heads = 2 * a.H_kv + (a.q_in != nullptr ? a.H_q : 0);
+  const long long total = (long long)a.batch * heads * (a.D / 2);
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (a.dtype == PA_F32)
+    hipLaunchKernelGGL(append_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,92 @@
+// Internal interface between the C-ABI layer (pa_api.cpp) and the gfx950 kernels (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;  // tokens per K/V block
+
+// ---- split rule ------------------------------------------------------------------------------
+// A row of n keys is cut into ceil(n / chunk) chunks of `chunk` tokens (the last one shorter);
+// chunk depends only on head_dim, so a row's split -- and with it the exact order of its fp32
+// reductions -- depends on that row's own length alone. chunk is a multiple of 16 and at most
+// 64 blocks, so one wave holds a chunk's block ids in one register.
+__host__ __device__ inline int chunk_tokens(int head_dim) {
+  return head_dim >= 128 ? 512 : 1024;
+}
+__host__ __device__ inline int num_splits(int n, int chunk) {
+  return n <= 0 ? 1 : (n + chunk - 1) / chunk;
+}
+
+// ---- kernel argument packs ---------------------------------------------------------------
+struct AppendArgs {
+  int layout, dtype, H_kv, H_q, D;
+  int num_blocks, batch_cap, seq_cap, rope_max_pos;
+  void* k;
+  void* v;
+  const float* cos;  // NULL: no RoPE
+  const float* sin;
+  const int32_t* block_tables;
+  int bt_stride;
+  const int32_t* positions;
+  const int32_t* dest;  // NULL: dest = positions
+  const void* k_new;
+  const void* v_new;
+  const void* q_in;  // NULL: no queries
+  void* q_out;
+  int batch;
+};
+
+struct DecodeArgs {
+  int layout, dtype, H_kv, H_q, D, n_q;
+  int num_blocks;
+  int seq_cap;  // padded layout
+  const void* k;
+  const void* v;
+  const void* q;
+  long long q_row_stride;  // elements
+  const int32_t* block_tables;  // paged
+  int bt_stride;
+  const int32_t* kv_lens;       // paged
+  const int32_t* gap_start;     // padded
+  const int32_t* gap_end;       // padded
+  int kv_cols;                  // padded
+  int batch;
+  int max_kv_len;  // host bound: paged max kv_len, padded kv_cols
+  int s_max;       // splits of the longest possible row
+  float scale;
+  float* out;
+  float* lse;
+  float* part_o;    // [batch][n_q*H_q][s_max][D]
+  float* part_lse;  // [batch][n_q*H_q][s_max] (log2 domain)
+};
+
+// Bytes of split-K partials for a decode call (0 when no row can split).
+inline size_t decode_workspace_bytes(int batch, int n_q, int H_q, int D, int s_max) {
+  if (s_max <= 1) return 0;
+  size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
+  size_t bytes = rows * (size_t)D * sizeof(float);
+  bytes = (bytes + 255) & ~(size_t)255;
+  bytes += rows * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+inline void carve_workspace(void* ws, int batch, int n_q, int H_q, int D, int s_max,
+                            float** part_o, float** part_lse) {
+  size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
+  size_t o_bytes = (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
+  *part_o = (float*)ws;
+  *part_lse = (float*)((char*)ws + o_bytes);
+}
+
+// ---- launchers (each returns the hipGetLastError of its launches) -----------------------------
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1
+hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream);      // n_q > 1
+hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

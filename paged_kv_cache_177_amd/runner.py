@@ -1,0 +1,125 @@
+"""Caller-side plumbing for one batched decode step: upload host arrays into a pool and device
+buffers, then enqueue the library calls. Used by the tests, the smoke check and the bench.
+
+Nothing here computes any part of attention: it copies arrays and calls the C ABI.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def to_torch(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Host storage array (np.float32, or np.uint16 bf16 bits) -> CPU tensor of the storage dtype."""
+    a = np.ascontiguousarray(a)
+    if dtype == "f32":
+        return torch.from_numpy(a.astype(np.float32, copy=False))
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+
+
+def to_numpy(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Device/CPU tensor of the storage dtype -> host storage array (bits preserved)."""
+    t = t.detach().cpu().contiguous()
+    if dtype == "f32":
+        return t.numpy().copy()
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+class PagedStep:
+    """One append-then-decode step over a paged pool.
+
+    ``case`` provides (duck-typed): dtype, num_q_heads, num_kv_heads, head_dim, num_blocks,
+    rope_theta, rope_max_pos, positions, dest, kv_lens, block_tables, k_pool, v_pool, k_new,
+    v_new, q, scale. With a RoPE table the queries are rotated by the append into ``q_rot`` and the
+    decode reads those; without one the decode reads ``q`` directly."""
+
+    def __init__(self, case, device: str = "cuda", stream=None):
+        self.case = case
+        self.dtype = case.dtype
+        self.device = device
+        self.stream = stream
+        desc = B.make_desc("paged", case.dtype, case.num_kv_heads, case.head_dim,
+                           num_blocks=case.num_blocks, rope_max_pos=case.rope_max_pos,
+                           rope_theta=case.rope_theta)
+        self.kv = B.alloc_pool(desc, device=device, stream=stream)
+        self.kv.k.copy_(to_torch(case.k_pool, case.dtype))
+        self.kv.v.copy_(to_torch(case.v_pool, case.dtype))
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+        self.block_tables = dev(case.block_tables.astype(np.int32))
+        self.bt_stride = int(case.block_tables.shape[1])
+        self.positions = dev(case.positions.astype(np.int32))
+        self.dest = dev(case.dest.astype(np.int32))
+        self.kv_lens = dev(case.kv_lens.astype(np.int32))
+        self.k_new = to_torch(case.k_new, case.dtype).to(device)
+        self.v_new = to_torch(case.v_new, case.dtype).to(device)
+        self.q = to_torch(case.q, case.dtype).to(device)
+        self.rope = case.rope_max_pos > 0
+        self.q_rot = torch.empty_like(self.q) if self.rope else None
+        self.batch = len(case.kv_lens)
+        self.H_q = case.num_q_heads
+        self.D = case.head_dim
+        self.max_kv_len = int(case.kv_lens.max(initial=0))
+        self.out = torch.empty((self.batch, self.H_q, self.D), dtype=torch.float32, device=device)
+        self.lse = torch.empty((self.batch, self.H_q), dtype=torch.float32, device=device)
+        need = B.pa_decode_attention(self.kv.pool, self.q, self.H_q * self.D, 1, self.H_q,
+                                     self.block_tables, self.bt_stride, self.kv_lens, self.batch,
+                                     self.max_kv_len, case.scale, out=self.out,
+                                     query_workspace=True)
+        self.workspace = (torch.empty(need, dtype=torch.uint8, device=device) if need > 0
+                          else None)
+
+    @property
+    def q_decode(self) -> torch.Tensor:
+        return self.q_rot if self.rope else self.q
+
+    def append(self):
+        B.pa_append_kv(self.kv.pool, self.block_tables, self.bt_stride, self.positions, self.dest,
+                       self.k_new, self.v_new, self.q if self.rope else None,
+                       self.q_rot, self.H_q if self.rope else 0, self.batch, stream=self.stream)
+
+    def decode(self, with_lse: bool = True):
+        B.pa_decode_attention(self.kv.pool, self.q_decode, self.H_q * self.D, 1, self.H_q,
+                              self.block_tables, self.bt_stride, self.kv_lens, self.batch,
+                              self.max_kv_len, self.case.scale, workspace=self.workspace,
+                              out=self.out, lse=self.lse if with_lse else None,
+                              stream=self.stream)
+
+    def step(self):
+        self.append()
+        self.decode()
+
+
+class MultiQueryStep:
+    """Multi-query paged attention: n_q shared queries per row over ragged per-row keys.
+
+    ``case`` provides: dtype, num_heads, head_dim, n_q, num_blocks, kv_lens, block_tables,
+    k_pool, v_pool, q ([n_q][H][dh], shared by all rows), scale."""
+
+    def __init__(self, case, device: str = "cuda", stream=None):
+        self.case = case
+        self.stream = stream
+        desc = B.make_desc("paged", case.dtype, case.num_heads, case.head_dim,
+                           num_blocks=case.num_blocks)
+        self.kv = B.alloc_pool(desc, device=device, stream=stream)
+        self.kv.k.copy_(to_torch(case.k_pool, case.dtype))
+        self.kv.v.copy_(to_torch(case.v_pool, case.dtype))
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+        self.block_tables = dev(case.block_tables.astype(np.int32))
+        self.bt_stride = int(case.block_tables.shape[1])
+        self.kv_lens = dev(case.kv_lens.astype(np.int32))
+        self.q = to_torch(case.q, case.dtype).to(device)
+        self.batch = len(case.kv_lens)
+        self.max_kv_len = int(case.kv_lens.max(initial=0))
+        shape = (self.batch, case.n_q, case.num_heads, case.head_dim)
+        self.out = torch.empty(shape, dtype=torch.float32, device=device)
+        self.lse = torch.empty(shape[:3], dtype=torch.float32, device=device)
+
+    def decode(self, with_lse: bool = True):
+        c = self.case
+        B.pa_decode_attention(self.kv.pool, self.q, 0, c.n_q, c.num_heads, self.block_tables,
+                              self.bt_stride, self.kv_lens, self.batch, self.max_kv_len, c.scale,
+                              out=self.out, lse=self.lse if with_lse else None,
+                              stream=self.stream)
