@@ -1,0 +1,200 @@
+"""Benchmark: one batched decode step (append_kv + paged decode attention + log-sum-exp merge) of
+the B=128 ragged bf16 workload on one MI355X, through the C ABI.
+
+Workload: 128 rows with contexts uniform in [512, 8192] (seed 2: kv_len 809..8139, sum 574 199),
+32 query / 8 KV heads, head_dim 64, bf16 N(0,1) values, 16-token blocks in a shuffled pool sized
+1.25x the blocks needed. One step reads 1.176 GB of K/V.
+
+Prints one JSON line. ``value`` is K/V GB/s of whole steps (wall clock over the timed steps,
+append + decode + merge, inputs resident in HBM); ``roofline`` uses HIP events recorded on the
+library's stream around every decode call inside the timed region; ``cpu_baseline`` times the
+fp64 oracle on the host cores over the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=128 ragged bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b128_traffic.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="b128", choices=["b128", "long"],
+                   help="b128 is the reported workload; long is for diagnostics")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush-mb", type=int, default=512,
+                   help="cache-flush write between the extra flushed decode timings")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    from paged_kv_cache_177_amd.build import sources
+
+    h = hashlib.sha256()
+    for s in sources():
+        with open(s, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(src_hash: str):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources (its 'source_hash' line matches); else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src_hash or "hbm_bytes_per_call" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_call"])
+
+
+def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 3):
+    """The oracle (as it stands) on the full workload's decode: gather every row through its block
+    table and run two-pass fp64 attention. Repeated until ~budget_s of CPU work, median taken."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+
+    k2, v2, _ = O.append_kv(case.k_pool, case.v_pool, case.dtype, "paged", case.block_tables,
+                            case.positions, case.dest, case.k_new, case.v_new)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_start) < budget_s:
+        t0 = time.perf_counter()
+        O.decode_paged(k2, v2, case.dtype, case.block_tables, case.kv_lens, case.q, case.scale)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+            if p.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": case.kv_bytes() / t / 1e9, "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"full {case.name} decode step (all {case.batch} rows, "
+                       f"{case.kv_bytes() / 1e9:.3f} GB K/V) in fp64 numpy, median of "
+                       f"{len(times)} run(s), {t:.2f} s each; host affinity "
+                       f"{len(os.sched_getaffinity(0))} cores, BLAS threads {cores}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_177_amd.runner import PagedStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    case = W.b128() if args.workload == "b128" else W.long_context()
+    kv_bytes = case.kv_bytes()
+    r = PagedStep(case, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        r.append()
+        r.decode()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        r.append()
+        evs[i][0].record(stream)
+        r.decode()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+
+    # extra: decode calls with the last-level cache flushed before each one (outside the events)
+    flush = torch.empty(args.flush_mb * (1 << 20), dtype=torch.uint8, device="cuda:0")
+    fl = []
+    for _ in range(10):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        r.decode()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl.append(a.elapsed_time(b))
+    del flush
+
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash)
+    out = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{case.name}: B={case.batch} ragged contexts "
+                                f"{int(case.n_ctx.min())}..{int(case.n_ctx.max())} "
+                                f"(kv_len sum {int(case.kv_lens.sum())}), H_q={case.num_q_heads}, "
+                                f"H_kv={case.num_kv_heads}, D={case.head_dim}, 16-token blocks, "
+                                f"shuffled pool of {case.num_blocks} blocks, seed {case.seed}"),
+                   "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
+                   "step": "append_kv + decode + lse merge"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
+                                 if traffic is not None else None),
+                     "kernel": "pa_decode_attention call (decode_vector_kernel + "
+                               "lse_reduce_kernel)",
+                     "bytes_per_launch": kv_bytes,
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
+        "detail": {"us_per_step": round(ms_per_step * 1e3, 2),
+                   "pct_hbm_peak_step": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9
+                                              / HBM_PEAK_GBS, 2),
+                   "decode_us_median": round(statistics.median(dec_ms) * 1e3, 2),
+                   "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                   "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                   "decode_us_flushed_median": round(statistics.median(fl) * 1e3, 2),
+                   "kv_gbs_flushed": round(kv_bytes / (statistics.median(fl) * 1e-3) / 1e9, 1),
+                   "source_hash": src_hash},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

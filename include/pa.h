@@ -120,7 +120,8 @@ pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t
  * q: [batch][n_q][num_q_heads][D] in the pool dtype; row b starts at element b * q_row_stride
  * (q_row_stride = 0 shares one [n_q][H_q][D] block of queries between all rows). Query head h reads
  * KV head h / G, G = num_q_heads / H_kv. Row b attends over its first kv_lens[b] tokens, gathered
- * through block_tables[b * bt_stride ...]; score = scale * <q, k>; exact softmax, computed online.
+ * through block_tables[b * bt_stride ...]; score = scale * <q, k> (scale finite and >= 0); exact
+ * softmax, computed online.
  * out: [batch][n_q][num_q_heads][D] fp32. lse: [batch][n_q][num_q_heads] fp32 or NULL.
  * n_q == 1 is the decode path (vector units; one workgroup per (row, KV head, split); long rows are
  * split into chunks whose partial results a second kernel merges by log-sum-exp). n_q > 1 is the
@@ -128,11 +129,15 @@ pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t
  * result does not depend on the rest of the batch.
  * Workspace: with workspace_needed != NULL the call only writes the bytes it needs for these
  * arguments there and launches nothing; otherwise workspace must hold that many bytes (it may be
- * NULL when none are needed). max_kv_len is a host upper bound of kv_lens (<= bt_stride * 16).
+ * NULL when none are needed). A workspace must be zero-filled before its first use: its first 256
+ * bytes hold the work counter of the split kernels, which every call leaves at zero again. Calls
+ * that overlap in time (other streams) need workspaces of their own. max_kv_len is a host upper
+ * bound of kv_lens (<= bt_stride * 16).
  * Preconditions (clamped, not checked): 0 <= kv_lens[b] <= max_kv_len; block ids < num_blocks.
  * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0, n_q < 1,
  * num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, layout not
- * PA_PAGED); PA_ERR_UNSUPPORTED (n_q == 1 with G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace
+ * PA_PAGED, scale negative or not finite, q not 16-byte aligned or q_row_stride not a multiple of
+ * 16 bytes); PA_ERR_UNSUPPORTED (n_q == 1 with G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace
  * too small). batch == 0 is a no-op. */
 pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
                               int32_t n_q, int32_t num_q_heads, const int32_t* block_tables,
@@ -150,7 +155,8 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
  * Workspace as for pa_decode_attention.
  * Preconditions (clamped, not checked): 0 <= gap_start[b] <= gap_end[b] <= kv_cols.
  * Errors: PA_ERR_NULL (pool, q, gap_start, gap_end, out); PA_ERR_SHAPE (batch < 0 or > batch_cap,
- * kv_cols < 0 or > seq_cap, num_q_heads not a positive multiple of H_kv, layout not PA_PADDED);
+ * kv_cols < 0 or > seq_cap, num_q_heads not a positive multiple of H_kv, layout not PA_PADDED,
+ * scale negative or not finite, q not 16-byte aligned);
  * PA_ERR_UNSUPPORTED (G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace too small). */
 pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
                                      int32_t num_q_heads, int32_t batch, const int32_t* gap_start,

@@ -182,6 +182,7 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   const int G = num_q_heads / d.num_kv_heads;
   if (n_q == 1 && G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
   if (!q_aligned(q, q_row_stride, d.dtype)) return PA_ERR_SHAPE;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
 
   const int s_max = n_q == 1 ? pa::num_splits(max_kv_len, pa::chunk_tokens(d.head_dim)) : 1;
   const size_t need = pa::decode_workspace_bytes(batch, n_q, num_q_heads, d.head_dim, s_max);
@@ -215,8 +216,8 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   a.out = out;
   a.lse = lse;
   if (need > 0)
-    pa::carve_workspace(workspace, batch, n_q, num_q_heads, d.head_dim, s_max, &a.part_o,
-                        &a.part_lse);
+    pa::carve_workspace(workspace, batch, n_q, num_q_heads, d.head_dim, s_max, &a.counter,
+                        &a.part_o, &a.part_lse);
   hipError_t e = n_q == 1 ? pa::launch_decode_vector(a, stream) : pa::launch_decode_mq(a, stream);
   if (e == hipSuccess && s_max > 1) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);
@@ -240,6 +241,7 @@ extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, cons
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
   const long long row_stride = (long long)num_q_heads * d.head_dim;
   if (!q_aligned(q, row_stride, d.dtype)) return PA_ERR_SHAPE;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
 
   const int s_max = pa::num_splits(kv_cols, pa::chunk_tokens(d.head_dim));
   const size_t need = pa::decode_workspace_bytes(batch, 1, num_q_heads, d.head_dim, s_max);
@@ -273,8 +275,8 @@ extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, cons
   a.out = out;
   a.lse = lse;
   if (need > 0)
-    pa::carve_workspace(workspace, batch, 1, num_q_heads, d.head_dim, s_max, &a.part_o,
-                        &a.part_lse);
+    pa::carve_workspace(workspace, batch, 1, num_q_heads, d.head_dim, s_max, &a.counter,
+                        &a.part_o, &a.part_lse);
   hipError_t e = pa::launch_decode_vector(a, stream);
   if (e == hipSuccess && s_max > 1) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);

@@ -8,24 +8,37 @@
 // each row's padding gap [gap_start, gap_end) (helexa PR #121, commit "slice 1":
 // batch_decode_mask over one gap per row).
 //
-// Mapping (one workgroup = 4 waves per (KV head g, row b, split s)):
+// Mapping (one workgroup of kWaves waves per chunk (KV head g, row b, split s)):
 //   * A row is cut into chunks of chunk_tokens(D) tokens; split s owns chunk s. The workgroup
-//     covers the G = H_q / H_kv query heads of KV head g, so every K/V byte is loaded once and
-//     used by all G heads straight from registers.
-//   * Inside a wave, LPT = D/16 lanes share one token (16 dims each); a "step" is the 64/LPT
-//     tokens one wave loads at once (exactly one 16-token block at D = 64). Steps of the chunk are
-//     dealt round-robin to the 4 waves; each wave prefetches its next step's K and V (one
-//     contiguous 16-byte-per-lane read per tensor) while it computes the current one.
+//     covers the G = H_q / H_kv query heads of KV head g, so each K/V byte is loaded once and
+//     feeds all G heads from registers.
+//   * A wave works one 16-token block per step. Every lane owns 8 dims (16 bytes of bf16) of
+//     TPL = D/32 of the block's tokens, so each 16-byte-per-lane load instruction reads one
+//     contiguous 1 KB run of the block: fully coalesced, non-temporal (K/V are read once), with a
+//     wave-uniform block base and a lane offset. Blocks of the chunk are dealt round-robin to the
+//     waves; each wave keeps its next block in flight while it computes the current one.
 //   * q.k: packed bf16 dot products (v_dot2_f32_bf16) accumulate in fp32, then a DPP butterfly
-//     over the LPT lanes of the token. Scores are kept in log2 units (scale * log2(e) folded in)
-//     so the softmax uses the hardware exp2.
-//   * Online softmax per lane: each lane keeps its own running max m, sum l and accumulator for
-//     the tokens it sees. m is only raised when a score exceeds it by more than 2^8 (log2 units),
-//     so rescaling is rare; all weights stay <= 2^8 and the result is exact up to rounding.
-//   * At the end lanes are merged with a common max: DPP inside each 16-lane row, then LDS across
-//     rows and waves. One split writes out/lse; several splits write normalised partials and their
-//     log-sum-exp, merged by lse_reduce_kernel.
+//     over the LPT = D/8 lanes of a token. Scores are kept in log2 units (scale * log2(e) folded
+//     in) so the softmax uses the hardware exp2.
+//   * Online softmax per lane: each lane keeps a running max m, sum l and an 8-dim accumulator
+//     per head for the tokens it sees. m is raised only when a score exceeds it by more than 8
+//     (log2 units), so rescales are rare; weights stay <= 2^8 and the result is exact up to
+//     rounding. Only a chunk's partial last block runs the masked update.
+//   * At the end the lanes' streams are merged to a common max (DPP inside 16-lane rows, a
+//     swizzle across rows, a swap across half-waves), then the waves through LDS. One split
+//     writes out/lse; several write normalised partials plus their log-sum-exp for
+//     lse_reduce_kernel.
+//   * Two launch shapes run the same chunks: a grid of one workgroup per (g, b, s) whose
+//     workgroups past a row's last split exit at once, and a persistent grid that pulls chunks
+//     from a counter (see decode_persistent_kernel), used when there are few (row, head) pairs.
 #include "pa_internal.h"
+
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_PERSISTENT
+#define PA_DECODE_PERSISTENT 1
+#endif
 
 namespace pa {
 namespace {
@@ -35,18 +48,19 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;  // log2 units
-constexpr int kWaves = 4;
+constexpr int kWaves = PA_DECODE_WAVES;
 constexpr float kNegInf = -__builtin_inff();
 
-// ---- cross-lane helpers (DPP) --------------------------------------------------------------
+// ---- cross-lane helpers -----------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i inside each 8-lane half row
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i inside each 16-lane row
 template <int N>
 __device__ __forceinline__ float row_ror(float x) {
   return dpp<0x120 + N>(x);
@@ -55,24 +69,23 @@ __device__ __forceinline__ float row_ror(float x) {
 // Sum over the LPT consecutive lanes that share one token (result in all of them).
 template <int LPT>
 __device__ __forceinline__ float token_lane_sum(float x) {
-  static_assert(LPT == 2 || LPT == 4 || LPT == 8, "lanes per token");
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16, "lanes per token");
   x += dpp<kQuadXor1>(x);
-  if constexpr (LPT >= 4) x += dpp<kQuadXor2>(x);
+  x += dpp<kQuadXor2>(x);
   if constexpr (LPT >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (LPT >= 16) x += dpp<kRowMirror>(x);
   return x;
 }
 
-// Reduce over the token streams of one 16-lane row (lanes congruent mod LPT); result in all.
+// Reduce over the token streams inside one 16-lane row (lanes congruent mod LPT).
 template <int LPT, bool MAX>
 __device__ __forceinline__ float row_stream_reduce(float x) {
-  if constexpr (LPT <= 1) x = MAX ? fmaxf(x, row_ror<1>(x)) : x + row_ror<1>(x);
-  if constexpr (LPT <= 2) x = MAX ? fmaxf(x, row_ror<2>(x)) : x + row_ror<2>(x);
   if constexpr (LPT <= 4) x = MAX ? fmaxf(x, row_ror<4>(x)) : x + row_ror<4>(x);
   if constexpr (LPT <= 8) x = MAX ? fmaxf(x, row_ror<8>(x)) : x + row_ror<8>(x);
   return x;
 }
 
-// Lane i <-> lane i ^ 16 (inside each 32-lane half): ds_swizzle in bit-mask mode
+// Lane i <-> lane i ^ 16 inside each 32-lane half: ds_swizzle, bit-mask mode
 // (and_mask 0x1f, or_mask 0, xor_mask 0x10).
 __device__ __forceinline__ float swap_rows16(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
@@ -80,335 +93,622 @@ __device__ __forceinline__ float swap_rows16(float x) {
 // Lane i <-> lane i ^ 32.
 __device__ __forceinline__ float swap_halves32(float x) { return __shfl_xor(x, 32); }
 
-// Sum over all token streams of the wave (lanes congruent mod LPT); result in all lanes.
-template <int LPT>
-__device__ __forceinline__ float wave_stream_sum(float x) {
-  x = row_stream_reduce<LPT, false>(x);
-  x += swap_rows16(x);
-  x += swap_halves32(x);
+template <int LPT, bool MAX>
+__device__ __forceinline__ float wave_stream_reduce(float x) {
+  x = row_stream_reduce<LPT, MAX>(x);
+  x = MAX ? fmaxf(x, swap_rows16(x)) : x + swap_rows16(x);
+  x = MAX ? fmaxf(x, swap_halves32(x)) : x + swap_halves32(x);
   return x;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// ---- per-dtype register fragments (16 elements of one token per lane) ---------------------------
-template <typename T>
-struct Frag;
-
-template <>
-struct Frag<__bf16> {
-  uint4 k[2], v[2];
-  __device__ __forceinline__ void load(const __bf16* kp, const __bf16* vp) {
-    const uint4* a = reinterpret_cast<const uint4*>(kp);
-    const uint4* b = reinterpret_cast<const uint4*>(vp);
-    k[0] = a[0];
-    k[1] = a[1];
-    v[0] = b[0];
-    v[1] = b[1];
-  }
-  __device__ __forceinline__ void zero_v() { v[0] = v[1] = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ void v_f32(float* o) const {
-    const uint32_t w[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      o[2 * i] = bf16_lo(w[i]);
-      o[2 * i + 1] = bf16_hi(w[i]);
-    }
-  }
-};
-
-template <>
-struct Frag<float> {
-  float4 k[4], v[4];
-  __device__ __forceinline__ void load(const float* kp, const float* vp) {
-    const float4* a = reinterpret_cast<const float4*>(kp);
-    const float4* b = reinterpret_cast<const float4*>(vp);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      k[i] = a[i];
-      v[i] = b[i];
-    }
-  }
-  __device__ __forceinline__ void zero_v() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  __device__ __forceinline__ void v_f32(float* o) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[4 * i] = v[i].x;
-      o[4 * i + 1] = v[i].y;
-      o[4 * i + 2] = v[i].z;
-      o[4 * i + 3] = v[i].w;
-    }
-  }
-};
-
-// Query registers of one lane: 16 dims of each of the G heads.
-template <typename T, int G>
-struct QRegs;
-
-template <int G>
-struct QRegs<__bf16, G> {
-  uint32_t q[G][8];
-  __device__ __forceinline__ void load(const __bf16* p, int head_stride) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4* a = reinterpret_cast<const uint4*>(p + (size_t)h * head_stride);
-      uint4 x = a[0], y = a[1];
-      q[h][0] = x.x; q[h][1] = x.y; q[h][2] = x.z; q[h][3] = x.w;
-      q[h][4] = y.x; q[h][5] = y.y; q[h][6] = y.z; q[h][7] = y.w;
-    }
-  }
-  __device__ __forceinline__ float dot(int h, const Frag<__bf16>& f) const {
-    const uint32_t w[8] = {f.k[0].x, f.k[0].y, f.k[0].z, f.k[0].w,
-                           f.k[1].x, f.k[1].y, f.k[1].z, f.k[1].w};
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[h][i]),
-                                          __builtin_bit_cast(bf16x2_t, w[i]), a, false);
-      b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[h][i + 1]),
-                                          __builtin_bit_cast(bf16x2_t, w[i + 1]), b, false);
-    }
-    return a + b;
-  }
-};
-
-template <int G>
-struct QRegs<float, G> {
-  float q[G][16];
-  __device__ __forceinline__ void load(const float* p, int head_stride) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float4* a = reinterpret_cast<const float4*>(p + (size_t)h * head_stride);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float4 x = a[i];
-        q[h][4 * i] = x.x; q[h][4 * i + 1] = x.y; q[h][4 * i + 2] = x.z; q[h][4 * i + 3] = x.w;
-      }
-    }
-  }
-  __device__ __forceinline__ float dot(int h, const Frag<float>& f) const {
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a = fmaf(q[h][4 * i], f.k[i].x, a);
-      b = fmaf(q[h][4 * i + 1], f.k[i].y, b);
-      a = fmaf(q[h][4 * i + 2], f.k[i].z, a);
-      b = fmaf(q[h][4 * i + 3], f.k[i].w, b);
-    }
-    return a + b;
-  }
-};
-
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// ---- the kernel ------------------------------------------------------------------------------
+// ---- 8 elements of one token (one lane's share) -------------------------------------------------
+template <typename T>
+struct Vec8;
+
+template <>
+struct Vec8<__bf16> {
+  uint4 w;
+  // K/V are streamed once: non-temporal loads keep them from displacing reused lines in the caches
+  __device__ __forceinline__ void load(const __bf16* p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    w = make_uint4(x.x, x.y, x.z, x.w);
+  }
+  __device__ __forceinline__ void load_cached(const __bf16* p) {
+    w = *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void to_f32(float* o) const {
+    o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+    o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z); o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+  }
+  // <a, b> over the 8 elements: one chain of packed dot products, fp32 accumulation of the
+  // exact bf16 products
+  __device__ __forceinline__ float dot(const Vec8& b) const {
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x),
+                                              __builtin_bit_cast(bf16x2_t, b.w.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y),
+                                        __builtin_bit_cast(bf16x2_t, b.w.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z),
+                                        __builtin_bit_cast(bf16x2_t, b.w.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w),
+                                        __builtin_bit_cast(bf16x2_t, b.w.w), s, false);
+    return s;
+  }
+};
+
+template <>
+struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
+  }
+  __device__ __forceinline__ void load_cached(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void to_f32(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+  __device__ __forceinline__ float dot(const Vec8& o) const {
+    float s0 = a.x * o.a.x;
+    float s1 = a.y * o.a.y;
+    s0 = fmaf(a.z, o.a.z, s0);
+    s1 = fmaf(a.w, o.a.w, s1);
+    s0 = fmaf(b.x, o.b.x, s0);
+    s1 = fmaf(b.y, o.b.y, s1);
+    s0 = fmaf(b.z, o.b.z, s0);
+    s1 = fmaf(b.w, o.b.w, s1);
+    return s0 + s1;
+  }
+};
+
+// One block's worth of this lane's K and V (TPL tokens).
+template <typename T, int TPL>
+struct BlockFrag {
+  Vec8<T> k[TPL], v[TPL];
+};
+
+// ---- one chunk of one (row, KV head): the unit of work of a workgroup ----------------------------
+struct Chunk {
+  int row, g, split;
+  int tok0, ntok, nblk, tail_blk;  // tail_blk: index of the partial last block, or -1
+  int ns;                          // splits of the row (1: write out/lse directly)
+  int gap_s, gap_shift;            // padded layout: the row's gap start and width
+};
+
+__device__ __forceinline__ Chunk make_chunk(int row, int g, int split, int n, int gap_s,
+                                            int gap_shift, int chunk) {
+  Chunk ch;
+  ch.row = row;
+  ch.g = g;
+  ch.split = split;
+  ch.tok0 = split * chunk;
+  const int rest = n - ch.tok0;
+  ch.ntok = rest < chunk ? (rest > 0 ? rest : 0) : chunk;
+  ch.nblk = (ch.ntok + kBlock - 1) / kBlock;
+  ch.tail_blk = (ch.ntok % kBlock) != 0 ? ch.nblk - 1 : -1;
+  ch.ns = num_splits(n, chunk);
+  ch.gap_s = gap_s;
+  ch.gap_shift = gap_shift;
+  return ch;
+}
+
+template <int G, int D, int WAVES>
+struct EpilogueSmem {
+  float acc[WAVES][G][D];
+  float m[WAVES][G];
+  float l[WAVES][G];
+};
+
+// Per-wave machinery shared by the grid and the persistent kernels: loads of queries, block ids
+// and K/V blocks, the online-softmax update for one block, and the end-of-chunk merge.
 template <typename T, int D, int G, bool PADDED>
-__global__ __launch_bounds__(256) void decode_vector_kernel(const DecodeArgs a) {
-  constexpr int LPT = D / 16;    // lanes per token
-  constexpr int TPS = 64 / LPT;  // tokens per wave step
-  const int g = blockIdx.x;
-  const int row = blockIdx.y;
-  const int split = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int tl = lane / LPT;
-  const int c = lane % LPT;
+struct Worker {
+  static constexpr int LPT = D / 8;         // lanes per token
+  static constexpr int TPI = 64 / LPT;      // tokens per load instruction
+  static constexpr int TPL = kBlock / TPI;  // tokens of a block per lane
+  static_assert(TPL >= 1 && TPL * TPI == kBlock, "block/lane geometry");
+  using Frag = BlockFrag<T, TPL>;
+  using Smem = EpilogueSmem<G, D, kWaves>;
 
-  // valid tokens of the row
-  int n, gap_s = 0, gap_shift = 0;
-  if constexpr (PADDED) {
-    const int cols = a.kv_cols;
-    gap_s = clampi(a.gap_start[row], 0, cols);
-    const int gap_e = clampi(a.gap_end[row], gap_s, cols);
-    gap_shift = gap_e - gap_s;
-    n = cols - gap_shift;
-  } else {
-    n = clampi(a.kv_lens[row], 0, a.max_kv_len);
-  }
-  const int chunk = chunk_tokens(D);
-  const int ns = num_splits(n, chunk);
-  if (split >= ns) return;
-  const int tok0 = split * chunk;
-  const int ntok = n - tok0 < chunk ? n - tok0 : chunk;  // >= 0
-  const int nsteps = (ntok + TPS - 1) / TPS;
+  const DecodeArgs& a;
+  const int lane, wave, tr, c;
+  const unsigned lane_off;  // this lane's element offset inside a [16][D] block (token tr)
+  const float qk_scale;
+  const T* __restrict__ kbase;
+  const T* __restrict__ vbase;
+  Vec8<T> q[G];
+  float m[G], l[G], acc[G][8];
 
-  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.k);
-  const T* __restrict__ vbase = reinterpret_cast<const T*>(a.v);
+  __device__ __forceinline__ explicit Worker(const DecodeArgs& args)
+      : a(args),
+        lane(threadIdx.x & 63),
+        wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
+        tr((threadIdx.x & 63) / LPT),
+        c((threadIdx.x & 63) % LPT),
+        lane_off((unsigned)(((threadIdx.x & 63) / LPT) * D + ((threadIdx.x & 63) % LPT) * 8)),
+        qk_scale(args.scale * kLog2e),
+        kbase(reinterpret_cast<const T*>(args.k)),
+        vbase(reinterpret_cast<const T*>(args.v)) {}
 
-  // block ids of this chunk: lane i holds logical block (tok0/16 + i)
-  int ids = 0;
-  size_t head_base = 0;
-  if constexpr (!PADDED) {
-    const int nblk = (ntok + kBlock - 1) / kBlock;
-    if (lane < nblk) {
-      int v = a.block_tables[(size_t)row * a.bt_stride + (tok0 >> 4) + lane];
-      ids = (unsigned)v < (unsigned)a.num_blocks ? v : 0;
-    }
-  } else {
-    head_base = ((size_t)row * a.H_kv + g) * (size_t)a.seq_cap * D;
-  }
-
-  // queries of the G heads of group g, this lane's 16 dims
-  QRegs<T, G> q;
-  q.load(reinterpret_cast<const T*>(a.q) + (size_t)row * a.q_row_stride + (size_t)g * G * D + c * 16,
-         D);
-  const float qk_scale = a.scale * kLog2e;
-
-  float m[G], l[G], acc[G][16];
+  // queries of the G heads of KV head g in row `row`: this lane's 8 dims of each
+  __device__ __forceinline__ void load_q(Vec8<T>* qq, int row, int g) const {
+    const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)row * a.q_row_stride +
+                  (size_t)g * G * D + c * 8;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
+    for (int h = 0; h < G; ++h) qq[h].load_cached(qp + (size_t)h * D);
   }
 
-  // element offset of this lane's 16 dims of token t (relative to the chunk start)
-  auto offset_of = [&](int step, int t) -> size_t {
+  // block ids of a chunk: lane i holds logical block tok0/16 + i (index clamped into the row's
+  // table; entries past the chunk are never used; ids clamped into the pool)
+  __device__ __forceinline__ int load_ids(int row, int tok0) const {
     if constexpr (PADDED) {
-      int tv = tok0 + t;
-      int col = tv < gap_s ? tv : tv + gap_shift;
-      col = col < a.kv_cols ? col : a.kv_cols - 1;
-      return head_base + (size_t)col * D + c * 16;
+      return 0;
     } else {
-      int pb;
-      if constexpr (TPS <= kBlock) {
-        pb = __builtin_amdgcn_readlane(ids, (step * TPS) >> 4);
-      } else {
-        pb = __shfl(ids, t >> 4);
-      }
-      return (((size_t)pb * a.H_kv + g) * kBlock + (t & (kBlock - 1))) * D + c * 16;
+      const int e = (tok0 >> 4) + lane;
+      const int v = a.block_tables[(size_t)row * a.bt_stride + (e < a.bt_stride ? e : a.bt_stride - 1)];
+      return v;
     }
-  };
-
-  const int my_steps = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
-  Frag<T> cur;
-  if (my_steps > 0) {
-    const int t = wave * TPS + tl;
-    const size_t off = offset_of(wave, t);
-    cur.load(kbase + off, vbase + off);
   }
-  for (int i = 0; i < my_steps; ++i) {
-    const int step = wave + i * kWaves;
-    Frag<T> nxt;
-    if (i + 1 < my_steps) {
-      const int s2 = step + kWaves;
-      const size_t off = offset_of(s2, s2 * TPS + tl);
-      nxt.load(kbase + off, vbase + off);
-    }
-    const int t = step * TPS + tl;
-    const bool tail = (step + 1) * TPS > ntok;  // wave-uniform
-    const bool valid = t < ntok;
-    if (tail && !valid) cur.zero_v();
+  __device__ __forceinline__ int clamp_id(int v) const {
+    return (unsigned)v < (unsigned)a.num_blocks ? v : 0;
+  }
 
-    float s[G];
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = token_lane_sum<LPT>(q.dot(h, cur)) * qk_scale;
-    if (tail) {
+    for (int h = 0; h < G; ++h) {
+      m[h] = kNegInf;
+      l[h] = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = valid ? s[h] : kNegInf;
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
+  }
+
+  __device__ __forceinline__ void load_block(Frag& f, const Chunk& ch, int ids, int blk) const {
+    if constexpr (PADDED) {
+      const size_t head_base = ((size_t)ch.row * a.H_kv + ch.g) * (size_t)a.seq_cap * D;
+#pragma unroll
+      for (int j = 0; j < TPL; ++j) {
+        const int tv = ch.tok0 + blk * kBlock + tr + j * TPI;
+        int col = tv < ch.gap_s ? tv : tv + ch.gap_shift;
+        col = col < a.kv_cols ? col : a.kv_cols - 1;
+        const size_t off = head_base + (size_t)col * D + c * 8;
+        f.k[j].load(kbase + off);
+        f.v[j].load(vbase + off);
+      }
+    } else {
+      const int pb = clamp_id(__builtin_amdgcn_readlane(ids, blk));
+      const size_t boff = ((size_t)pb * a.H_kv + ch.g) * (size_t)(kBlock * D);
+      // uniform block base + a 32-bit lane byte offset: the scalar-base form of the global load
+      const char* kb = reinterpret_cast<const char*>(kbase + boff);
+      const char* vb = reinterpret_cast<const char*>(vbase + boff);
+      const unsigned lb = lane_off * (unsigned)sizeof(T);
+#pragma unroll
+      for (int j = 0; j < TPL; ++j) {
+        const unsigned o = lb + (unsigned)(j * TPI * D * sizeof(T));
+        f.k[j].load(reinterpret_cast<const T*>(kb + o));
+        f.v[j].load(reinterpret_cast<const T*>(vb + o));
+      }
+    }
+  }
+
+  // Online-softmax update with one block of the chunk. MASK is for the chunk's partial last block:
+  // its slots past the chunk end may hold anything (NaN included) and never reach the sums.
+  template <bool MASK>
+  __device__ __forceinline__ void update(const Frag& f, const Chunk& ch, int blk) {
+    bool valid[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) valid[j] = !MASK || blk * kBlock + tr + j * TPI < ch.ntok;
+    // raw scores q.k; the scale (times log2 e) is applied to the block maximum and inside the
+    // exponent's fused multiply-add
+    float s[TPL][G];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s[j][h] = token_lane_sum<LPT>(q[h].dot(f.k[j]));
+        if (MASK) s[j][h] = valid[j] ? s[j][h] : kNegInf;
+      }
+    float smax[G];
     bool need = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) need |= s[h] > m[h] + kRescale;
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int j = 1; j < TPL; ++j) mx = fmaxf(mx, s[j][h]);
+      smax[h] = mx * qk_scale;
+      need |= smax[h] > m[h] + kRescale;
+    }
     if (need) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = s[h] > m[h] + kRescale ? s[h] : m[h];
+        const float mn = smax[h] > m[h] + kRescale ? smax[h] : m[h];
         const float al = exp2_fast(m[h] - mn);
         l[h] *= al;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[h][e] *= al;
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
         m[h] = mn;
       }
     }
-    float p[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      p[h] = exp2_fast(s[h] - m[h]);
-      if (tail) p[h] = valid ? p[h] : 0.f;
-      l[h] += p[h];
-    }
-    float vf[16];
-    cur.v_f32(vf);
+    for (int j = 0; j < TPL; ++j) {
+      float vf[8];
+      f.v[j].to_f32(vf);
+      if (MASK) {
+        // masked slots may hold anything (NaN included): never let them reach the sums
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int e = 0; e < 8; ++e) vf[e] = valid[j] ? vf[e] : 0.f;
+      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
-    cur = nxt;
-  }
-
-  // ---- merge the lanes' streams to one (m, l, acc) per wave: DPP inside each 16-lane row, then
-  // a swizzle across the two rows of each half-wave and a swap across the two half-waves ----------
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
+      for (int h = 0; h < G; ++h) {
+        float p = exp2_fast(fmaf(s[j][h], qk_scale, -m[h]));
+        // a stream that has seen only masked tokens has m = -inf: exp2(-inf - -inf) is NaN
+        if (MASK) p = valid[j] ? p : 0.f;
+        l[h] += p;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mr = row_stream_reduce<LPT, true>(m[h]);
-    mr = fmaxf(mr, swap_rows16(mr));
-    mr = fmaxf(mr, swap_halves32(mr));
-    const float f = (m[h] == kNegInf) ? 0.f : exp2_fast(m[h] - mr);
-    l[h] = wave_stream_sum<LPT>(l[h] * f);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = wave_stream_sum<LPT>(acc[h][e] * f);
-    m[h] = mr;
-  }
-  if (lane < LPT) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s_acc[wave][h][c * 16 + e] = acc[h][e];
-      if (c == 0) {
-        s_m[wave][h] = m[h];
-        s_l[wave][h] = l[h];
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
       }
     }
   }
-  __syncthreads();
 
-  const int H_q = a.H_kv * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
-    float A = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_m[w][h];
-      const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - mx);
-      A = fmaf(f, s_acc[w][h][d], A);
-      L = fmaf(f, s_l[w][h], L);
+  __device__ __forceinline__ int blk_of(int i) const { return wave + i * kWaves; }
+  __device__ __forceinline__ int my_blocks(const Chunk& ch) const {
+    return wave < ch.nblk ? (ch.nblk - wave + kWaves - 1) / kWaves : 0;
+  }
+
+  // Stream this wave's blocks (wave, wave + kWaves, ...) of `ch`, whose first block is already in
+  // f0. With `nxt_first`, the first block of this wave in `nx` is loaded into f0 as the last
+  // prefetch, so the next chunk's data is in flight before this one's merge.
+  // Stream this wave's blocks (wave, wave + kWaves, ...) of `ch`, whose first block is already in
+  // f0; the next block is always in flight. Full blocks take the unmasked update; the chunk's
+  // partial last block (if this wave owns it) is taken last, masked. With `nxt_first`, the last
+  // prefetch is this wave's first block of the next chunk `nx`, left in f0.
+  __device__ __forceinline__ void run_blocks(Frag& f0, Frag& f1, const Chunk& ch, int ids, int my,
+                                             bool nxt_first, const Chunk& nx, int nx_ids) {
+    const bool own_tail = my > 0 && blk_of(my - 1) == ch.tail_blk;
+    const int full = own_tail ? my - 1 : my;
+    for (int i = 0; i < full; ++i) {
+      if (i + 1 < my) load_block(f1, ch, ids, blk_of(i + 1));
+      else if (nxt_first) load_block(f1, nx, nx_ids, wave);
+      update<false>(f0, ch, blk_of(i));
+      f0 = f1;
     }
-    const float o = L > 0.f ? A / L : 0.f;
-    const float lse2 = L > 0.f ? mx + __log2f(L) : kNegInf;
-    const int hq = g * G + h;
-    if (ns == 1) {
-      a.out[((size_t)row * H_q + hq) * D + d] = o;
-      if (a.lse != nullptr && d == 0) a.lse[(size_t)row * H_q + hq] = lse2 * kLn2;
-    } else {
-      const size_t pr = ((size_t)row * H_q + hq) * a.s_max + split;
-      a.part_o[pr * D + d] = o;
-      if (d == 0) a.part_lse[pr] = lse2;
+    if (own_tail) {
+      if (nxt_first) load_block(f1, nx, nx_ids, wave);
+      update<true>(f0, ch, blk_of(my - 1));
+      f0 = f1;
+    }
+    if (my == 0 && nxt_first) load_block(f0, nx, nx_ids, wave);
+  }
+
+  // Merge the lanes' streams to one (m, l, acc) per wave and park it in LDS (then a barrier).
+  __device__ __forceinline__ void merge_to_smem(Smem& sm) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mw = wave_stream_reduce<LPT, true>(m[h]);
+      const float f = (m[h] == kNegInf) ? 0.f : exp2_fast(m[h] - mw);
+      l[h] = wave_stream_reduce<LPT, false>(l[h] * f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = wave_stream_reduce<LPT, false>(acc[h][e] * f);
+      m[h] = mw;
+    }
+    if (lane < LPT) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.acc[wave][h][c * 8 + e] = acc[h][e];
+        if (c == 0) {
+          sm.m[wave][h] = m[h];
+          sm.l[wave][h] = l[h];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Combine the waves' parts and write out/lse (one split) or the split's partial.
+  __device__ __forceinline__ void write_result(const Smem& sm, const Chunk& ch) const {
+    const int H_q = a.H_kv * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+      const int h = idx / D;
+      const int d = idx % D;
+      float mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][h]);
+      float A = 0.f, L = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.m[w][h];
+        const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - mx);
+        A = fmaf(f, sm.acc[w][h][d], A);
+        L = fmaf(f, sm.l[w][h], L);
+      }
+      const float o = L > 0.f ? A / L : 0.f;
+      const float lse2 = L > 0.f ? mx + __log2f(L) : kNegInf;
+      const int hq = ch.g * G + h;
+      if (ch.ns == 1) {
+        a.out[((size_t)ch.row * H_q + hq) * D + d] = o;
+        if (a.lse != nullptr && d == 0) a.lse[(size_t)ch.row * H_q + hq] = lse2 * kLn2;
+      } else {
+        const size_t pr = ((size_t)ch.row * H_q + hq) * a.s_max + ch.split;
+        a.part_o[pr * D + d] = o;
+        if (d == 0) a.part_lse[pr] = lse2;
+      }
+    }
+  }
+};
+
+// Valid tokens of a row (and, padded, its gap start and width), lengths clamped to the bounds.
+template <bool PADDED>
+__device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_s, int* gap_shift) {
+  if constexpr (PADDED) {
+    const int cols = a.kv_cols;
+    const int gs = clampi(a.gap_start[row], 0, cols);
+    const int ge = clampi(a.gap_end[row], gs, cols);
+    *gap_s = gs;
+    *gap_shift = ge - gs;
+    return cols - (ge - gs);
+  } else {
+    *gap_s = 0;
+    *gap_shift = 0;
+    return clampi(a.kv_lens[row], 0, a.max_kv_len);
+  }
+}
+
+// ---- grid kernel: one workgroup per (KV head, row, split); splits past the row's end exit -------
+template <typename T, int D, int G, bool PADDED>
+__global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const DecodeArgs a) {
+  using W = Worker<T, D, G, PADDED>;
+  __shared__ typename W::Smem sm;
+  W w(a);
+  const int g = blockIdx.x;
+  const int row = blockIdx.y;
+  const int split = blockIdx.z;
+  const int chunk = chunk_tokens(D);
+  // issued before the row length is known, so their latency overlaps the length load
+  int ids = w.load_ids(row, split * chunk);
+  w.load_q(w.q, row, g);
+  int gap_s, gap_shift;
+  const int n = row_valid<PADDED>(a, row, &gap_s, &gap_shift);
+  const Chunk ch = make_chunk(row, g, split, n, gap_s, gap_shift, chunk);
+  if (split >= ch.ns) return;
+  w.reset();
+  typename W::Frag f0, f1;
+  const int my = w.my_blocks(ch);
+  if (my > 0) w.load_block(f0, ch, ids, w.blk_of(0));
+  w.run_blocks(f0, f1, ch, ids, my, false, ch, ids);
+  w.merge_to_smem(sm);
+  w.write_result(sm, ch);
+}
+
+// ---- persistent kernel --------------------------------------------------------------------------
+// A fixed grid of workgroups (as many as fit on the device) takes chunks from a counter in the
+// workspace, in an order that puts every row's full chunks first and the shorter last chunks at the
+// end. A workgroup knows its next chunk one step ahead: that chunk's block ids and queries load
+// while the current one streams, and its first K/V block is the current chunk's last prefetch.
+// The split of each row is the same as in the grid kernel, so results are identical.
+constexpr int kMaxRows = 1024;
+
+template <bool PADDED>
+struct RowSmem {
+  int n[kMaxRows];
+  int full_pre[kMaxRows + 1];  // exclusive prefix over rows of full chunks (n / chunk)
+  int part_pre[kMaxRows + 1];  // exclusive prefix over rows of last partial chunks (0 or 1)
+  int gap_s[PADDED ? kMaxRows : 1];
+  int gap_shift[PADDED ? kMaxRows : 1];
+  int wave_tot[2][kWaves];
+  int ticket[3];
+};
+
+// Exclusive prefix sums over rows of (full, partial) chunk counts into LDS; rows are split into
+// contiguous runs per thread, then a two-level scan over threads.
+template <bool PADDED>
+__device__ void scan_rows(RowSmem<PADDED>& rs, int B, int chunk) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kPer = (kMaxRows + kThreads - 1) / kThreads;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  int fl[kPer], pl[kPer];
+  int fs = 0, ps = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = t * kPer + i;
+    int f = 0, p = 0;
+    if (b < B) {
+      const int n = rs.n[b];
+      f = n / chunk;
+      p = (n % chunk != 0 || n == 0) ? 1 : 0;
+    }
+    fl[i] = fs;
+    pl[i] = ps;
+    fs += f;
+    ps += p;
+  }
+  // inclusive scan of the per-thread totals within the wave
+  int fi = fs, pi = ps;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int fu = __shfl_up(fi, o);
+    const int pu = __shfl_up(pi, o);
+    if (lane >= o) {
+      fi += fu;
+      pi += pu;
+    }
+  }
+  if (lane == 63) {
+    rs.wave_tot[0][wave] = fi;
+    rs.wave_tot[1][wave] = pi;
+  }
+  __syncthreads();
+  int fw = 0, pw = 0;
+  for (int w2 = 0; w2 < wave; ++w2) {
+    fw += rs.wave_tot[0][w2];
+    pw += rs.wave_tot[1][w2];
+  }
+  const int fbase = fw + fi - fs, pbase = pw + pi - ps;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = t * kPer + i;
+    if (b < B) {
+      rs.full_pre[b] = fbase + fl[i];
+      rs.part_pre[b] = pbase + pl[i];
+    }
+  }
+  if (t == 0) {
+    int ft = 0, pt = 0;
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      ft += rs.wave_tot[0][w2];
+      pt += rs.wave_tot[1][w2];
+    }
+    rs.full_pre[B] = ft;
+    rs.part_pre[B] = pt;
+  }
+  __syncthreads();
+}
+
+// LDS reads land in vector registers; every workgroup-uniform value read from LDS goes through
+// readfirstlane so that the compiler keeps it (and all that derives from it) scalar.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ Chunk uni_chunk(const Chunk& c) {
+  Chunk u;
+  u.row = uni(c.row);
+  u.g = uni(c.g);
+  u.split = uni(c.split);
+  u.tok0 = uni(c.tok0);
+  u.ntok = uni(c.ntok);
+  u.nblk = uni(c.nblk);
+  u.tail_blk = uni(c.tail_blk);
+  u.ns = uni(c.ns);
+  u.gap_s = uni(c.gap_s);
+  u.gap_shift = uni(c.gap_shift);
+  return u;
+}
+
+// last index b in [0, B) with pre[b] <= k (pre non-decreasing, pre[B] > k)
+__device__ __forceinline__ int find_row(const int* pre, int B, int k) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uni(pre[mid]) <= k) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <bool PADDED>
+__device__ __forceinline__ Chunk decode_ticket(const RowSmem<PADDED>& rs, int B, int H_kv,
+                                               int n_full, int t, int chunk) {
+  int k = t / H_kv;
+  const int g = t - k * H_kv;
+  int row, split;
+  if (k < n_full) {
+    row = find_row(rs.full_pre, B, k);
+    split = k - rs.full_pre[row];
+  } else {
+    k -= n_full;
+    row = find_row(rs.part_pre, B, k);
+    split = rs.n[row] / chunk;
+  }
+  const int gs = PADDED ? uni(rs.gap_s[row]) : 0;
+  const int gsh = PADDED ? uni(rs.gap_shift[row]) : 0;
+  return make_chunk(uni(row), uni(g), uni(split), uni(rs.n[row]), gs, gsh, chunk);
+}
+
+template <typename T, int D, int G, bool PADDED>
+__global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(const DecodeArgs a) {
+  using W = Worker<T, D, G, PADDED>;
+  __shared__ typename W::Smem sm;
+  __shared__ RowSmem<PADDED> rs;
+  W w(a);
+  const int B = a.batch;
+  const int chunk = chunk_tokens(D);
+  int* counter = a.counter;
+
+  if (threadIdx.x == 0) {
+    rs.ticket[0] = atomicAdd(counter, 1);
+    rs.ticket[1] = atomicAdd(counter, 1);
+  }
+  for (int b = threadIdx.x; b < B; b += 64 * kWaves) {
+    int gs, gsh;
+    rs.n[b] = row_valid<PADDED>(a, b, &gs, &gsh);
+    if constexpr (PADDED) {
+      rs.gap_s[b] = gs;
+      rs.gap_shift[b] = gsh;
+    }
+  }
+  __syncthreads();
+  scan_rows<PADDED>(rs, B, chunk);
+  const int n_full = uni(rs.full_pre[B]);
+  const int n_items = (n_full + uni(rs.part_pre[B])) * a.H_kv;
+
+  const int t_cur = uni(rs.ticket[0]);
+  const int t_nxt = uni(rs.ticket[1]);
+  if (t_cur >= n_items) return;  // uniform: no work left for this workgroup
+  Chunk cur = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_cur, chunk);
+  int ids = w.load_ids(cur.row, cur.tok0);
+  w.load_q(w.q, cur.row, cur.g);
+  bool has_nx = t_nxt < n_items;
+  Chunk nx = has_nx ? decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_nxt, chunk) : cur;
+  int nx_ids = has_nx ? w.load_ids(nx.row, nx.tok0) : 0;
+  Vec8<T> nx_q[G];
+  if (has_nx) w.load_q(nx_q, nx.row, nx.g);
+
+  typename W::Frag f0, f1;
+  int my = w.my_blocks(cur);
+  if (my > 0) w.load_block(f0, cur, ids, w.blk_of(0));
+  for (int k = 0;; ++k) {
+    // the chunk after next: its ticket is read after this chunk's merge barrier
+    if (threadIdx.x == 0 && has_nx) rs.ticket[(k + 2) % 3] = atomicAdd(counter, 1);
+    w.reset();
+    const bool nxt_first = has_nx && w.my_blocks(nx) > 0;
+    w.run_blocks(f0, f1, cur, ids, my, nxt_first, nx, nx_ids);
+    w.merge_to_smem(sm);
+    int t_nn = 0;
+    Chunk nn = cur;
+    if (has_nx) {
+      t_nn = uni(rs.ticket[(k + 2) % 3]);
+      if (t_nn < n_items) nn = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_nn, chunk);
+    }
+    w.write_result(sm, cur);
+    __syncthreads();  // the merge area is reused by the next chunk
+    if (!has_nx) break;
+    cur = uni_chunk(nx);
+    ids = nx_ids;
+#pragma unroll
+    for (int h = 0; h < G; ++h) w.q[h] = nx_q[h];
+    my = w.my_blocks(cur);
+    has_nx = t_nn < n_items;
+    if (has_nx) {
+      nx = uni_chunk(nn);
+      nx_ids = w.load_ids(nx.row, nx.tok0);
+      w.load_q(nx_q, nx.row, nx.g);
     }
   }
 }
 
 // Merge the split partials of one (row, query head): out = sum_s w_s o_s / sum_s w_s with
-// w_s = 2^(lse_s - max lse), lse = max + log2(sum w_s) (returned in natural-log units).
+// w_s = 2^(lse_s - max lse); lse = max + log2(sum w_s), returned in natural-log units.
+// One wave per (row, head): lane s reads partial lse_s, the weights are reduced across the wave,
+// then each lane accumulates its output dims over the splits.
 template <bool PADDED>
-__global__ __launch_bounds__(128) void lse_reduce_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
   const int hq = blockIdx.x;
   const int row = blockIdx.y;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
+  // the decode kernel has finished: re-arm its work counter for the next call
+  if (a.counter != nullptr && hq == 0 && row == 0 && lane == 0) *a.counter = 0;
   int n;
   if constexpr (PADDED) {
     const int gs = clampi(a.gap_start[row], 0, a.kv_cols);
@@ -418,31 +718,78 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(const DecodeArgs a) {
     n = clampi(a.kv_lens[row], 0, a.max_kv_len);
   }
   const int ns = num_splits(n, chunk_tokens(a.D));
-  if (ns <= 1 || d >= a.D) return;
-  const int H_q = a.H_q;
-  const size_t base = ((size_t)row * H_q + hq) * a.s_max;
+  if (ns <= 1) return;
+  const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
+  // pass 1: the maximum partial lse (lanes stride over the splits)
   float mx = kNegInf;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[base + s]);
-  float A = 0.f, W = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = a.part_lse[base + s];
-    const float f = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
-    W += f;
-    A = fmaf(f, a.part_o[(base + s) * a.D + d], A);
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  // pass 2: weights and the weighted sum of partial outputs (lane = output dim)
+  float W = 0.f;
+  float A[2] = {0.f, 0.f};
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float ls = s < ns ? a.part_lse[base + s] : kNegInf;
+    const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
+    const int cnt = ns - s0 < 64 ? ns - s0 : 64;
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __shfl(w, k);
+      W += wk;
+      const float* po = a.part_o + (base + s0 + k) * a.D;
+      if (lane < a.D) A[0] = fmaf(wk, po[lane], A[0]);
+      if (a.D > 64) A[1] = fmaf(wk, po[64 + lane], A[1]);
+    }
   }
-  a.out[((size_t)row * H_q + hq) * a.D + d] = W > 0.f ? A / W : 0.f;
-  if (a.lse != nullptr && d == 0)
-    a.lse[(size_t)row * H_q + hq] = W > 0.f ? (mx + __log2f(W)) * kLn2 : kNegInf;
+  float* out = a.out + ((size_t)row * a.H_q + hq) * a.D;
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  if (lane < a.D) out[lane] = W > 0.f ? A[0] * inv : 0.f;
+  if (a.D > 64) out[64 + lane] = W > 0.f ? A[1] * inv : 0.f;
+  if (a.lse != nullptr && lane == 0)
+    a.lse[(size_t)row * a.H_q + hq] = W > 0.f ? (mx + __log2f(W)) * kLn2 : kNegInf;
+}
+
+// Workgroups of `kernel` that fit on the current device at once (cached per device).
+template <typename K>
+int resident_workgroups(K kernel) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, 0) != hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cache[dev] = per_cu * cus;
+  return cache[dev];
+}
+
+template <typename T, int D, int G, bool PADDED>
+hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
+  const long long items = (long long)a.batch * a.H_kv * a.s_max;
+  // Few (row, KV head) pairs with many splits each (long rows): most of a split grid's workgroups
+  // would find nothing to do, so the persistent kernel takes over. Otherwise the split grid runs,
+  // with more waves per SIMD. Both cut rows into the same chunks: their results are identical.
+  if (PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows) {
+    auto kern = decode_persistent_kernel<T, D, G, PADDED>;
+    const int resident = resident_workgroups(kern);
+    if (resident > 0 && (long long)a.batch * a.H_kv * 2 <= resident) {
+      const int grid = (int)(items < resident ? items : resident);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  dim3 grid(a.H_kv, a.batch, a.s_max);
+  hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED>), grid, dim3(64 * kWaves), 0, stream,
+                     a);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.H_kv, a.batch, a.s_max);
-  if (a.layout == PA_PADDED)
-    hipLaunchKernelGGL((decode_vector_kernel<T, D, G, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_vector_kernel<T, D, G, false>), grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return a.layout == PA_PADDED ? launch_layout<T, D, G, true>(a, stream)
+                               : launch_layout<T, D, G, false>(a, stream);
 }
 
 template <typename T, int D>
@@ -475,9 +822,9 @@ hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.H_q * a.n_q, a.batch);
   if (a.layout == PA_PADDED)
-    hipLaunchKernelGGL(lse_reduce_kernel<true>, grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(lse_reduce_kernel<true>, grid, dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel<false>, grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(lse_reduce_kernel<false>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

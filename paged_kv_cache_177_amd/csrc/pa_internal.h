@@ -15,8 +15,16 @@ constexpr int kBlock = 16;  // tokens per K/V block
 // chunk depends only on head_dim, so a row's split -- and with it the exact order of its fp32
 // reductions -- depends on that row's own length alone. chunk is a multiple of 16 and at most
 // 64 blocks, so one wave holds a chunk's block ids in one register.
+#ifndef PA_CHUNK_D128
+#define PA_CHUNK_D128 512
+#endif
+#ifndef PA_CHUNK_D64
+#define PA_CHUNK_D64 1024
+#endif
+static_assert(PA_CHUNK_D128 % 16 == 0 && PA_CHUNK_D128 <= 1024, "chunk: <= 64 blocks");
+static_assert(PA_CHUNK_D64 % 16 == 0 && PA_CHUNK_D64 <= 1024, "chunk: <= 64 blocks");
 __host__ __device__ inline int chunk_tokens(int head_dim) {
-  return head_dim >= 128 ? 512 : 1024;
+  return head_dim >= 128 ? PA_CHUNK_D128 : PA_CHUNK_D64;
 }
 __host__ __device__ inline int num_splits(int n, int chunk) {
   return n <= 0 ? 1 : (n + chunk - 1) / chunk;
@@ -63,24 +71,29 @@ struct DecodeArgs {
   float* lse;
   float* part_o;    // [batch][n_q*H_q][s_max][D]
   float* part_lse;  // [batch][n_q*H_q][s_max] (log2 domain)
+  int* counter;     // work counter of the persistent decode kernel (0 between calls), or NULL
 };
 
-// Bytes of split-K partials for a decode call (0 when no row can split).
+// Workspace of a decode call (0 bytes when no row can split):
+//   [256 B: work counter (int) of the persistent kernel; must be 0 before the first call, each call
+//    leaves it 0] [split partial outputs, fp32] [split partial log-sum-exps, fp32]
+constexpr size_t kCounterBytes = 256;
 inline size_t decode_workspace_bytes(int batch, int n_q, int H_q, int D, int s_max) {
   if (s_max <= 1) return 0;
   size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
-  size_t bytes = rows * (size_t)D * sizeof(float);
-  bytes = (bytes + 255) & ~(size_t)255;
-  bytes += rows * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  size_t bytes = kCounterBytes;
+  bytes += (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
+  bytes += (rows * sizeof(float) + 255) & ~(size_t)255;
+  return bytes;
 }
 
 inline void carve_workspace(void* ws, int batch, int n_q, int H_q, int D, int s_max,
-                            float** part_o, float** part_lse) {
+                            int** counter, float** part_o, float** part_lse) {
   size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
   size_t o_bytes = (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
-  *part_o = (float*)ws;
-  *part_lse = (float*)((char*)ws + o_bytes);
+  *counter = (int*)ws;
+  *part_o = (float*)((char*)ws + kCounterBytes);
+  *part_lse = (float*)((char*)ws + kCounterBytes + o_bytes);
 }
 
 // ---- launchers (each returns the hipGetLastError of its launches) -----------------------------

@@ -68,7 +68,8 @@ class PagedStep:
                                      self.block_tables, self.bt_stride, self.kv_lens, self.batch,
                                      self.max_kv_len, case.scale, out=self.out,
                                      query_workspace=True)
-        self.workspace = (torch.empty(need, dtype=torch.uint8, device=device) if need > 0
+        # zero-filled once: its first bytes are the decode kernel's work counter
+        self.workspace = (torch.zeros(need, dtype=torch.uint8, device=device) if need > 0
                           else None)
 
     @property

@@ -119,13 +119,13 @@ def test_decode_workspace_query():
                                  out=FAKE, query_workspace=True)
     rows = 128 * 32 * 9
     o = (rows * 64 * 4 + 255) // 256 * 256
-    assert need == o + (rows * 4 + 255) // 256 * 256
+    assert need == 256 + o + (rows * 4 + 255) // 256 * 256
     # head_dim 128 uses 512-token chunks
     p = _fake_pool(head_dim=128)
     need = B.pa_decode_attention(p, FAKE, 32 * 128, 1, 32, FAKE, 64, FAKE, 4, 1024, 0.1,
                                  out=FAKE, query_workspace=True)
     rows = 4 * 32 * 2
-    assert need == (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert need == 256 + (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -220,3 +220,12 @@ def test_append_argument_errors():
     assert call(batch=0) == B.PA_OK                     # empty batch: a no-op, no launch
     p.rope_cos = None
     assert call() == B.PA_ERR_NULL                      # pool with RoPE but no table pointer
+
+
+@pytest.mark.parametrize("scale", [-0.125, float("nan"), float("inf")])
+def test_decode_rejects_bad_scale(scale):
+    p = _fake_pool()
+    with pytest.raises(B.PaError) as e:
+        B.pa_decode_attention(p, FAKE, 32 * 64, 1, 32, FAKE, 64, FAKE, 4, 1000, scale, out=FAKE,
+                              query_workspace=True)
+    assert e.value.status == B.PA_ERR_SHAPE

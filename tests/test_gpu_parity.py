@@ -117,7 +117,23 @@ def test_b128_full_size_sampled_rows(b128_case):
     c = b128_case
     order = np.argsort(c.kv_lens)
     rows = np.unique(np.concatenate([order[:3], order[-3:], order[::21]]))
-    run_and_check_paged(c, rows=rows)
+    r, _, _ = run_and_check_paged(c, rows=rows)
+    # a row decoded on its own (few rows: the persistent launch) gives the same bits as in the
+    # full batch (many rows: the split grid)
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    for b in [int(order[0]), int(order[-1]), 77]:
+        cb = W.PagedCase(**{**c.__dict__,
+                            "n_ctx": c.n_ctx[b:b + 1], "positions": c.positions[b:b + 1],
+                            "dest": c.dest[b:b + 1], "kv_lens": c.kv_lens[b:b + 1],
+                            "block_tables": c.block_tables[b:b + 1],
+                            "k_new": c.k_new[b:b + 1], "v_new": c.v_new[b:b + 1],
+                            "q": c.q[b:b + 1]})
+        rb = PagedStep(cb)
+        rb.kv = r.kv  # share the already-appended pool
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b])
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
 @pytest.fixture(scope="module")
