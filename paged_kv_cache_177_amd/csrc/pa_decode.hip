@@ -700,51 +700,68 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(const De
 
 // Merge the split partials of one (row, query head): out = sum_s w_s o_s / sum_s w_s with
 // w_s = 2^(lse_s - max lse); lse = max + log2(sum w_s), returned in natural-log units.
-// One wave per (row, head): lane s reads partial lse_s, the weights are reduced across the wave,
-// then each lane accumulates its output dims over the splits.
+// One wave per (row, head). It is latency-bound, so the chain of dependent loads is kept short:
+// the first 64 partial lse values load together with the row length (speculatively: the
+// workspace always holds s_max of them), and the partial outputs load in unrolled batches.
 template <bool PADDED>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
   const int hq = blockIdx.x;
   const int row = blockIdx.y;
   const int lane = threadIdx.x;
+  const int D = a.D;
   // the decode kernel has finished: re-arm its work counter for the next call
   if (a.counter != nullptr && hq == 0 && row == 0 && lane == 0) *a.counter = 0;
-  int n;
-  if constexpr (PADDED) {
-    const int gs = clampi(a.gap_start[row], 0, a.kv_cols);
-    const int ge = clampi(a.gap_end[row], gs, a.kv_cols);
-    n = a.kv_cols - (ge - gs);
-  } else {
-    n = clampi(a.kv_lens[row], 0, a.max_kv_len);
-  }
-  const int ns = num_splits(n, chunk_tokens(a.D));
-  if (ns <= 1) return;
   const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
-  // pass 1: the maximum partial lse (lanes stride over the splits)
-  float mx = kNegInf;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
+  const float lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
+  int gs, gsh;
+  const int n = row_valid<PADDED>(a, row, &gs, &gsh);
+  const int ns = num_splits(n, chunk_tokens(D));
+  if (ns <= 1) return;
+
+  // maximum over the splits' lse
+  float mx = lane < ns ? lse0 : kNegInf;
+  for (int s = 64 + lane; s < ns; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  // pass 2: weights and the weighted sum of partial outputs (lane = output dim)
-  float W = 0.f;
-  float A[2] = {0.f, 0.f};
+
+  float W = 0.f, A0 = 0.f, A1 = 0.f;
+  const float* po = a.part_o + base * D;
   for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    const float ls = s < ns ? a.part_lse[base + s] : kNegInf;
+    float ls = s0 == 0 ? lse0 : (s0 + lane < ns ? a.part_lse[base + s0 + lane] : kNegInf);
+    if (s0 + lane >= ns) ls = kNegInf;
     const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
+    W += w;
+    const int wb = __builtin_bit_cast(int, w);
     const int cnt = ns - s0 < 64 ? ns - s0 : 64;
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __shfl(w, k);
-      W += wk;
-      const float* po = a.part_o + (base + s0 + k) * a.D;
-      if (lane < a.D) A[0] = fmaf(wk, po[lane], A[0]);
-      if (a.D > 64) A[1] = fmaf(wk, po[64 + lane], A[1]);
+    int k = 0;
+    for (; k + 8 <= cnt; k += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float* p = po + (size_t)(s0 + k + i) * D;
+        v0[i] = lane < D ? p[lane] : 0.f;
+        v1[i] = D > 64 ? p[64 + lane] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, k + i));
+        A0 = fmaf(wk, v0[i], A0);
+        A1 = fmaf(wk, v1[i], A1);
+      }
+    }
+    for (; k < cnt; ++k) {
+      const float* p = po + (size_t)(s0 + k) * D;
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, k));
+      if (lane < D) A0 = fmaf(wk, p[lane], A0);
+      if (D > 64) A1 = fmaf(wk, p[64 + lane], A1);
     }
   }
-  float* out = a.out + ((size_t)row * a.H_q + hq) * a.D;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  float* out = a.out + ((size_t)row * a.H_q + hq) * D;
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  if (lane < a.D) out[lane] = W > 0.f ? A[0] * inv : 0.f;
-  if (a.D > 64) out[64 + lane] = W > 0.f ? A[1] * inv : 0.f;
+  if (lane < D) out[lane] = A0 * inv;
+  if (D > 64) out[64 + lane] = A1 * inv;
   if (a.lse != nullptr && lane == 0)
     a.lse[(size_t)row * a.H_q + hq] = W > 0.f ? (mx + __log2f(W)) * kLn2 : kNegInf;
 }

@@ -124,3 +124,40 @@ class MultiQueryStep:
                               self.bt_stride, self.kv_lens, self.batch, self.max_kv_len, c.scale,
                               out=self.out, lse=self.lse if with_lse else None,
                               stream=self.stream)
+
+
+class PaddedLockstep:
+    """A right-padded lockstep batch: pool [batch_cap][H_kv][seq_cap][D] plus the calls on it.
+
+    The caller fills ``kv.k``/``kv.v`` (torch views) and passes per-step device arrays."""
+
+    def __init__(self, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 batch_cap: int, seq_cap: int, rope_theta: float = 0.0, rope_max_pos: int = 0,
+                 device: str = "cuda", stream=None):
+        self.dtype = dtype
+        self.H_q, self.H_kv, self.D = num_q_heads, num_kv_heads, head_dim
+        self.device = device
+        self.stream = stream
+        desc = B.make_desc("padded", dtype, num_kv_heads, head_dim, batch_cap=batch_cap,
+                           seq_cap=seq_cap, rope_max_pos=rope_max_pos, rope_theta=rope_theta)
+        self.kv = B.alloc_pool(desc, device=device, stream=stream)
+        self.rope = rope_max_pos > 0
+        self._ws = None
+
+    def append(self, positions, dest, k_new, v_new, q_in=None, q_out=None):
+        B.pa_append_kv(self.kv.pool, None, 1, positions, dest, k_new, v_new, q_in, q_out,
+                       self.H_q if q_in is not None else 0, positions.shape[0],
+                       stream=self.stream)
+
+    def decode(self, q, gap_start, gap_end, kv_cols: int, scale: float):
+        batch = q.shape[0]
+        out = torch.empty((batch, self.H_q, self.D), dtype=torch.float32, device=self.device)
+        lse = torch.empty((batch, self.H_q), dtype=torch.float32, device=self.device)
+        need = B.pa_decode_attention_padded(self.kv.pool, q, self.H_q, batch, gap_start, gap_end,
+                                            kv_cols, scale, out=out, query_workspace=True)
+        if need > 0 and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        B.pa_decode_attention_padded(self.kv.pool, q, self.H_q, batch, gap_start, gap_end, kv_cols,
+                                     scale, workspace=self._ws if need > 0 else None, out=out,
+                                     lse=lse, stream=self.stream)
+        return out, lse

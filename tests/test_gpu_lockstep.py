@@ -1,0 +1,209 @@
+"""The B=16 lockstep protocol on the GPU: 32 consecutive decode steps over 16 ragged rows, two rows
+leaving and two sequences joining at step 16, blocks allocated on demand from a shuffled pool
+(LIFO free list, freed blocks recycled). Every step runs append + paged decode and, in parallel,
+the right-padded lockstep form (re-assembled at the join: each surviving row keeps its prefix and
+its decode columns, the gap is dropped). The oracle follows the same steps on its own copies of
+both pools."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from paged_kv_cache_177_amd import binding as B
+from paged_kv_cache_177_amd.blocks import BlockAllocator, SequenceBlocks, block_table_array
+from paged_kv_cache_177_amd.runner import PaddedLockstep, to_numpy, to_torch
+
+from _parity import assert_attention_close, log
+
+pytestmark = pytest.mark.gpu
+
+BS = 16
+
+
+def _stack(rows):
+    return np.ascontiguousarray(np.stack(rows))
+
+
+class PagedSide:
+    """Host (oracle) and device copies of the paged pool, the allocator and the block tables."""
+
+    def __init__(self, plan):
+        self.plan = plan
+        H, D = plan.num_kv_heads, plan.head_dim
+        perm = plan.perm
+        self.poison = int(perm[-1])
+        self.seq = {}
+        off = 0
+        for sid in range(16):
+            k = math.ceil(plan.seq_ctx(sid) / BS)
+            self.seq[sid] = SequenceBlocks(perm[off:off + k])
+            off += k
+        self.alloc = BlockAllocator(perm[off:-1])
+        self.alloc.adopt(perm[:off])
+        shape = (plan.num_blocks, H, BS, D)
+        self.k = np.full(shape, W.POISON_BF16, np.uint16)
+        self.v = np.full(shape, W.POISON_BF16, np.uint16)
+        desc = B.make_desc("paged", "bf16", H, D, num_blocks=plan.num_blocks,
+                           rope_max_pos=plan.rope_max_pos, rope_theta=plan.rope_theta)
+        self.dev = B.alloc_pool(desc)
+        for sid in range(16):
+            self.write_history(sid, upload=False)
+        self.dev.k.copy_(to_torch(self.k, "bf16"))
+        self.dev.v.copy_(to_torch(self.v, "bf16"))
+        self.stride = math.ceil(plan.rope_max_pos / BS)
+        self.cos, self.sin = O.rope_tables(plan.rope_theta, plan.head_dim, plan.rope_max_pos)
+
+    def write_history(self, sid, upload=True):
+        kh, vh = self.plan.history(sid)
+        t = np.arange(len(kh))
+        blocks = np.asarray(self.seq[sid].blocks, np.int64)
+        blk, slot = blocks[t // BS], t % BS
+        self.k[blk, :, slot, :] = kh
+        self.v[blk, :, slot, :] = vh
+        if upload:
+            bt = torch.from_numpy(blk).cuda()
+            st = torch.from_numpy(slot.astype(np.int64)).cuda()
+            self.dev.k[bt, :, st, :] = to_torch(kh, "bf16").cuda()
+            self.dev.v[bt, :, st, :] = to_torch(vh, "bf16").cuda()
+
+    def release(self, sid):
+        """A sequence leaves: its blocks go back on the free list, poisoned on both sides."""
+        blocks = self.seq.pop(sid).blocks
+        self.alloc.free(blocks)
+        self.k[blocks] = W.POISON_BF16
+        self.v[blocks] = W.POISON_BF16
+        idx = torch.tensor(blocks, device="cuda")
+        self.dev.k[idx] = float("nan")
+        self.dev.v[idx] = float("nan")
+
+    def join(self, sid):
+        n = self.plan.seq_ctx(sid)
+        s = SequenceBlocks()
+        if n > 0:
+            s.ensure_token(n - 1, self.alloc)
+        self.seq[sid] = s
+        self.write_history(sid)
+
+
+def test_b16_lockstep_protocol():
+    plan = W.b16_plan()
+    log(f"[lockstep] contexts {plan.n_ctx0.tolist()} leave {plan.leave_slots.tolist()} "
+        f"join {plan.join_ctx.tolist()} pool {plan.num_blocks} blocks")
+    H_q, H, D, scale = plan.num_q_heads, plan.num_kv_heads, plan.head_dim, plan.scale
+    P = PagedSide(plan)
+    sched = plan.schedule()
+    seq_cap = 2200
+    ws = None
+
+    # padded form: segment 1 assembled from the initial histories
+    def assemble(histories):
+        kp, vp, prefix, plen = O.assemble_padded(histories, seq_cap, W.POISON_BF16)
+        L = PaddedLockstep("bf16", H_q, H, D, 16, seq_cap, rope_theta=plan.rope_theta,
+                           rope_max_pos=plan.rope_max_pos)
+        L.kv.k.copy_(to_torch(kp, "bf16"))
+        L.kv.v.copy_(to_torch(vp, "bf16"))
+        return L, kp, vp, prefix, plen
+
+    hist0 = [tuple(np.ascontiguousarray(np.moveaxis(a, 0, 1)) for a in plan.history(sid))
+             for sid in range(16)]
+    L, kpad, vpad, prefix, plen = assemble(hist0)
+    seg_start = 0
+
+    for s, rows in enumerate(sched):
+        if s == plan.join_step:
+            # paged: leavers free their blocks, joiners take (recycled) blocks for their history
+            for slot in plan.leave_slots.tolist():
+                P.release(sched[s - 1][slot][1])
+            for slot, sid, _ in rows:
+                if sid >= 16:
+                    P.join(sid)
+            # padded: extract every surviving row (prefix + decode columns), add the joiners,
+            # re-assemble; the GPU pool is rebuilt from its own extracted rows
+            new_hist, dev_hist = [], []
+            cols_done = s - seg_start
+            for slot, sid, _ in rows:
+                if sid >= 16:
+                    kh, vh = plan.history(sid)
+                    h = (np.ascontiguousarray(np.moveaxis(kh, 0, 1)),
+                         np.ascontiguousarray(np.moveaxis(vh, 0, 1)))
+                    new_hist.append(h)
+                    dev_hist.append(h)
+                else:
+                    new_hist.append(O.extract_row_padded(kpad, vpad, slot, int(prefix[slot]), plen,
+                                                         cols_done))
+                    cols = np.concatenate([np.arange(int(prefix[slot])),
+                                           np.arange(plen, plen + cols_done)])
+                    ci = torch.from_numpy(cols).cuda()
+                    dev_hist.append((to_numpy(L.kv.k[slot][:, ci, :], "bf16"),
+                                     to_numpy(L.kv.v[slot][:, ci, :], "bf16")))
+            for (a, b), (c, d) in zip(new_hist, dev_hist):
+                np.testing.assert_array_equal(a, c)
+                np.testing.assert_array_equal(b, d)
+            L, kpad, vpad, prefix, plen = assemble(new_hist)
+            seg_start = s
+
+        positions = np.array([pos for _, _, pos in rows], np.int32)
+        for (slot, sid, pos) in rows:
+            P.seq[sid].ensure_token(int(pos), P.alloc)
+        bt = block_table_array([P.seq[sid] for _, sid, _ in rows], P.stride, P.poison)
+        ins = [plan.step_inputs(sid, s) for _, sid, _ in rows]
+        q = _stack([x[0] for x in ins])
+        k = _stack([x[1] for x in ins])
+        v = _stack([x[2] for x in ins])
+        kv_lens = positions + 1
+
+        # ---- GPU, paged
+        d_bt = torch.from_numpy(bt).cuda()
+        d_pos = torch.from_numpy(positions).cuda()
+        d_len = torch.from_numpy(kv_lens.astype(np.int32)).cuda()
+        d_q = to_torch(q, "bf16").cuda()
+        d_k = to_torch(k, "bf16").cuda()
+        d_v = to_torch(v, "bf16").cuda()
+        d_qr = torch.empty_like(d_q)
+        B.pa_append_kv(P.dev.pool, d_bt, P.stride, d_pos, None, d_k, d_v, d_q, d_qr, H_q, 16)
+        out = torch.empty((16, H_q, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((16, H_q), dtype=torch.float32, device="cuda")
+        max_len = int(kv_lens.max())
+        need = B.pa_decode_attention(P.dev.pool, d_qr, H_q * D, 1, H_q, d_bt, P.stride, d_len, 16,
+                                     max_len, scale, out=out, query_workspace=True)
+        if need and (ws is None or ws.numel() < need):
+            ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        B.pa_decode_attention(P.dev.pool, d_qr, H_q * D, 1, H_q, d_bt, P.stride, d_len, 16,
+                              max_len, scale, workspace=ws if need else None, out=out, lse=lse)
+
+        # ---- GPU, padded lockstep: the step's token at column plen + (s - seg_start)
+        col = plen + (s - seg_start)
+        d_col = torch.full((16,), col, dtype=torch.int32, device="cuda")
+        d_qp = torch.empty_like(d_q)
+        L.append(d_pos, d_col, d_k, d_v, d_q, d_qp)
+        gs = torch.from_numpy(prefix.astype(np.int32)).cuda()
+        ge = torch.full((16,), plen, dtype=torch.int32, device="cuda")
+        out_p, lse_p = L.decode(d_qp, gs, ge, col + 1, scale)
+        torch.cuda.synchronize()
+
+        # ---- oracle, both forms
+        P.k, P.v, q2 = O.append_kv(P.k, P.v, "bf16", "paged", bt, positions, positions, k, v,
+                                   P.cos, P.sin, q_in=q)
+        o_ref, l_ref = O.decode_paged(P.k, P.v, "bf16", bt, kv_lens, q2, scale)
+        kpad, vpad, q2p = O.append_kv(kpad, vpad, "bf16", "padded", None, positions,
+                                      np.full(16, col, np.int32), k, v, P.cos, P.sin, q_in=q)
+        np.testing.assert_array_equal(q2p, q2)
+        np.testing.assert_array_equal(to_numpy(d_qr, "bf16"), q2)
+        op_ref, lp_ref = O.decode_padded(kpad, vpad, "bf16", prefix, np.full(16, plen), col + 1,
+                                         q2, scale)
+        np.testing.assert_array_equal(op_ref, o_ref)  # same logical tokens: identical in fp64
+        mx, mean = assert_attention_close(out.cpu().numpy(), o_ref[:, 0], "bf16", f"step {s}")
+        assert_attention_close(lse.cpu().numpy(), l_ref[:, 0], "bf16", f"step {s} lse")
+        assert_attention_close(out_p.cpu().numpy(), op_ref[:, 0], "bf16", f"padded step {s}")
+        assert_attention_close(lse_p.cpu().numpy(), lp_ref[:, 0], "bf16", f"padded step {s} lse")
+        if s % 8 == 7 or s == plan.join_step:
+            np.testing.assert_array_equal(to_numpy(P.dev.k, "bf16"), P.k)
+            np.testing.assert_array_equal(to_numpy(P.dev.v, "bf16"), P.v)
+            np.testing.assert_array_equal(to_numpy(L.kv.k, "bf16"), kpad)
+            np.testing.assert_array_equal(to_numpy(L.kv.v, "bf16"), vpad)
+        log(f"[lockstep] step {s} ok max_err={mx:.2e} mean_err={mean:.2e} "
+            f"free_blocks={P.alloc.num_free}")

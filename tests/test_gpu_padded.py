@@ -1,0 +1,99 @@
+"""GPU parity of the right-padded lockstep form (append at the lockstep column + decode that skips
+each row's padding gap) against the fp64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from paged_kv_cache_177_amd.runner import PaddedLockstep, PagedStep, to_numpy, to_torch
+
+from _parity import assert_attention_close, bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check_padded(pc, gap_override=None):
+    """Append + padded decode on the GPU vs the oracle: the padded pool bit for bit, attention
+    within tolerance. Returns (out, lse) of the GPU."""
+    log(f"[padded] case={pc.name} B={pc.batch} D={pc.head_dim} padded_len={pc.padded_len} "
+        f"seq_cap={pc.seq_cap} dtype={pc.dtype}")
+    dev = "cuda"
+    L = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
+                       pc.seq_cap, rope_theta=pc.rope_theta, rope_max_pos=pc.rope_max_pos)
+    L.kv.k.copy_(to_torch(pc.k_pad, pc.dtype))
+    L.kv.v.copy_(to_torch(pc.v_pad, pc.dtype))
+    pos = torch.from_numpy(pc.positions).to(dev)
+    dest = torch.from_numpy(pc.dest).to(dev)
+    k_new = to_torch(pc.k_new, pc.dtype).to(dev)
+    v_new = to_torch(pc.v_new, pc.dtype).to(dev)
+    q = to_torch(pc.q, pc.dtype).to(dev)
+    rope = pc.rope_max_pos > 0
+    q_rot = torch.empty_like(q) if rope else None
+    L.append(pos, dest, k_new, v_new, q if rope else None, q_rot)
+    gs_np = pc.prefix_lens.astype(np.int32)
+    ge_np = np.full(pc.batch, pc.padded_len, np.int32)
+    if gap_override is not None:
+        gs_np, ge_np = gap_override
+    gs = torch.from_numpy(gs_np).to(dev)
+    ge = torch.from_numpy(ge_np).to(dev)
+    out, lse = L.decode(q_rot if rope else q, gs, ge, pc.kv_cols, pc.scale)
+    torch.cuda.synchronize()
+
+    cos = sin = None
+    if rope:
+        cos, sin = O.rope_tables(pc.rope_theta, pc.head_dim, pc.rope_max_pos)
+    k2, v2, q2 = O.append_kv(pc.k_pad, pc.v_pad, pc.dtype, "padded", None, pc.positions,
+                             pc.dest, pc.k_new, pc.v_new, cos, sin,
+                             q_in=pc.q if rope else None)
+    q_used = q2 if rope else pc.q
+    np.testing.assert_array_equal(bits(to_numpy(L.kv.k, pc.dtype), pc.dtype), bits(k2, pc.dtype))
+    np.testing.assert_array_equal(bits(to_numpy(L.kv.v, pc.dtype), pc.dtype), bits(v2, pc.dtype))
+    if rope:
+        np.testing.assert_array_equal(bits(to_numpy(q_rot, pc.dtype), pc.dtype),
+                                      bits(q2, pc.dtype))
+    o_ref, l_ref = O.decode_padded(k2, v2, pc.dtype, gs_np, ge_np, pc.kv_cols, q_used, pc.scale)
+    mx, mean = assert_attention_close(out.cpu().numpy(), o_ref[:, 0], pc.dtype, "out")
+    assert_attention_close(lse.cpu().numpy(), l_ref[:, 0], pc.dtype, "lse")
+    log(f"[padded] ok case={pc.name} max_err={mx:.2e} mean_err={mean:.2e}")
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("reading", ["A", "B"])
+def test_tiny_padded(reading):
+    run_and_check_padded(W.padded_from_paged(W.tiny(reading)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny_edges_padded(dtype):
+    run_and_check_padded(W.padded_from_paged(W.tiny_edges(dtype=dtype), seq_cap=48))
+
+
+@pytest.mark.parametrize("D,G,dtype", [(64, 4, "bf16"), (128, 4, "bf16"), (64, 2, "f32"),
+                                       (32, 1, "bf16")])
+def test_ragged_padded_with_splits(D, G, dtype):
+    """Gaps of every width, kv_cols spanning several chunks (split + merge), NaN in every gap."""
+    n = [0, 5, 16, 700, 1023, 1500, 2100, 3000]
+    c = W.make_paged_case(f"padded-D{D}-G{G}-{dtype}", 31, n, 2 * G, 2, D, dtype,
+                          rope_theta=1e4 if dtype == "f32" else 0.0)
+    run_and_check_padded(W.padded_from_paged(c, seq_cap=3100))
+
+
+def test_uniform_lengths_have_no_gap():
+    c = W.make_paged_case("uniform", 32, [300] * 6, 32, 8, 64, "bf16")
+    pc = W.padded_from_paged(c)
+    assert np.all(pc.prefix_lens == pc.padded_len)  # gap_start == gap_end
+    run_and_check_padded(pc)
+
+
+def test_padded_matches_paged():
+    """The same logical tokens, paged vs right-padded: both within tolerance of the oracle and of
+    each other."""
+    c = W.make_paged_case("pvp", 33, [40, 900, 1100, 2500], 32, 8, 64, "bf16", rope_theta=1e6)
+    out_pad, lse_pad = run_and_check_padded(W.padded_from_paged(c, seq_cap=2600))
+    r = PagedStep(c)
+    r.step()
+    torch.cuda.synchronize()
+    assert_attention_close(out_pad, r.out.cpu().numpy(), "bf16", "padded vs paged")
+    assert_attention_close(lse_pad, r.lse.cpu().numpy(), "bf16", "padded vs paged lse")

@@ -8,6 +8,8 @@ unchanged, so neither side's inputs come from the other.
 
 from .generators import (  # noqa: F401
     PagedCase,
+    PaddedCase,
+    padded_from_paged,
     MQCase,
     LockstepPlan,
     POISON_BF16,

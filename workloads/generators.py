@@ -171,6 +171,68 @@ def long_context(seed: int = 3) -> PagedCase:
     return make_paged_case("long", seed, n, 32, 8, 128, "bf16", rng=rng)
 
 
+@dataclass
+class PaddedCase:
+    """One lockstep step over right-padded rows (the padded form of a paged case): row b's history
+    fills columns [0, n_b), the batch is padded to padded_len = max n_b, and the step's token goes
+    to column padded_len at position n_b. Unwritten columns hold NaN."""
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    seq_cap: int
+    rope_theta: float
+    rope_max_pos: int
+    prefix_lens: np.ndarray      # int32[B] = n_b
+    padded_len: int
+    k_pad: np.ndarray            # [B][H_kv][seq_cap][D] storage, before the append
+    v_pad: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    q: np.ndarray
+    scale: float
+
+    @property
+    def batch(self) -> int:
+        return len(self.prefix_lens)
+
+    @property
+    def positions(self) -> np.ndarray:
+        return self.prefix_lens.astype(np.int32)
+
+    @property
+    def dest(self) -> np.ndarray:
+        return np.full(self.batch, self.padded_len, np.int32)
+
+    @property
+    def kv_cols(self) -> int:
+        return self.padded_len + 1
+
+
+def padded_from_paged(case: PagedCase, seq_cap: int | None = None) -> PaddedCase:
+    """Lay a paged case's histories out right-padded (pure data movement, no arithmetic)."""
+    B, H, D = case.batch, case.num_kv_heads, case.head_dim
+    n = case.n_ctx.astype(np.int64)
+    padded_len = int(n.max(initial=0))
+    cap = seq_cap if seq_cap is not None else padded_len + 1
+    sd = storage_np_dtype(case.dtype)
+    k_pad = np.full((B, H, cap, D), poison_value(case.dtype), dtype=sd)
+    v_pad = np.full((B, H, cap, D), poison_value(case.dtype), dtype=sd)
+    for b in range(B):
+        t = np.arange(int(n[b]))
+        blk = case.block_tables[b, t // BLOCK_SIZE]
+        k_pad[b, :, : n[b], :] = np.moveaxis(case.k_pool[blk, :, t % BLOCK_SIZE, :], 0, 1)
+        v_pad[b, :, : n[b], :] = np.moveaxis(case.v_pool[blk, :, t % BLOCK_SIZE, :], 0, 1)
+    return PaddedCase(name=case.name + "-padded", dtype=case.dtype,
+                      num_q_heads=case.num_q_heads, num_kv_heads=H, head_dim=D, seq_cap=cap,
+                      rope_theta=case.rope_theta,
+                      rope_max_pos=max(case.rope_max_pos, padded_len + 1) if case.rope_theta else 0,
+                      prefix_lens=case.n_ctx.astype(np.int32), padded_len=padded_len,
+                      k_pad=k_pad, v_pad=v_pad, k_new=case.k_new, v_new=case.v_new, q=case.q,
+                      scale=case.scale)
+
+
 # --------------------------------------------------------------------------------------------
 # Lockstep B=16 protocol
 # --------------------------------------------------------------------------------------------
