@@ -137,7 +137,7 @@ pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t
  * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0, n_q < 1,
  * num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, layout not
  * PA_PAGED, scale negative or not finite, q not 16-byte aligned or q_row_stride not a multiple of
- * 16 bytes); PA_ERR_UNSUPPORTED (n_q == 1 with G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace
+ * 16 bytes); PA_ERR_UNSUPPORTED (n_q == 1 with G not in {1, 2, 4, 8}; n_q > 1 with an fp32 pool); PA_ERR_CAPACITY (workspace
  * too small). batch == 0 is a no-op. */
 pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
                               int32_t n_q, int32_t num_q_heads, const int32_t* block_tables,

@@ -181,6 +181,7 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   if ((int64_t)max_kv_len > (int64_t)bt_stride * pa::kBlock) return PA_ERR_SHAPE;
   const int G = num_q_heads / d.num_kv_heads;
   if (n_q == 1 && G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (n_q > 1 && d.dtype != PA_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core path: bf16 only
   if (!q_aligned(q, q_row_stride, d.dtype)) return PA_ERR_SHAPE;
   if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
 

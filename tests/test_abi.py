@@ -229,3 +229,11 @@ def test_decode_rejects_bad_scale(scale):
         B.pa_decode_attention(p, FAKE, 32 * 64, 1, 32, FAKE, 64, FAKE, 4, 1000, scale, out=FAKE,
                               query_workspace=True)
     assert e.value.status == B.PA_ERR_SHAPE
+
+
+def test_multi_query_needs_bf16():
+    p = _fake_pool(dtype="f32")
+    with pytest.raises(B.PaError) as e:
+        B.pa_decode_attention(p, FAKE, 0, 16, 8, FAKE, 64, FAKE, 4, 1000, 0.125, out=FAKE,
+                              query_workspace=True)
+    assert e.value.status == B.PA_ERR_UNSUPPORTED
