@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="cache-flush write between the extra flushed decode timings")
+    p.add_argument("--traffic-calibration", action="store_true",
+                   help="finish with 5 device copies of 256 MiB (a known-size reference for "
+                        "hardware byte counters)")
     return p.parse_args()
 
 
@@ -189,10 +192,17 @@ def main():
                    "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                    "decode_us_flushed_median": round(statistics.median(fl) * 1e3, 2),
                    "kv_gbs_flushed": round(kv_bytes / (statistics.median(fl) * 1e-3) / 1e9, 1),
+                   "traffic_bytes_per_call": traffic,
                    "source_hash": src_hash},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case)
+    if args.traffic_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 
