@@ -120,10 +120,16 @@ def main():
     r = PagedStep(case, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        r.append()
-        r.decode()
-    torch.cuda.synchronize()
+    # untimed warm-up: at least W steps and at least one second of them (the GPU takes a while to
+    # reach its steady clocks; shorter warm-ups measured up to 10% slow)
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < 1.0:
+        for _ in range(10):
+            r.append()
+            r.decode()
+        done += 10
+        torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]

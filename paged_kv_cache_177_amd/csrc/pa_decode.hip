@@ -294,7 +294,10 @@ struct Worker {
       // uniform block base + a 32-bit lane byte offset: the scalar-base form of the global load
       const char* kb = reinterpret_cast<const char*>(kbase + boff);
       const char* vb = reinterpret_cast<const char*>(vbase + boff);
-      const unsigned lb = lane_off * (unsigned)sizeof(T);
+      unsigned lb = lane_off * (unsigned)sizeof(T);
+      // keep the lane offset a 32-bit value at the load, so the compiler cannot hoist a 64-bit
+      // widening out of the loop and fall back to vector 64-bit addresses (costing registers)
+      asm volatile("" : "+v"(lb));
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const unsigned o = lb + (unsigned)(j * TPI * D * sizeof(T));
@@ -496,9 +499,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
 // ---- persistent kernel --------------------------------------------------------------------------
 // A fixed grid of workgroups (as many as fit on the device) takes chunks from a counter in the
 // workspace, in an order that puts every row's full chunks first and the shorter last chunks at the
-// end. A workgroup knows its next chunk one step ahead: that chunk's block ids and queries load
-// while the current one streams, and its first K/V block is the current chunk's last prefetch.
-// The split of each row is the same as in the grid kernel, so results are identical.
+// end, so no workgroup slot is spent on a split past a row's end. A workgroup knows its next chunk
+// one step ahead: while the current chunk streams, that chunk's block ids and queries are loaded
+// and parked in LDS, so a chunk starts with its first K/V loads. The split of each row is the same
+// as in the grid kernel, so results are identical.
 constexpr int kMaxRows = 1024;
 
 template <bool PADDED>
@@ -626,21 +630,32 @@ __device__ __forceinline__ Chunk decode_ticket(const RowSmem<PADDED>& rs, int B,
   return make_chunk(uni(row), uni(g), uni(split), uni(rs.n[row]), gs, gsh, chunk);
 }
 
+#ifdef PA_PERSISTENT_WAVES_PER_EU
+#define PA_PERSISTENT_ATTR __attribute__((amdgpu_waves_per_eu(PA_PERSISTENT_WAVES_PER_EU, 8)))
+#else
+#define PA_PERSISTENT_ATTR
+#endif
 template <typename T, int D, int G, bool PADDED>
-__global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves) PA_PERSISTENT_ATTR void decode_persistent_kernel(
+    const DecodeArgs a) {
   using W = Worker<T, D, G, PADDED>;
+  constexpr int kQVec = G * D * (int)sizeof(T) / 16;  // 16-byte pieces of one (row, g) query set
+  static_assert(kQVec <= 64 * kWaves, "query staging: at most one piece per thread");
   __shared__ typename W::Smem sm;
   __shared__ RowSmem<PADDED> rs;
+  __shared__ int s_ids[2][64];
+  __shared__ uint4 s_q[2][kQVec];
   W w(a);
   const int B = a.batch;
   const int chunk = chunk_tokens(D);
   int* counter = a.counter;
+  const int tid = threadIdx.x;
 
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     rs.ticket[0] = atomicAdd(counter, 1);
     rs.ticket[1] = atomicAdd(counter, 1);
   }
-  for (int b = threadIdx.x; b < B; b += 64 * kWaves) {
+  for (int b = tid; b < B; b += 64 * kWaves) {
     int gs, gsh;
     rs.n[b] = row_valid<PADDED>(a, b, &gs, &gsh);
     if constexpr (PADDED) {
@@ -653,48 +668,65 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(const De
   const int n_full = uni(rs.full_pre[B]);
   const int n_items = (n_full + uni(rs.part_pre[B])) * a.H_kv;
 
-  const int t_cur = uni(rs.ticket[0]);
-  const int t_nxt = uni(rs.ticket[1]);
+  int t_cur = uni(rs.ticket[0]);
+  int t_nxt = uni(rs.ticket[1]);
   if (t_cur >= n_items) return;  // uniform: no work left for this workgroup
-  Chunk cur = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_cur, chunk);
-  int ids = w.load_ids(cur.row, cur.tok0);
-  w.load_q(w.q, cur.row, cur.g);
-  bool has_nx = t_nxt < n_items;
-  Chunk nx = has_nx ? decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_nxt, chunk) : cur;
-  int nx_ids = has_nx ? w.load_ids(nx.row, nx.tok0) : 0;
-  Vec8<T> nx_q[G];
-  if (has_nx) w.load_q(nx_q, nx.row, nx.g);
 
-  typename W::Frag f0, f1;
-  int my = w.my_blocks(cur);
-  if (my > 0) w.load_block(f0, cur, ids, w.blk_of(0));
-  for (int k = 0;; ++k) {
-    // the chunk after next: its ticket is read after this chunk's merge barrier
-    if (threadIdx.x == 0 && has_nx) rs.ticket[(k + 2) % 3] = atomicAdd(counter, 1);
-    w.reset();
-    const bool nxt_first = has_nx && w.my_blocks(nx) > 0;
-    w.run_blocks(f0, f1, cur, ids, my, nxt_first, nx, nx_ids);
-    w.merge_to_smem(sm);
-    int t_nn = 0;
-    Chunk nn = cur;
-    if (has_nx) {
-      t_nn = uni(rs.ticket[(k + 2) % 3]);
-      if (t_nn < n_items) nn = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_nn, chunk);
+  // a chunk's block ids (wave 0) and queries (one 16-byte piece per thread): global -> registers,
+  // later parked in LDS
+  auto fetch = [&](const Chunk& ch, int& pid, uint4& pq) {
+    if (w.wave == 0) pid = w.load_ids(ch.row, ch.tok0);
+    if (tid < kQVec) {
+      const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)ch.row * a.q_row_stride +
+                    (size_t)ch.g * G * D;
+      pq = reinterpret_cast<const uint4*>(qp)[tid];
     }
+  };
+  auto park = [&](int slot, int pid, const uint4& pq) {
+    if (w.wave == 0) s_ids[slot][w.lane] = pid;
+    if (tid < kQVec) s_q[slot][tid] = pq;
+  };
+
+  Chunk cur = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_cur, chunk);
+  {
+    int pid = 0;
+    uint4 pq = make_uint4(0, 0, 0, 0);
+    fetch(cur, pid, pq);
+    park(0, pid, pq);
+  }
+  __syncthreads();
+  bool has_nx = t_nxt < n_items;
+  for (int k = 0;; ++k) {
+    const int slot = k & 1;
+    // the chunk after next: its ticket is read after this chunk's merge barrier
+    if (tid == 0 && has_nx) rs.ticket[(k + 2) % 3] = atomicAdd(counter, 1);
+    const int ids = s_ids[slot][w.lane];
+    {
+      const T* qs = reinterpret_cast<const T*>(s_q[slot]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) w.q[h].load_cached(qs + h * D + w.c * 8);
+    }
+    Chunk nx = cur;
+    int pid = 0;
+    uint4 pq = make_uint4(0, 0, 0, 0);
+    if (has_nx) {
+      nx = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_nxt, chunk);
+      fetch(nx, pid, pq);
+    }
+    w.reset();
+    typename W::Frag f0, f1;
+    const int my = w.my_blocks(cur);
+    if (my > 0) w.load_block(f0, cur, ids, w.blk_of(0));
+    w.run_blocks(f0, f1, cur, ids, my, false, cur, ids);
+    if (has_nx) park(slot ^ 1, pid, pq);
+    w.merge_to_smem(sm);
+    const int t_nn = has_nx ? uni(rs.ticket[(k + 2) % 3]) : n_items;
     w.write_result(sm, cur);
-    __syncthreads();  // the merge area is reused by the next chunk
+    __syncthreads();  // the merge area and this slot are reused
     if (!has_nx) break;
     cur = uni_chunk(nx);
-    ids = nx_ids;
-#pragma unroll
-    for (int h = 0; h < G; ++h) w.q[h] = nx_q[h];
-    my = w.my_blocks(cur);
-    has_nx = t_nn < n_items;
-    if (has_nx) {
-      nx = uni_chunk(nn);
-      nx_ids = w.load_ids(nx.row, nx.tok0);
-      w.load_q(nx_q, nx.row, nx.g);
-    }
+    t_nxt = t_nn;
+    has_nx = t_nxt < n_items;
   }
 }
 
@@ -791,7 +823,7 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   if (PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows) {
     auto kern = decode_persistent_kernel<T, D, G, PADDED>;
     const int resident = resident_workgroups(kern);
-    if (resident > 0 && (long long)a.batch * a.H_kv * 2 <= resident) {
+    if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || (long long)a.batch * a.H_kv * 2 <= resident)) {
       const int grid = (int)(items < resident ? items : resident);
       hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), 0, stream, a);
       return hipGetLastError();
