@@ -33,6 +33,10 @@
 //     from a counter (see decode_persistent_kernel), used when there are few (row, head) pairs.
 #include "pa_internal.h"
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
 #endif
@@ -371,29 +375,30 @@ struct Worker {
     return wave < ch.nblk ? (ch.nblk - wave + kWaves - 1) / kWaves : 0;
   }
 
-  // Stream this wave's blocks (wave, wave + kWaves, ...) of `ch`, whose first block is already in
-  // f0. With `nxt_first`, the first block of this wave in `nx` is loaded into f0 as the last
-  // prefetch, so the next chunk's data is in flight before this one's merge.
-  // Stream this wave's blocks (wave, wave + kWaves, ...) of `ch`, whose first block is already in
-  // f0; the next block is always in flight. Full blocks take the unmasked update; the chunk's
-  // partial last block (if this wave owns it) is taken last, masked. With `nxt_first`, the last
-  // prefetch is this wave's first block of the next chunk `nx`, left in f0.
-  __device__ __forceinline__ void run_blocks(Frag& f0, Frag& f1, const Chunk& ch, int ids, int my,
-                                             bool nxt_first, const Chunk& nx, int nx_ids) {
-    const bool own_tail = my > 0 && blk_of(my - 1) == ch.tail_blk;
-    const int full = own_tail ? my - 1 : my;
-    for (int i = 0; i < full; ++i) {
-      if (i + 1 < my) load_block(f1, ch, ids, blk_of(i + 1));
-      else if (nxt_first) load_block(f1, nx, nx_ids, wave);
+  // Stream this wave's `my` blocks (wave, wave + kWaves, ...) of `ch`; the caller has issued the
+  // first one into f0. The two fragments swap roles every block (loop unrolled by two), so the next
+  // block is always in flight while the current one is computed, with no register copies (copying
+  // a fragment would wait for its load). The loads of the steady loop are unconditional, so the
+  // wait before each update covers exactly the older fragment. The chunk's partial last block, if
+  // this wave owns it (it is then the wave's last block), takes the masked update.
+  __device__ __forceinline__ void run_blocks(Frag& f0, Frag& f1, const Chunk& ch, int ids, int my) {
+    int i = 0;
+    for (; i + 2 < my; i += 2) {
+      load_block(f1, ch, ids, blk_of(i + 1));
       update<false>(f0, ch, blk_of(i));
-      f0 = f1;
+      load_block(f0, ch, ids, blk_of(i + 2));
+      update<false>(f1, ch, blk_of(i + 1));
     }
-    if (own_tail) {
-      if (nxt_first) load_block(f1, nx, nx_ids, wave);
-      update<true>(f0, ch, blk_of(my - 1));
-      f0 = f1;
+    const bool tail = my > 0 && blk_of(my - 1) == ch.tail_blk;
+    if (i + 1 < my) {
+      load_block(f1, ch, ids, blk_of(i + 1));
+      update<false>(f0, ch, blk_of(i));
+      if (tail) update<true>(f1, ch, blk_of(i + 1));
+      else update<false>(f1, ch, blk_of(i + 1));
+    } else if (i < my) {
+      if (tail) update<true>(f0, ch, blk_of(i));
+      else update<false>(f0, ch, blk_of(i));
     }
-    if (my == 0 && nxt_first) load_block(f0, nx, nx_ids, wave);
   }
 
   // Merge the lanes' streams to one (m, l, acc) per wave and park it in LDS (then a barrier).
@@ -491,17 +496,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   typename W::Frag f0, f1;
   const int my = w.my_blocks(ch);
   if (my > 0) w.load_block(f0, ch, ids, w.blk_of(0));
-  w.run_blocks(f0, f1, ch, ids, my, false, ch, ids);
+  w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
 }
 
 // ---- persistent kernel --------------------------------------------------------------------------
-// A fixed grid of workgroups (as many as fit on the device) takes chunks from a counter in the
-// workspace, in an order that puts every row's full chunks first and the shorter last chunks at the
-// end, so no workgroup slot is spent on a split past a row's end. A workgroup knows its next chunk
+// A fixed grid of workgroups (as many as fit on the device) takes chunks (after two fixed ones
+// each) from a counter in the workspace, in an order that puts every row's full chunks first and
+// the shorter last chunks at the end, so no workgroup slot is spent on a split past a row's end. A workgroup knows its next chunk
 // one step ahead: while the current chunk streams, that chunk's block ids and queries are loaded
-// and parked in LDS, so a chunk starts with its first K/V loads. The split of each row is the same
+// and parked in LDS, and its first K/V block is in flight while the current chunk's result is
+// merged and written. The split of each row is the same
 // as in the grid kernel, so results are identical.
 constexpr int kMaxRows = 1024;
 
@@ -630,13 +636,8 @@ __device__ __forceinline__ Chunk decode_ticket(const RowSmem<PADDED>& rs, int B,
   return make_chunk(uni(row), uni(g), uni(split), uni(rs.n[row]), gs, gsh, chunk);
 }
 
-#ifdef PA_PERSISTENT_WAVES_PER_EU
-#define PA_PERSISTENT_ATTR __attribute__((amdgpu_waves_per_eu(PA_PERSISTENT_WAVES_PER_EU, 8)))
-#else
-#define PA_PERSISTENT_ATTR
-#endif
 template <typename T, int D, int G, bool PADDED>
-__global__ __launch_bounds__(64 * kWaves) PA_PERSISTENT_ATTR void decode_persistent_kernel(
+__global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
     const DecodeArgs a) {
   using W = Worker<T, D, G, PADDED>;
   constexpr int kQVec = G * D * (int)sizeof(T) / 16;  // 16-byte pieces of one (row, g) query set
@@ -651,10 +652,10 @@ __global__ __launch_bounds__(64 * kWaves) PA_PERSISTENT_ATTR void decode_persist
   int* counter = a.counter;
   const int tid = threadIdx.x;
 
-  if (tid == 0) {
-    rs.ticket[0] = atomicAdd(counter, 1);
-    rs.ticket[1] = atomicAdd(counter, 1);
-  }
+  // The first two chunks of every workgroup are fixed by its index; later ones come from the
+  // counter, offset past them (so the launch does not start with every workgroup contending for
+  // one atomic).
+  const int n_static = 2 * (int)gridDim.x;
   for (int b = tid; b < B; b += 64 * kWaves) {
     int gs, gsh;
     rs.n[b] = row_valid<PADDED>(a, b, &gs, &gsh);
@@ -668,8 +669,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PERSISTENT_ATTR void decode_persist
   const int n_full = uni(rs.full_pre[B]);
   const int n_items = (n_full + uni(rs.part_pre[B])) * a.H_kv;
 
-  int t_cur = uni(rs.ticket[0]);
-  int t_nxt = uni(rs.ticket[1]);
+  int t_cur = (int)blockIdx.x;
+  int t_nxt = (int)(blockIdx.x + gridDim.x);
   if (t_cur >= n_items) return;  // uniform: no work left for this workgroup
 
   // a chunk's block ids (wave 0) and queries (one 16-byte piece per thread): global -> registers,
@@ -696,10 +697,12 @@ __global__ __launch_bounds__(64 * kWaves) PA_PERSISTENT_ATTR void decode_persist
   }
   __syncthreads();
   bool has_nx = t_nxt < n_items;
+  typename W::Frag f0, f1;
+  bool pre = false;  // f0 already holds (in flight) this wave's first block of `cur`
   for (int k = 0;; ++k) {
     const int slot = k & 1;
     // the chunk after next: its ticket is read after this chunk's merge barrier
-    if (tid == 0 && has_nx) rs.ticket[(k + 2) % 3] = atomicAdd(counter, 1);
+    if (tid == 0 && has_nx) rs.ticket[(k + 2) % 3] = n_static + atomicAdd(counter, 1);
     const int ids = s_ids[slot][w.lane];
     {
       const T* qs = reinterpret_cast<const T*>(s_q[slot]);
@@ -714,12 +717,21 @@ __global__ __launch_bounds__(64 * kWaves) PA_PERSISTENT_ATTR void decode_persist
       fetch(nx, pid, pq);
     }
     w.reset();
-    typename W::Frag f0, f1;
     const int my = w.my_blocks(cur);
-    if (my > 0) w.load_block(f0, cur, ids, w.blk_of(0));
-    w.run_blocks(f0, f1, cur, ids, my, false, cur, ids);
+    if (!pre && my > 0) w.load_block(f0, cur, ids, w.blk_of(0));
+    w.run_blocks(f0, f1, cur, ids, my);
     if (has_nx) park(slot ^ 1, pid, pq);
     w.merge_to_smem(sm);
+    // the merge barrier has published the next chunk's block ids: its first block goes in flight
+    // before this chunk's results are combined and written
+    pre = false;
+    if (has_nx) {
+      const Chunk nu = uni_chunk(nx);
+      if (w.my_blocks(nu) > 0) {
+        w.load_block(f0, nu, s_ids[slot ^ 1][w.lane], w.blk_of(0));
+        pre = true;
+      }
+    }
     const int t_nn = has_nx ? uni(rs.ticket[(k + 2) % 3]) : n_items;
     w.write_result(sm, cur);
     __syncthreads();  // the merge area and this slot are reused
@@ -798,20 +810,25 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
     a.lse[(size_t)row * a.H_q + hq] = W > 0.f ? (mx + __log2f(W)) * kLn2 : kNegInf;
 }
 
-// Workgroups of `kernel` that fit on the current device at once (cached per device).
-template <typename K>
-int resident_workgroups(K kernel) {
-  static int cache[64] = {0};
+// Workgroups of `kernel` that fit on the current device at once (per-CU occupancy x CUs), cached
+// per (device, kernel, dynamic LDS size).
+int resident_workgroups(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] > 0) return cache[dev];
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_tuple(dev, kernel, lds);
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, lds) !=
+      hipSuccess)
     return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  cache[dev] = per_cu * cus;
-  return cache[dev];
+  cache[key] = per_cu * cus;
+  return per_cu * cus;
 }
 
 template <typename T, int D, int G, bool PADDED>
@@ -822,7 +839,7 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   // with more waves per SIMD. Both cut rows into the same chunks: their results are identical.
   if (PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows) {
     auto kern = decode_persistent_kernel<T, D, G, PADDED>;
-    const int resident = resident_workgroups(kern);
+    const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
     if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || (long long)a.batch * a.H_kv * 2 <= resident)) {
       const int grid = (int)(items < resident ? items : resident);
       hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), 0, stream, a);
