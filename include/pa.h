@@ -56,7 +56,7 @@ typedef enum { PA_PAGED = 0, PA_PADDED = 1 } pa_layout;
 typedef struct {
   int32_t layout;        /* pa_layout */
   int32_t dtype;         /* pa_dtype: storage type of K, V and of the queries used with the pool */
-  int32_t num_kv_heads;  /* H_kv >= 1 */
+  int32_t num_kv_heads;  /* H_kv in [1, 65535] */
   int32_t head_dim;      /* D in {32, 64, 128} */
   int32_t block_size;    /* must be 16 */
   int32_t num_blocks;    /* PA_PAGED: physical blocks (>= 1); ignored for PA_PADDED */
@@ -108,8 +108,8 @@ pa_status pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size_t dev_buf_
  * Preconditions (clamped, not checked): 0 <= positions[b] < rope_max_pos, dest[b] inside the row
  * (< bt_stride*16, or < seq_cap), block ids < num_blocks, b < batch_cap for PA_PADDED.
  * Errors: PA_ERR_NULL for a missing pointer (block_tables is required for PA_PAGED, positions
- * always); PA_ERR_SHAPE for batch < 0, bt_stride < 1, num_q_heads not a positive multiple of H_kv,
- * batch > batch_cap (PA_PADDED). batch == 0 is a no-op. */
+ * always); PA_ERR_SHAPE for batch < 0 or > 65535, bt_stride < 1, num_q_heads not a positive
+ * multiple of H_kv, batch > batch_cap (PA_PADDED). batch == 0 is a no-op. */
 pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
                        const int32_t* positions, const int32_t* dest, const void* k_new,
                        const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
@@ -134,11 +134,12 @@ pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t
  * that overlap in time (other streams) need workspaces of their own. max_kv_len is a host upper
  * bound of kv_lens (<= bt_stride * 16).
  * Preconditions (clamped, not checked): 0 <= kv_lens[b] <= max_kv_len; block ids < num_blocks.
- * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0, n_q < 1,
- * num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, layout not
- * PA_PAGED, scale negative or not finite, q not 16-byte aligned or q_row_stride not a multiple of
- * 16 bytes); PA_ERR_UNSUPPORTED (n_q == 1 with G not in {1, 2, 4, 8}; n_q > 1 with an fp32 pool); PA_ERR_CAPACITY (workspace
- * too small). batch == 0 is a no-op. */
+ * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0 or > 65535,
+ * n_q < 1, num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, more
+ * than 65535 splits for max_kv_len, layout not PA_PAGED, scale negative or not finite, q not
+ * 16-byte aligned or q_row_stride not a multiple of 16 bytes); PA_ERR_UNSUPPORTED (n_q == 1 with G
+ * not in {1, 2, 4, 8}; n_q > 1 with an fp32 pool); PA_ERR_CAPACITY (workspace too small).
+ * batch == 0 is a no-op. */
 pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
                               int32_t n_q, int32_t num_q_heads, const int32_t* block_tables,
                               int32_t bt_stride, const int32_t* kv_lens, int32_t batch,
@@ -154,8 +155,8 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
  * pa_decode_attention; the same split rule applies to the row's count of valid columns.
  * Workspace as for pa_decode_attention.
  * Preconditions (clamped, not checked): 0 <= gap_start[b] <= gap_end[b] <= kv_cols.
- * Errors: PA_ERR_NULL (pool, q, gap_start, gap_end, out); PA_ERR_SHAPE (batch < 0 or > batch_cap,
- * kv_cols < 0 or > seq_cap, num_q_heads not a positive multiple of H_kv, layout not PA_PADDED,
+ * Errors: PA_ERR_NULL (pool, q, gap_start, gap_end, out); PA_ERR_SHAPE (batch < 0, > batch_cap
+ * or > 65535, kv_cols < 0 or > seq_cap, more than 65535 splits for kv_cols, num_q_heads not a positive multiple of H_kv, layout not PA_PADDED,
  * scale negative or not finite, q not 16-byte aligned);
  * PA_ERR_UNSUPPORTED (G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace too small). */
 pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,

@@ -18,7 +18,7 @@ pa_status check_desc(const pa_pool_desc* d) {
   if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (d->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (d->num_kv_heads < 1) return PA_ERR_SHAPE;
+  if (d->num_kv_heads < 1 || d->num_kv_heads > pa::kMaxGridYZ) return PA_ERR_SHAPE;
   if (d->layout == PA_PAGED && d->num_blocks < 1) return PA_ERR_SHAPE;
   if (d->layout == PA_PADDED && (d->batch_cap < 1 || d->seq_cap < 1)) return PA_ERR_SHAPE;
   if (d->rope_max_pos < 0) return PA_ERR_SHAPE;
@@ -128,7 +128,7 @@ extern "C" pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tabl
   if (positions == nullptr || k_new == nullptr || v_new == nullptr) return PA_ERR_NULL;
   if ((q_in == nullptr) != (q_out == nullptr)) return PA_ERR_NULL;
   if (d.layout == PA_PAGED && block_tables == nullptr) return PA_ERR_NULL;
-  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch < 0 || batch > pa::kMaxGridYZ) return PA_ERR_SHAPE;
   if (d.layout == PA_PAGED && bt_stride < 1) return PA_ERR_SHAPE;
   if (d.layout == PA_PADDED && batch > d.batch_cap) return PA_ERR_SHAPE;
   if (q_in != nullptr && (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0))
@@ -175,7 +175,8 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   if (d.layout != PA_PAGED) return PA_ERR_SHAPE;
   if (q == nullptr || block_tables == nullptr || kv_lens == nullptr || out == nullptr)
     return PA_ERR_NULL;
-  if (batch < 0 || n_q < 1 || bt_stride < 1 || max_kv_len < 0 || q_row_stride < 0)
+  if (batch < 0 || batch > pa::kMaxGridYZ || n_q < 1 || bt_stride < 1 || max_kv_len < 0 ||
+      q_row_stride < 0)
     return PA_ERR_SHAPE;
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
   if ((int64_t)max_kv_len > (int64_t)bt_stride * pa::kBlock) return PA_ERR_SHAPE;
@@ -186,6 +187,7 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
 
   const int s_max = n_q == 1 ? pa::num_splits(max_kv_len, pa::chunk_tokens(d.head_dim)) : 1;
+  if (s_max > pa::kMaxGridYZ) return PA_ERR_SHAPE;
   const size_t need = pa::decode_workspace_bytes(batch, n_q, num_q_heads, d.head_dim, s_max);
   if (workspace_needed != nullptr) {
     *workspace_needed = need;
@@ -236,7 +238,9 @@ extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, cons
   if (d.layout != PA_PADDED) return PA_ERR_SHAPE;
   if (q == nullptr || gap_start == nullptr || gap_end == nullptr || out == nullptr)
     return PA_ERR_NULL;
-  if (batch < 0 || batch > d.batch_cap || kv_cols < 0 || kv_cols > d.seq_cap) return PA_ERR_SHAPE;
+  if (batch < 0 || batch > d.batch_cap || batch > pa::kMaxGridYZ || kv_cols < 0 ||
+      kv_cols > d.seq_cap)
+    return PA_ERR_SHAPE;
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
   const int G = num_q_heads / d.num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
@@ -245,6 +249,7 @@ extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, cons
   if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
 
   const int s_max = pa::num_splits(kv_cols, pa::chunk_tokens(d.head_dim));
+  if (s_max > pa::kMaxGridYZ) return PA_ERR_SHAPE;
   const size_t need = pa::decode_workspace_bytes(batch, 1, num_q_heads, d.head_dim, s_max);
   if (workspace_needed != nullptr) {
     *workspace_needed = need;

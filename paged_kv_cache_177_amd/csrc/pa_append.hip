@@ -49,16 +49,18 @@ __device__ __forceinline__ void rotate_pair(float x_lo, float x_hi, float c, flo
   *r_hi = d + e;
 }
 
+// Grid (ceil(heads * D/2 / 256), batch): blockIdx.y is the row, so its position, destination and
+// block-table entry are workgroup-uniform loads issued at once; the index inside the row needs only
+// shifts (D/2 is a power of two).
 template <typename T>
-__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
-  const int half = a.D / 2;
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int log2_half) {
+  const int half = 1 << log2_half;
   const int heads = 2 * a.H_kv + (a.q_in != nullptr ? a.H_q : 0);
-  const long long total = (long long)a.batch * heads * half;
-  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= total) return;
-  const int i = (int)(tid % half);
-  const int hh = (int)((tid / half) % heads);
-  const int b = (int)(tid / ((long long)half * heads));
+  const int idx = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int b = (int)blockIdx.y;
+  if (idx >= heads * half) return;
+  const int i = idx & (half - 1);
+  const int hh = idx >> log2_half;
 
   const bool rope = a.cos != nullptr;
   int pos = a.positions[b];
@@ -118,13 +120,16 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int heads = 2 * a.H_kv + (a.q_in != nullptr ? a.H_q : 0);
-  const long long total = (long long)a.batch * heads * (a.D / 2);
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const int half = a.D / 2;
+  if (a.batch <= 0 || heads * half == 0) return hipSuccess;
+  int log2_half = 0;
+  while ((1 << log2_half) < half) ++log2_half;
+  if ((1 << log2_half) != half) return hipErrorInvalidValue;  // head_dim is 32, 64 or 128
+  const dim3 grid((unsigned)((heads * half + 255) / 256), (unsigned)a.batch);
   if (a.dtype == PA_F32)
-    hipLaunchKernelGGL(append_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(256), 0, stream, a, log2_half);
   else
-    hipLaunchKernelGGL(append_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(append_kernel<__bf16>, grid, dim3(256), 0, stream, a, log2_half);
   return hipGetLastError();
 }
 

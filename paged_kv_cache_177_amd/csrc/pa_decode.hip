@@ -744,11 +744,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
 
 // Merge the split partials of one (row, query head): out = sum_s w_s o_s / sum_s w_s with
 // w_s = 2^(lse_s - max lse); lse = max + log2(sum w_s), returned in natural-log units.
-// One wave per (row, head). It is latency-bound, so the chain of dependent loads is kept short:
-// the first 64 partial lse values load together with the row length (speculatively: the
-// workspace always holds s_max of them), and the partial outputs load in unrolled batches.
+// One wave per (row, head). It is latency-bound, so the chain of dependent loads is kept short: the
+// first 64 partial lse values and the first kSpec partial outputs load together with the row length
+// (speculatively: the workspace always holds s_max of each; slots past the row's splits are
+// discarded by a select, so whatever they hold never reaches the sums), and later partial outputs
+// load in batches of kSpec.
 template <bool PADDED>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
+  constexpr int kSpec = 8;
   const int hq = blockIdx.x;
   const int row = blockIdx.y;
   const int lane = threadIdx.x;
@@ -756,7 +759,21 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
   // the decode kernel has finished: re-arm its work counter for the next call
   if (a.counter != nullptr && hq == 0 && row == 0 && lane == 0) *a.counter = 0;
   const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
+  const float* po = a.part_o + base * D;
   const float lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
+  // this lane's dims (lane, and 64 + lane when D = 128) of the partial outputs of splits
+  // s0 + [0, kSpec), indices clamped into [0, last]
+  auto load_batch = [&](int s0, int last, float* v0, float* v1) {
+#pragma unroll
+    for (int i = 0; i < kSpec; ++i) {
+      const int si = s0 + i < last ? s0 + i : last;
+      const float* p = po + (size_t)si * D;
+      v0[i] = lane < D ? p[lane] : 0.f;
+      v1[i] = D > 64 ? p[64 + lane] : 0.f;
+    }
+  };
+  float v0[kSpec], v1[kSpec];
+  load_batch(0, a.s_max - 1, v0, v1);
   int gs, gsh;
   const int n = row_valid<PADDED>(a, row, &gs, &gsh);
   const int ns = num_splits(n, chunk_tokens(D));
@@ -769,7 +786,6 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
 
   float W = 0.f, A0 = 0.f, A1 = 0.f;
-  const float* po = a.part_o + base * D;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     float ls = s0 == 0 ? lse0 : (s0 + lane < ns ? a.part_lse[base + s0 + lane] : kNegInf);
     if (s0 + lane >= ns) ls = kNegInf;
@@ -777,27 +793,16 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
     W += w;
     const int wb = __builtin_bit_cast(int, w);
     const int cnt = ns - s0 < 64 ? ns - s0 : 64;
-    int k = 0;
-    for (; k + 8 <= cnt; k += 8) {
-      float v0[8], v1[8];
+    for (int k = 0; k < cnt; k += kSpec) {
+      if (s0 + k > 0) load_batch(s0 + k, ns - 1, v0, v1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float* p = po + (size_t)(s0 + k + i) * D;
-        v0[i] = lane < D ? p[lane] : 0.f;
-        v1[i] = D > 64 ? p[64 + lane] : 0.f;
+      for (int i = 0; i < kSpec; ++i) {
+        const bool ok = k + i < cnt;
+        // lanes past the splits hold w = 0; the select also drops stale slots' values
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
+        A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
+        A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, k + i));
-        A0 = fmaf(wk, v0[i], A0);
-        A1 = fmaf(wk, v1[i], A1);
-      }
-    }
-    for (; k < cnt; ++k) {
-      const float* p = po + (size_t)(s0 + k) * D;
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, k));
-      if (lane < D) A0 = fmaf(wk, p[lane], A0);
-      if (D > 64) A1 = fmaf(wk, p[64 + lane], A1);
     }
   }
 #pragma unroll

@@ -9,6 +9,7 @@
 namespace pa {
 
 constexpr int kBlock = 16;  // tokens per K/V block
+constexpr int kMaxGridYZ = 65535;  // largest grid extent in y and z (rows, splits and heads go there)
 
 // ---- split rule ------------------------------------------------------------------------------
 // A row of n keys is cut into ceil(n / chunk) chunks of `chunk` tokens (the last one shorter);

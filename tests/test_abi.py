@@ -63,6 +63,7 @@ def test_pool_size_query():
     ("dtype", 7, B.PA_ERR_UNSUPPORTED),
     ("layout", 5, B.PA_ERR_UNSUPPORTED),
     ("num_kv_heads", 0, B.PA_ERR_SHAPE),
+    ("num_kv_heads", 65536, B.PA_ERR_SHAPE),
     ("num_blocks", 0, B.PA_ERR_SHAPE),
     ("rope_max_pos", -1, B.PA_ERR_SHAPE),
 ])
@@ -140,6 +141,8 @@ def test_decode_workspace_query():
     (dict(max_kv_len=64 * 16 + 1), B.PA_ERR_SHAPE),
     (dict(q=FAKE + 2), B.PA_ERR_SHAPE),             # misaligned q rows
     (dict(q_row_stride=32 * 64 + 1), B.PA_ERR_SHAPE),
+    (dict(batch=65536), B.PA_ERR_SHAPE),            # rows go to a grid dimension (<= 65535)
+    (dict(bt_stride=4194305, max_kv_len=65536 * 1024 + 1), B.PA_ERR_SHAPE),  # 65537 splits
 ])
 def test_decode_argument_errors(kw, status):
     p = _fake_pool()
@@ -189,10 +192,11 @@ def test_layout_mismatch_and_null_pool():
     (dict(kv_cols=65), B.PA_ERR_SHAPE),                 # > seq_cap
     (dict(gap_start=None), B.PA_ERR_NULL),
     (dict(num_q_heads=40), B.PA_ERR_UNSUPPORTED),       # G = 5
+    (dict(batch=65536, cap=70000), B.PA_ERR_SHAPE),      # rows go to a grid dimension
 ])
 def test_padded_argument_errors(kw, status):
     p = B.Pool()
-    p.desc = B.make_desc("padded", "bf16", 8, 64, batch_cap=4, seq_cap=64)
+    p.desc = B.make_desc("padded", "bf16", 8, 64, batch_cap=kw.get("cap", 4), seq_cap=64)
     p.k, p.v = 0x10000, 0x20000
     args = dict(q=FAKE, num_q_heads=32, batch=4, gap_start=FAKE, gap_end=FAKE, kv_cols=64)
     args.update(kw)
@@ -215,6 +219,7 @@ def test_append_argument_errors():
     assert call(k=None) == B.PA_ERR_NULL
     assert call(qi=FAKE) == B.PA_ERR_NULL               # q_in without q_out
     assert call(batch=-2) == B.PA_ERR_SHAPE
+    assert call(batch=65536) == B.PA_ERR_SHAPE          # rows go to a grid dimension
     assert call(stride=0) == B.PA_ERR_SHAPE
     assert call(qi=FAKE, qo=FAKE, hq=12) == B.PA_ERR_SHAPE
     assert call(batch=0) == B.PA_OK                     # empty batch: a no-op, no launch
