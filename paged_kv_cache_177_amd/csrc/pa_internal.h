@@ -73,6 +73,7 @@ struct DecodeArgs {
   float* part_o;    // [batch][n_q*H_q][s_max][D]
   float* part_lse;  // [batch][n_q*H_q][s_max] (log2 domain)
   int* counter;     // work counter of the persistent decode kernel (0 between calls), or NULL
+  int mq_tiles;     // multi-query path: 16-row query tiles per (row, KV head)
 };
 
 // Workspace of a decode call (0 bytes when no row can split):

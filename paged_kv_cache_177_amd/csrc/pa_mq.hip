@@ -5,7 +5,8 @@
 //
 // Query "rows" of KV head g are the (query i, head h) pairs with h in g's group: r = i * G + (h - gG).
 // One workgroup (4 waves) takes 16 query rows of one (row b, KV head g); its waves split the row's
-// 16-token key blocks round-robin and merge through LDS at the end. Per block, per wave:
+// 16-token key blocks round-robin (two blocks in flight per wave while one is computed) and merge
+// through LDS at the end. Per block, per wave:
 //   S^T[16 keys][16 q] = K[16 keys][D] . Q^T[D][16 q]   v_mfma_f32_16x16x32_bf16, D/32 steps
 //       K is the A operand straight from the block (lane: key l%16, 8 dims), Q^T the B operand
 //       (lane: query l%16, 8 dims); the result puts query l%16 in lane l, keys 4(l/16)..+3.
@@ -16,6 +17,8 @@
 //       P is split into bf16 hi + lo parts (two products), so the weights keep ~16 bits.
 // Query rows therefore sit in the same lanes in S^T and O^T: rescales and the final division are
 // lane-local.
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -32,6 +35,7 @@ constexpr float kRescale = 8.0f;  // log2 units
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaves = 4;
 constexpr int kTileRows = 16;
+constexpr int kXcds = 8;  // accelerator dies of the chip, each with its own L2
 
 __device__ __forceinline__ float swap_rows16(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
@@ -57,13 +61,33 @@ struct MqSmem {
 };
 
 template <int D>
+// D = 32 (the latent cross-attention shape) is held to 7 waves per SIMD (72 registers, no spills):
+// nearly a whole launch of that workload is resident at once. (8 waves spill; measured slower.)
+__attribute__((amdgpu_waves_per_eu(D == 32 ? 7 : 1)))
 __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const DecodeArgs a) {
   constexpr int KC = D / 32;  // k-steps of the score product
   constexpr int NH = D / 16;  // dim tiles of the output product
   __shared__ MqSmem<D> sm;
-  const int tile = blockIdx.x;
-  const int g = blockIdx.y;
-  const int row = blockIdx.z;
+  int tile, g, row;
+  {
+    // Workgroups are dealt to the 8 XCDs round-robin by index. All query tiles of one (row, KV
+    // head) read the same keys and values, so they are numbered to land on one XCD, where the
+    // first tile's reads leave the blocks in that XCD's L2 for the others.
+    const int T = (int)a.mq_tiles;
+    const int P = a.batch * a.H_kv;
+    const int L = (int)blockIdx.x;
+    int pair;
+    if (P % kXcds == 0) {
+      const int q = L / kXcds;
+      tile = q % T;
+      pair = (q / T) * kXcds + L % kXcds;
+    } else {
+      tile = L % T;
+      pair = L / T;
+    }
+    row = pair / a.H_kv;
+    g = pair % a.H_kv;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // query row inside the tile (S^T / O^T column)
@@ -87,8 +111,6 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
       qf[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  const int n = clampi(a.kv_lens[row], 0, a.max_kv_len);
-  const int nblk = (n + kBlock - 1) / kBlock;
   const int* bt = a.block_tables + (size_t)row * a.bt_stride;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v);
@@ -105,9 +127,8 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     u32x4_t k[KC];
     u32x4_t v[D / 32];
   };
-  auto load = [&](Frag& f, int blk) {
-    int pb = bt[blk];
-    pb = (unsigned)pb < (unsigned)a.num_blocks ? pb : 0;
+  // issue the loads of one block (physical id pb, already clamped into the pool)
+  auto load = [&](Frag& f, int pb) {
     const size_t base = ((size_t)pb * a.H_kv + g) * (size_t)(kBlock * D);
     const __bf16* kb = kbase + base + (size_t)col * D + 8 * grp;
 #pragma unroll
@@ -116,7 +137,10 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) f.v[c] = *reinterpret_cast<const u32x4_t*>(vb + 512 * c);
   };
-  auto compute = [&](const Frag& f, int blk) {
+  // One block: scores, online-softmax update, output product. MASK (the row's partial last block
+  // only) drops the keys at or past n: their slots may hold anything, NaN included.
+  auto compute = [&](auto mask_tag, const Frag& f, int blk, int n) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // stage V in this wave's LDS area ([16 keys][D]); the wave reads it back transposed
     u32x4_t* vs = reinterpret_cast<u32x4_t*>(sm.v[wave]);
 #pragma unroll
@@ -130,28 +154,32 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
                                                   0, 0, 0);
     const int key0 = blk * kBlock + 4 * grp;
     bool valid[4];
-    float bm = kNegInf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      valid[j] = key0 + j < n;
-      s[j] = valid[j] ? s[j] : kNegInf;
-      bm = fmaxf(bm, s[j]);
+      valid[j] = !MASK || key0 + j < n;
+      if (MASK) s[j] = valid[j] ? s[j] : kNegInf;
     }
-    bm = fmaxf(bm, swap_rows16(bm));
-    bm = fmaxf(bm, swap_halves32(bm));
-    const float bms = bm * qk_scale;
-    if (bms > m + kRescale) {
-      const float al = exp2_fast(m - bms);
-      l *= al;
+    // The running max of a query is shared by its four key groups (lanes col + 16 grp). It is
+    // raised, to the block maximum over all 16 keys, only when some lane's own keys beat it by
+    // more than kRescale; otherwise the block needs no cross-lane step at all.
+    const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__builtin_amdgcn_ballot_w64(lm * qk_scale > m + kRescale) != 0) {
+      float bm = fmaxf(lm, swap_rows16(lm));
+      bm = fmaxf(bm, swap_halves32(bm));
+      const float bms = bm * qk_scale;
+      if (bms > m + kRescale) {
+        const float al = exp2_fast(m - bms);
+        l *= al;
 #pragma unroll
-      for (int t = 0; t < NH; ++t) o[t] *= al;
-      m = bms;
+        for (int t = 0; t < NH; ++t) o[t] *= al;
+        m = bms;
+      }
     }
     s16x4_t p_hi, p_lo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float p = exp2_fast(fmaf(s[j], qk_scale, -m));
-      p = valid[j] ? p : 0.f;
+      if (MASK) p = valid[j] ? p : 0.f;  // a zero scale would make -inf * 0 a NaN
       l += p;
       const unsigned short h = bf16_bits(p);
       p_hi[j] = (short)h;
@@ -165,22 +193,53 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const unsigned short x = vsh[(4 * grp + j) * D + 16 * t + col];
-        vt[j] = valid[j] ? (short)x : (short)0;
+        vt[j] = (!MASK || valid[j]) ? (short)x : (short)0;
       }
       o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_hi, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_lo, o[t], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   };
+  // full blocks take the unmasked form; the row's partial last block the masked one
+  auto step = [&](const Frag& f, int blk, int n) {
+    if ((blk + 1) * kBlock <= n)
+      compute(std::false_type{}, f, blk, n);
+    else
+      compute(std::true_type{}, f, blk, n);
+  };
 
-  // blocks wave, wave + 4, ...: the next one is always in flight
+  // This wave's blocks are wave, wave + 4, ...; they are taken in windows of up to 64, whose block
+  // ids one load brings in (one per lane; the first window's is issued before the row length is
+  // known: the table row always has bt_stride entries). A ring of three fragments keeps two blocks
+  // in flight while one is computed; the ring is unrolled so no fragment is copied, and every load
+  // is issued unconditionally (past the window's end it re-reads the window's last block, which is
+  // already cached, and the compute is skipped), so each wait covers exactly the fragment it needs.
+  auto window_ids = [&](int w0, int cnt) {
+    const int e = w0 + (lane < cnt ? lane : cnt - 1);
+    const int idx = wave + e * kWaves;
+    const int pb = bt[idx < a.bt_stride ? idx : a.bt_stride - 1];
+    return (unsigned)pb < (unsigned)a.num_blocks ? pb : 0;
+  };
+  int ids = window_ids(0, 64);
+  const int n = clampi(a.kv_lens[row], 0, a.max_kv_len);
+  const int nblk = (n + kBlock - 1) / kBlock;
   const int my = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;
-  Frag f0, f1;
-  if (my > 0) load(f0, wave);
-  for (int i = 0; i < my; ++i) {
-    if (i + 1 < my) load(f1, wave + (i + 1) * kWaves);
-    compute(f0, wave + i * kWaves);
-    f0 = f1;
+  for (int w0 = 0; w0 < my; w0 += 64) {
+    const int cnt = my - w0 < 64 ? my - w0 : 64;
+    if (w0 > 0) ids = window_ids(w0, cnt);
+    auto id_at = [&](int j) { return __builtin_amdgcn_readlane(ids, j < cnt ? j : cnt - 1); };
+    auto blk_at = [&](int j) { return wave + (w0 + j) * kWaves; };
+    Frag f0, f1, f2;
+    load(f0, id_at(0));
+    load(f1, id_at(1));
+    for (int j = 0; j < cnt; j += 3) {
+      load(f2, id_at(j + 2));
+      step(f0, blk_at(j), n);
+      load(f0, id_at(j + 3));
+      if (j + 1 < cnt) step(f1, blk_at(j + 1), n);
+      load(f1, id_at(j + 4));
+      if (j + 2 < cnt) step(f2, blk_at(j + 2), n);
+    }
   }
 
   // merge the key groups' partial sums, then the waves through LDS
@@ -224,16 +283,20 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype != PA_BF16) return hipErrorNotSupported;
   const int rows = a.n_q * (a.H_q / a.H_kv);
-  dim3 grid((rows + kTileRows - 1) / kTileRows, a.H_kv, a.batch);
+  DecodeArgs b = a;
+  b.mq_tiles = (rows + kTileRows - 1) / kTileRows;
+  const long long wgs = (long long)b.mq_tiles * a.H_kv * a.batch;
+  if (wgs * 64 * kWaves > 0xffffffffLL) return hipErrorInvalidValue;  // grid x holds < 2^32 threads
+  const dim3 grid((unsigned)wgs);
   switch (a.D) {
     case 32:
-      hipLaunchKernelGGL(mq_paged_mfma_kernel<32>, grid, dim3(64 * kWaves), 0, stream, a);
+      hipLaunchKernelGGL(mq_paged_mfma_kernel<32>, grid, dim3(64 * kWaves), 0, stream, b);
       break;
     case 64:
-      hipLaunchKernelGGL(mq_paged_mfma_kernel<64>, grid, dim3(64 * kWaves), 0, stream, a);
+      hipLaunchKernelGGL(mq_paged_mfma_kernel<64>, grid, dim3(64 * kWaves), 0, stream, b);
       break;
     case 128:
-      hipLaunchKernelGGL(mq_paged_mfma_kernel<128>, grid, dim3(64 * kWaves), 0, stream, a);
+      hipLaunchKernelGGL(mq_paged_mfma_kernel<128>, grid, dim3(64 * kWaves), 0, stream, b);
       break;
     default:
       return hipErrorInvalidValue;
