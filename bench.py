@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=128 ragged bf16"
+METRIC_LONG = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=4 long-context bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b128_traffic.txt")
 
 
@@ -35,8 +36,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="b128", choices=["b128", "long"],
-                   help="b128 is the reported workload; long is for diagnostics")
+    p.add_argument("--workload", default="b128", choices=["b128", "long", "mq"],
+                   help="b128 is the reported workload; long (B=4 long-context split-K) and mq "
+                        "(latent cross-attention on the matrix cores) measure the other paths")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="cache-flush write between the extra flushed decode timings")
@@ -72,12 +74,36 @@ def read_traffic(src_hash: str):
     return float(vals["hbm_bytes_per_call"])
 
 
+def blas_threads() -> int:
+    import threadpoolctl
+
+    blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+            if p.get("user_api") == "blas"]
+    return int(max(blas)) if blas else 1
+
+
+def cpu_baseline_mq(case, flops: float, budget_s: float = 10.0, max_reps: int = 3):
+    """The oracle on the full multi-query workload (all rows, shared latent queries)."""
+    import oracle as O
+
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_start) < budget_s:
+        t0 = time.perf_counter()
+        O.decode_paged(case.k_pool, case.v_pool, case.dtype, case.block_tables, case.kv_lens,
+                       case.q, case.scale, shared_q=True)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    cores = blas_threads()
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"full {case.name} workload ({len(case.kv_lens)} rows x {case.n_q} queries) "
+                       f"in fp64 numpy, median of {len(times)} run(s), {t:.2f} s each; host "
+                       f"affinity {len(os.sched_getaffinity(0))} cores, BLAS threads {cores}")}
+
+
 def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 3):
     """The oracle (as it stands) on the full workload's decode: gather every row through its block
     table and run two-pass fp64 attention. Repeated until ~budget_s of CPU work, median taken."""
-    import numpy as np
-    import threadpoolctl
-
     import oracle as O
 
     k2, v2, _ = O.append_kv(case.k_pool, case.v_pool, case.dtype, "paged", case.block_tables,
@@ -89,9 +115,7 @@ def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 3):
         O.decode_paged(k2, v2, case.dtype, case.block_tables, case.kv_lens, case.q, case.scale)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
-            if p.get("user_api") == "blas"]
-    cores = max(blas) if blas else 1
+    cores = blas_threads()
     return {"value": case.kv_bytes() / t / 1e9, "unit": "GB/s", "cores": int(cores),
             "kind": "oracle",
             "sample": (f"full {case.name} decode step (all {case.batch} rows, "
@@ -100,12 +124,84 @@ def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 3):
                        f"{len(os.sched_getaffinity(0))} cores, BLAS threads {cores}")}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix-core peak
+
+
+def main_mq(args):
+    """Latent cross-attention on the matrix cores: 16 rows x 256 shared latent queries over ragged
+    spike-token keys (8 heads of 32), one pa_decode_attention call per step."""
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_177_amd.runner import MultiQueryStep
+
+    torch.cuda.set_device(0)
+    case = W.mq()
+    r = MultiQueryStep(case, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    flops = 4.0 * case.n_q * float(case.kv_lens.sum()) * case.num_heads * case.head_dim
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < 1.0:
+        for _ in range(10):
+            r.decode()
+        done += 10
+        torch.cuda.synchronize()
+    # back-to-back calls between one pair of events: the average is the kernel's launch duration
+    # (a call is short enough that events around each one would mostly time the host)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(args.steps):
+        r.decode()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    avg_ms = a.elapsed_time(b) / args.steps
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    out = {
+        "metric": "multi-query latent cross-attention TFLOP/s + us/call, 16 x 256 queries, bf16",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{case.name}: B={len(case.kv_lens)} rows x {case.n_q} shared "
+                                f"latent queries, {case.num_heads} heads of {case.head_dim}, "
+                                f"ragged keys {int(case.kv_lens.min())}..{int(case.kv_lens.max())} "
+                                f"(sum {int(case.kv_lens.sum())}), 16-token blocks, seed "
+                                f"{case.seed}"),
+                   "global_batch": len(case.kv_lens), "flops_per_step": flops,
+                   "step": "one multi-query pa_decode_attention call"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "mq_paged_mfma_kernel", "flops_per_launch": flops,
+                     "avg_launch_us": round(avg_ms * 1e3, 2)},
+        "detail": {"us_per_call": round(avg_ms * 1e3, 2), "source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_mq(case, flops)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "mq":
+        main_mq(args)
+        return
 
     import numpy as np
     import torch
@@ -161,9 +257,9 @@ def main():
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = read_traffic(src_hash)
+    traffic = read_traffic(src_hash) if args.workload == "b128" else None
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "b128" else METRIC_LONG,
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -186,8 +282,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
                                  if traffic is not None else None),
-                     "kernel": "pa_decode_attention call (decode_vector_kernel + "
-                               "lse_reduce_kernel)",
+                     "kernel": ("pa_decode_attention call (decode_vector_kernel + "
+                                "lse_reduce_kernel)") if args.workload == "b128" else
+                               ("pa_decode_attention call (decode_persistent_kernel + "
+                                "lse_reduce_kernel)"),
                      "bytes_per_launch": kv_bytes,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "detail": {"us_per_step": round(ms_per_step * 1e3, 2),

@@ -742,25 +742,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
   }
 }
 
+// Waves that merge one row's splits: a function of the row's own split count only, so a row's
+// result never depends on the rest of the batch. The launch brings reduce_waves(s_max).
+__host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (ns <= 64 ? 4 : 8); }
+
 // Merge the split partials of one (row, query head): out = sum_s w_s o_s / sum_s w_s with
 // w_s = 2^(lse_s - max lse); lse = max + log2(sum w_s), returned in natural-log units.
-// One wave per (row, head). It is latency-bound, so the chain of dependent loads is kept short: the
-// first 64 partial lse values and the first kSpec partial outputs load together with the row length
-// (speculatively: the workspace always holds s_max of each; slots past the row's splits are
-// discarded by a select, so whatever they hold never reaches the sums), and later partial outputs
-// load in batches of kSpec.
-template <bool PADDED>
-__global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
+// reduce_waves(ns) waves share the row's splits in contiguous ranges; each merges its range
+// against its own maximum and wave 0 combines their results in wave order. It is latency-bound,
+// so the chain of dependent loads is kept short: wave 0's first 64 partial lse values and first
+// kSpec partial outputs load together with the row length (speculatively: the workspace always
+// holds s_max of each; slots past the range are dropped by a select, so whatever they hold never
+// reaches the sums), and later partial outputs load in batches of kSpec.
+template <bool PADDED, int NW>
+__global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a) {
   constexpr int kSpec = 8;
+  __shared__ float s_acc[NW][128];
+  __shared__ float s_mw[NW][2];
   const int hq = blockIdx.x;
   const int row = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int D = a.D;
   // the decode kernel has finished: re-arm its work counter for the next call
-  if (a.counter != nullptr && hq == 0 && row == 0 && lane == 0) *a.counter = 0;
+  if (a.counter != nullptr && hq == 0 && row == 0 && threadIdx.x == 0) *a.counter = 0;
   const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
   const float* po = a.part_o + base * D;
-  const float lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
   // this lane's dims (lane, and 64 + lane when D = 128) of the partial outputs of splits
   // s0 + [0, kSpec), indices clamped into [0, last]
   auto load_batch = [&](int s0, int last, float* v0, float* v1) {
@@ -773,40 +780,79 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeArgs a) {
     }
   };
   float v0[kSpec], v1[kSpec];
-  load_batch(0, a.s_max - 1, v0, v1);
+  float lse0 = kNegInf;
+  if (wave == 0) {
+    lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
+    load_batch(0, a.s_max - 1, v0, v1);
+  }
   int gs, gsh;
   const int n = row_valid<PADDED>(a, row, &gs, &gsh);
   const int ns = num_splits(n, chunk_tokens(D));
-  if (ns <= 1) return;
+  if (ns <= 1) return;  // the same for every wave of the workgroup
+  const int nw = reduce_waves(ns);
+  const int per = (ns + nw - 1) / nw;
+  const int sb = wave < nw ? wave * per : ns;
+  const int se = sb + per < ns ? sb + per : ns;
+  if (wave > 0 && sb < se) {
+    lse0 = lane < se - sb ? a.part_lse[base + sb + lane] : kNegInf;
+    load_batch(sb, se - 1, v0, v1);
+  }
 
-  // maximum over the splits' lse
-  float mx = lane < ns ? lse0 : kNegInf;
-  for (int s = 64 + lane; s < ns; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
+  float mx = kNegInf, W = 0.f, A0 = 0.f, A1 = 0.f;
+  if (sb < se) {
+    // maximum over this wave's splits' lse
+    mx = lane < se - sb ? lse0 : kNegInf;
+    for (int s = sb + 64 + lane; s < se; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-
-  float W = 0.f, A0 = 0.f, A1 = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    float ls = s0 == 0 ? lse0 : (s0 + lane < ns ? a.part_lse[base + s0 + lane] : kNegInf);
-    if (s0 + lane >= ns) ls = kNegInf;
-    const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
-    W += w;
-    const int wb = __builtin_bit_cast(int, w);
-    const int cnt = ns - s0 < 64 ? ns - s0 : 64;
-    for (int k = 0; k < cnt; k += kSpec) {
-      if (s0 + k > 0) load_batch(s0 + k, ns - 1, v0, v1);
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int s0 = sb; s0 < se; s0 += 64) {
+      float ls = s0 == sb ? lse0 : (s0 + lane < se ? a.part_lse[base + s0 + lane] : kNegInf);
+      if (s0 + lane >= se) ls = kNegInf;
+      const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
+      W += w;
+      const int wb = __builtin_bit_cast(int, w);
+      const int cnt = se - s0 < 64 ? se - s0 : 64;
+      for (int k = 0; k < cnt; k += kSpec) {
+        if (s0 + k > sb) load_batch(s0 + k, se - 1, v0, v1);
 #pragma unroll
-      for (int i = 0; i < kSpec; ++i) {
-        const bool ok = k + i < cnt;
-        // lanes past the splits hold w = 0; the select also drops stale slots' values
-        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
-        A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
-        A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
+        for (int i = 0; i < kSpec; ++i) {
+          const bool ok = k + i < cnt;
+          // lanes past the range hold w = 0; the select also drops stale slots' values
+          const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
+          A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
+          A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+    for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  }
+  if constexpr (NW > 1) {
+    if (lane < D) s_acc[wave][lane] = A0;
+    if (D > 64) s_acc[wave][64 + lane] = A1;
+    if (lane == 0) {
+      s_mw[wave][0] = mx;
+      s_mw[wave][1] = W;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    if (nw > 1) {
+      float M = kNegInf;
+      for (int w = 0; w < nw; ++w) M = fmaxf(M, s_mw[w][0]);
+      float Wt = 0.f, B0 = 0.f, B1 = 0.f;
+      for (int w = 0; w < nw; ++w) {
+        const float mw = s_mw[w][0];
+        const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+        Wt = fmaf(f, s_mw[w][1], Wt);
+        if (lane < D) B0 = fmaf(f, s_acc[w][lane], B0);
+        if (D > 64) B1 = fmaf(f, s_acc[w][64 + lane], B1);
+      }
+      mx = M;
+      W = Wt;
+      A0 = B0;
+      A1 = B1;
+    }
+  }
   float* out = a.out + ((size_t)row * a.H_q + hq) * D;
   const float inv = W > 0.f ? 1.f / W : 0.f;
   if (lane < D) out[lane] = A0 * inv;
@@ -890,13 +936,26 @@ hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream) {
   return a.dtype == PA_F32 ? launch_t<float>(a, stream) : launch_t<__bf16>(a, stream);
 }
 
-hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.H_q * a.n_q, a.batch);
-  if (a.layout == PA_PADDED)
-    hipLaunchKernelGGL(lse_reduce_kernel<true>, grid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(lse_reduce_kernel<false>, grid, dim3(64), 0, stream, a);
+template <bool PADDED>
+hipError_t launch_lse_reduce_layout(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.H_q * a.n_q, a.batch);
+  switch (reduce_waves(a.s_max)) {
+    case 1:
+      hipLaunchKernelGGL((lse_reduce_kernel<PADDED, 1>), grid, dim3(64), 0, stream, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL((lse_reduce_kernel<PADDED, 4>), grid, dim3(256), 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((lse_reduce_kernel<PADDED, 8>), grid, dim3(512), 0, stream, a);
+      break;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
+  return a.layout == PA_PADDED ? launch_lse_reduce_layout<true>(a, stream)
+                               : launch_lse_reduce_layout<false>(a, stream);
 }
 
 }  // namespace pa
