@@ -97,3 +97,10 @@ def test_padded_matches_paged():
     torch.cuda.synchronize()
     assert_attention_close(out_pad, r.out.cpu().numpy(), "bf16", "padded vs paged")
     assert_attention_close(lse_pad, r.lse.cpu().numpy(), "bf16", "padded vs paged lse")
+
+
+def test_padded_long_rows_multiwave_merge():
+    """Rows of 20 and 70 chunks (their merges run on 4 and 8 waves) next to a short one."""
+    c = W.make_paged_case("padded-long", 34, [99, 20 * 1024 + 7, 70 * 1024 - 9], 8, 2, 64,
+                          "bf16")
+    run_and_check_padded(W.padded_from_paged(c))

@@ -105,6 +105,34 @@ def test_sharp_softmax_and_large_scores():
     run_and_check_paged(case)
 
 
+def _single_row(c, b):
+    return W.PagedCase(**{**c.__dict__,
+                          "n_ctx": c.n_ctx[b:b + 1], "positions": c.positions[b:b + 1],
+                          "dest": c.dest[b:b + 1], "kv_lens": c.kv_lens[b:b + 1],
+                          "block_tables": c.block_tables[b:b + 1],
+                          "k_new": c.k_new[b:b + 1], "v_new": c.v_new[b:b + 1],
+                          "q": c.q[b:b + 1]})
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_merge_wave_counts(D):
+    """One batch whose rows split into 1, 3, 19 and 70 chunks: their log-sum-exp merges run on 1,
+    1, 4 and 8 waves. Every row matches the oracle, and a row decoded on its own (a launch sized
+    for that row alone) gives the same bits as in the batch."""
+    chunk = 1024 if D <= 64 else 512
+    n = [700, 3 * chunk, 18 * chunk + 5, 70 * chunk - 3]
+    case = W.make_paged_case(f"merge-waves-D{D}", 61 + D, [x - 1 for x in n], 8, 2, D, "bf16")
+    r, _, _ = run_and_check_paged(case)
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    for b in range(case.batch):
+        rb = PagedStep(_single_row(case, b))
+        rb.kv = r.kv  # the already-appended pool
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b])
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
+
+
 @pytest.fixture(scope="module")
 def b128_case():
     log("[gen] b128 seed 2")
