@@ -36,9 +36,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="b128", choices=["b128", "long", "mq"],
-                   help="b128 is the reported workload; long (B=4 long-context split-K) and mq "
-                        "(latent cross-attention on the matrix cores) measure the other paths")
+    p.add_argument("--workload", default="b128", choices=["b128", "long", "mq", "b16"],
+                   help="b128 is the reported workload; long (B=4 long-context split-K), mq "
+                        "(latent cross-attention on the matrix cores) and b16 (the B=16 "
+                        "lockstep step, paged and right-padded) measure the other paths")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="cache-flush write between the extra flushed decode timings")
@@ -193,6 +194,106 @@ def main_mq(args):
     print(json.dumps(out), flush=True)
 
 
+def main_b16(args):
+    """The B=16 lockstep step at the protocol's starting geometry (contexts of seed 1, 32/8 heads,
+    D=64, bf16, RoPE theta 1e6): append_kv (keys, values and query rotation) + decode + merge, in
+    the paged form and in the right-padded form. A step moves ~36 MB and is launch-bound, so the
+    line reports microseconds per step, timed over back-to-back steps between one pair of events."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_177_amd import binding as B
+    from paged_kv_cache_177_amd.runner import PaddedLockstep, PagedStep, to_torch
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    plan = W.b16_plan()
+    case = W.make_paged_case("b16", plan.seed, plan.n_ctx0, plan.num_q_heads, plan.num_kv_heads,
+                             plan.head_dim, plan.dtype, rope_theta=plan.rope_theta)
+    kv_bytes = case.kv_bytes()
+    stream = torch.cuda.current_stream()
+    paged = PagedStep(case, device=dev)
+
+    pc = W.padded_from_paged(case)
+    L = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
+                       pc.seq_cap, rope_theta=pc.rope_theta, rope_max_pos=pc.rope_max_pos,
+                       device=dev)
+    L.kv.k.copy_(to_torch(pc.k_pad, pc.dtype))
+    L.kv.v.copy_(to_torch(pc.v_pad, pc.dtype))
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    pos, dest = d(pc.positions), d(pc.dest)
+    k_new, v_new = to_torch(pc.k_new, pc.dtype).to(dev), to_torch(pc.v_new, pc.dtype).to(dev)
+    q_in = to_torch(pc.q, pc.dtype).to(dev)
+    q_rot = torch.empty_like(q_in)
+    gs, ge = d(pc.prefix_lens.astype(np.int32)), d(np.full(pc.batch, pc.padded_len, np.int32))
+    out = torch.empty((pc.batch, pc.num_q_heads, pc.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((pc.batch, pc.num_q_heads), dtype=torch.float32, device=dev)
+    need = B.pa_decode_attention_padded(L.kv.pool, q_rot, pc.num_q_heads, pc.batch, gs, ge,
+                                        pc.kv_cols, pc.scale, out=out, query_workspace=True)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def padded_step():
+        L.append(pos, dest, k_new, v_new, q_in, q_rot)
+        B.pa_decode_attention_padded(L.kv.pool, q_rot, pc.num_q_heads, pc.batch, gs, ge,
+                                     pc.kv_cols, pc.scale, workspace=ws if need else None,
+                                     out=out, lse=lse)
+
+    def timed(fn):
+        t_w = time.perf_counter()
+        done = 0
+        while done < args.warmup or time.perf_counter() - t_w < 1.0:
+            for _ in range(10):
+                fn()
+            done += 10
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / args.steps, a.elapsed_time(b) * 1e3 / args.steps
+
+    wall_paged, ev_paged = timed(paged.step)
+    wall_padded, ev_padded = timed(padded_step)
+    out_line = {
+        "metric": "B=16 lockstep decode step us (append + decode + merge), paged, bf16",
+        "value": round(ev_paged, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_paged / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"b16: B=16 ragged contexts {int(case.n_ctx.min())}.."
+                                f"{int(case.n_ctx.max())} (kv_len sum {int(case.kv_lens.sum())}), "
+                                f"H_q=32, H_kv=8, D=64, 16-token blocks, RoPE theta 1e6, seed "
+                                f"{plan.seed}"),
+                   "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
+                   "step": "append_kv (k, v, q rotation) + decode + lse merge"},
+        "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (ev_paged * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kv_bytes / (ev_paged * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "whole step (launch-bound)",
+                     "bytes_per_launch": kv_bytes, "avg_launch_us": round(ev_paged, 2)},
+        "detail": {"paged_us_per_step_events": round(ev_paged, 2),
+                   "paged_us_per_step_wall": round(wall_paged, 2),
+                   "padded_us_per_step_events": round(ev_padded, 2),
+                   "padded_us_per_step_wall": round(wall_padded, 2),
+                   "source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        out_line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -201,6 +302,9 @@ def main():
         sys.exit(2)
     if args.workload == "mq":
         main_mq(args)
+        return
+    if args.workload == "b16":
+        main_b16(args)
         return
 
     import numpy as np

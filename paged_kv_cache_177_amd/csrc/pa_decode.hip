@@ -30,7 +30,7 @@
 //     lse_reduce_kernel.
 //   * Two launch shapes run the same chunks: a grid of one workgroup per (g, b, s) whose
 //     workgroups past a row's last split exit at once, and a persistent grid that pulls chunks
-//     from a counter (see decode_persistent_kernel), used when there are few (row, head) pairs.
+//     from a counter (see decode_persistent_kernel), used when rows are long enough for many splits.
 #include "pa_internal.h"
 
 #include <map>
@@ -510,6 +510,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
 // merged and written. The split of each row is the same
 // as in the grid kernel, so results are identical.
 constexpr int kMaxRows = 1024;
+constexpr int kPersistentMinSplits = 16;  // s_max from which the persistent launch is used
 
 template <bool PADDED>
 struct RowSmem {
@@ -885,13 +886,15 @@ int resident_workgroups(const void* kernel, size_t lds) {
 template <typename T, int D, int G, bool PADDED>
 hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   const long long items = (long long)a.batch * a.H_kv * a.s_max;
-  // Few (row, KV head) pairs with many splits each (long rows): most of a split grid's workgroups
-  // would find nothing to do, so the persistent kernel takes over. Otherwise the split grid runs,
-  // with more waves per SIMD. Both cut rows into the same chunks: their results are identical.
+  // Rows long enough for many splits: the split grid would cover s_max splits of every row, and
+  // the rows' differing lengths leave many of its workgroups with nothing to do, so the persistent
+  // kernel takes over. With few splits per row the split grid starts faster (a workgroup needs
+  // no row scan before its first loads) and runs more waves per SIMD. Both cut rows into the
+  // same chunks: their results are identical.
   if (PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows) {
     auto kern = decode_persistent_kernel<T, D, G, PADDED>;
     const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
-    if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || (long long)a.batch * a.H_kv * 2 <= resident)) {
+    if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits)) {
       const int grid = (int)(items < resident ? items : resident);
       hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), 0, stream, a);
       return hipGetLastError();

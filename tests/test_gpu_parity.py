@@ -117,8 +117,9 @@ def _single_row(c, b):
 @pytest.mark.parametrize("D", [64, 128])
 def test_split_merge_wave_counts(D):
     """One batch whose rows split into 1, 3, 19 and 70 chunks: their log-sum-exp merges run on 1,
-    1, 4 and 8 waves. Every row matches the oracle, and a row decoded on its own (a launch sized
-    for that row alone) gives the same bits as in the batch."""
+    1, 4 and 8 waves. Every row matches the oracle, and a row decoded on its own gives the same
+    bits as in the batch, although the launches differ: the batch (70 splits) runs the persistent
+    kernel with an 8-wave merge, the two short rows alone run the split grid with a 1-wave one."""
     chunk = 1024 if D <= 64 else 512
     n = [700, 3 * chunk, 18 * chunk + 5, 70 * chunk - 3]
     case = W.make_paged_case(f"merge-waves-D{D}", 61 + D, [x - 1 for x in n], 8, 2, D, "bf16")
@@ -146,8 +147,8 @@ def test_b128_full_size_sampled_rows(b128_case):
     order = np.argsort(c.kv_lens)
     rows = np.unique(np.concatenate([order[:3], order[-3:], order[::21]]))
     r, _, _ = run_and_check_paged(c, rows=rows)
-    # a row decoded on its own (few rows: the persistent launch) gives the same bits as in the
-    # full batch (many rows: the split grid)
+    # a row decoded on its own (a launch sized for that row: other grid, other s_max) gives the
+    # same bits as in the full batch
     out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
     for b in [int(order[0]), int(order[-1]), 77]:
         cb = W.PagedCase(**{**c.__dict__,
