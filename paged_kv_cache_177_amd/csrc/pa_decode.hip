@@ -754,10 +754,12 @@ __host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (
 // so the chain of dependent loads is kept short: wave 0's first 64 partial lse values and first
 // kSpec partial outputs load together with the row length (speculatively: the workspace always
 // holds s_max of each; slots past the range are dropped by a select, so whatever they hold never
-// reaches the sums), and later partial outputs load in batches of kSpec.
+// reaches the sums), and later partial outputs load in batches of kSpec (8, 16 or 32 with the
+// wave count).
 template <bool PADDED, int NW>
 __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a) {
-  constexpr int kSpec = 8;
+  // partial outputs per batch of loads: a long row's wave covers its whole range in one or two
+  constexpr int kSpec = NW == 1 ? 8 : (NW == 4 ? 16 : 32);
   __shared__ float s_acc[NW][128];
   __shared__ float s_mw[NW][2];
   const int hq = blockIdx.x;
