@@ -21,9 +21,12 @@ from .reference import (  # noqa: F401
     attend_brute_force,
     attend_online_tiled,
     attend_split_merge,
+    attend_block_sparse,
+    attend_block_mask_additive,
     merge_partials,
     decode_paged,
     decode_padded,
+    decode_paged_block_sparse,
     decode_padded_additive_mask,
     padded_valid_columns,
     extract_row_padded,

@@ -34,6 +34,11 @@ Open points of the pages and the reading taken here:
     multiply-add), so that the stored keys are reproducible bit for bit.
   * GQA: query head h reads KV head h // G with G = H_q / H_kv (consecutive grouping).
   * A row with no valid key gives out = 0 and lse = -inf.
+  * Block-sparse cross-attention [CX-K]: the mask is given per (block of 16 consecutive queries,
+    16-token key block); query i of a row attends exactly to the keys of the blocks j with
+    keep[i // 16][j]. The pages state only a boolean tile mask computed outside the kernel; the
+    16 x 16 tile granularity is this library's reading (one matrix-core tile of queries by one
+    K/V block of keys).
 """
 
 from __future__ import annotations
@@ -286,6 +291,52 @@ def attend_split_merge(q, K, V, scale, bounds):
     return merge_partials(outs, lses)
 
 
+def attend_block_sparse(q, K, V, scale, keep):
+    """Block-sparse cross-attention for one row [CX-K]: query i attends to the keys of the 16-token
+    blocks j with keep[i // 16, j] and to no other; with no kept key it gives out = 0 and
+    lse = -inf (the guard for a fully masked row).
+
+    q (n_q, H_q, D), K/V (n, H_kv, D) fp64; keep bool (ceil(n_q / 16), >= ceil(n / 16)).
+    Each query is exact softmax attention over its kept key set (the two-pass definition)."""
+    n_q, H_q, D = q.shape
+    n = K.shape[0]
+    out = np.zeros((n_q, H_q, D), dtype=np.float64)
+    lse = np.full((n_q, H_q), -np.inf, dtype=np.float64)
+    for i in range(n_q):
+        cols = [t for t in range(n) if keep[i // BLOCK, t // BLOCK]]
+        if cols:
+            o, l = attend_two_pass(q[i:i + 1], K[cols], V[cols], scale)
+            out[i] = o[0]
+            lse[i] = l[0]
+    return out, lse
+
+
+def attend_block_mask_additive(q, K, V, scale, keep):
+    """The same block-sparse attention written as dense scores plus an additive mask: -inf on the
+    scores of dropped (query, key) pairs, then one softmax per query; a query whose scores are all
+    -inf gives out = 0 and lse = -inf. Self-check of ``attend_block_sparse``."""
+    n_q, H_q, D = q.shape
+    n, H_kv, _ = K.shape
+    G = H_q // H_kv
+    out = np.zeros((n_q, H_q, D), dtype=np.float64)
+    lse = np.full((n_q, H_q), -np.inf, dtype=np.float64)
+    if n == 0:
+        return out, lse
+    qi = np.arange(n_q)[:, None] // BLOCK
+    kj = np.arange(n)[None, :] // BLOCK
+    add = np.where(keep[qi, kj], 0.0, -np.inf)  # (n_q, n)
+    for h in range(H_q):
+        g = h // G
+        s = scale * (q[:, h, :] @ K[:, g, :].T) + add
+        m = s.max(axis=1)
+        live = np.isfinite(m)
+        w = np.exp(s[live] - m[live, None])
+        l = w.sum(axis=1)
+        out[live, h, :] = (w @ V[:, g, :]) / l[:, None]
+        lse[live, h] = m[live] + np.log(l)
+    return out, lse
+
+
 # --------------------------------------------------------------------------------------------
 # Batched decode entry points (the operations the library exports)
 # --------------------------------------------------------------------------------------------
@@ -388,3 +439,21 @@ def assemble_padded(histories, seq_cap, fill):
         k_pad[b, :, :kh.shape[1], :] = kh
         v_pad[b, :, :vh.shape[1], :] = vh
     return k_pad, v_pad, prefix, int(prefix.max(initial=0))
+
+
+def decode_paged_block_sparse(k_pool, v_pool, dtype, block_tables, kv_lens, q, scale, keep,
+                              shared_q=False):
+    """Block-sparse multi-query decode over the paged pool [CX-K], [NG-0.7]: row b's queries attend
+    over its first kv_len tokens (gathered through its block table), restricted by keep[b]
+    (bool (B, ceil(n_q / 16), >= ceil(max kv_len / 16))). q as for ``decode_paged``."""
+    B = len(kv_lens)
+    outs, lses = [], []
+    for b in range(B):
+        qb = storage_to_f64(np.asarray(q if shared_q else q[b]), dtype)
+        if qb.ndim == 2:
+            qb = qb[None]
+        K, V = gather_paged(k_pool, v_pool, dtype, block_tables[b], kv_lens[b])
+        o, l = attend_block_sparse(qb, K, V, scale, np.asarray(keep[b], dtype=bool))
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)

@@ -434,3 +434,111 @@ def test_padding_is_position_inert():
     for o, l in res[1:]:
         np.testing.assert_array_equal(o, res[0][0])
         np.testing.assert_array_equal(l, res[0][1])
+
+
+# ---------------------------------------------------------------------------------------------
+# Block-sparse cross-attention (query blocks of 16 x 16-token key blocks)
+# ---------------------------------------------------------------------------------------------
+def _keep(rng, n_q, n, p=0.5):
+    return rng.random(((n_q + 15) // 16, (n + 15) // 16)) < p
+
+
+@pytest.mark.parametrize("n,n_q,H_q,H_kv,D", [(40, 20, 4, 4, 32), (150, 37, 8, 2, 64),
+                                              (64, 24, 8, 8, 16)])
+def test_block_sparse_matches_torch_sdpa_with_bool_mask(n, n_q, H_q, H_kv, D):
+    """Library routine: torch CPU scaled_dot_product_attention in fp64 with a boolean attn_mask
+    built elementwise from the block mask (True = the pair takes part). Queries that keep no key
+    are left out of torch's comparison (torch gives NaN there) and must be 0 / -inf here."""
+    rng = _rng(500 + n)
+    q, K, V = _rand_row(rng, n, H_q, H_kv, D, n_q)
+    keep = _keep(rng, n_q, n)
+    keep[0, :] = False  # the first query block keeps nothing
+    scale = W.fp32_scale(D)
+    out, lse = O.attend_block_sparse(q, K, V, scale, keep)
+    G = H_q // H_kv
+    pair = np.array([[keep[i // 16, t // 16] for t in range(n)] for i in range(n_q)])
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+    tv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+    mask = torch.from_numpy(pair)[None].expand(H_q, n_q, n)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                           scale=scale).permute(1, 0, 2).numpy()
+    live = pair.any(axis=1)
+    assert live.any() and not live.all()
+    np.testing.assert_allclose(out[live], ref[live], rtol=0, atol=1e-12)
+    assert np.all(out[~live] == 0) and np.all(np.isneginf(lse[~live]))
+    s = scale * np.einsum("hqd,hkd->hqk", tq.numpy(), tk.numpy())
+    s = np.where(pair[None], s, -np.inf)
+    ref_lse = scipy.special.logsumexp(s[:, live, :], axis=-1).T
+    np.testing.assert_allclose(lse[live], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_block_sparse_special_cases():
+    rng = _rng(510)
+    q, K, V = _rand_row(rng, 70, 4, 2, 32, n_q=33)
+    scale = 0.17
+    # every block kept: the dense definition (per-query products sum in another order than the
+    # batched one, so equal up to rounding)
+    full = np.ones((3, 5), dtype=bool)
+    o1, l1 = O.attend_block_sparse(q, K, V, scale, full)
+    o2, l2 = O.attend_two_pass(q, K, V, scale)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+    # nothing kept: zeros and -inf, no NaN
+    o, l = O.attend_block_sparse(q, K, V, scale, ~full)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    # 65 keys: key block 4 holds one token (key 64); with only that block kept, for the second
+    # query block only, those queries get that value exactly and the others zeros
+    one = np.zeros((3, 5), dtype=bool)
+    one[1, 4] = True
+    o, l = O.attend_block_sparse(q, K[:65], V[:65], scale, one)
+    for i in range(16, 32):
+        for h in range(4):
+            np.testing.assert_array_equal(o[i, h], V[64, h // 2])
+            assert l[i, h] == pytest.approx(scale * q[i, h] @ K[64, h // 2], abs=1e-14)
+    assert np.all(o[:16] == 0) and np.all(o[32:] == 0)
+    # the mask indexes queries (i // 16) and keys (t // 16), not the other way round: tile 0 keeps
+    # only key block 1 and tile 1 only key block 0; each equals dense attention over that slice
+    sw = np.zeros((3, 5), dtype=bool)
+    sw[0, 1] = True
+    sw[1, 0] = True
+    o, _ = O.attend_block_sparse(q, K, V, scale, sw)
+    d1, _ = O.attend_two_pass(q[:16], K[16:32], V[16:32], scale)
+    d0, _ = O.attend_two_pass(q[16:32], K[:16], V[:16], scale)
+    np.testing.assert_allclose(o[:16], d1, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[16:32], d0, rtol=0, atol=1e-14)
+
+
+def test_block_sparse_brute_force_and_additive_form():
+    rng = _rng(520)
+    for n, n_q in [(5, 3), (17, 18), (40, 33)]:
+        q, K, V = _rand_row(rng, n, 4, 2, 8, n_q)
+        keep = _keep(rng, n_q, n, 0.6)
+        o1, l1 = O.attend_block_sparse(q, K, V, 0.31, keep)
+        o3, l3 = O.attend_block_mask_additive(q, K, V, 0.31, keep)
+        np.testing.assert_allclose(o1, o3, rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(np.isneginf(l1), np.isneginf(l3))
+        fin = np.isfinite(l1)
+        np.testing.assert_allclose(l1[fin], l3[fin], rtol=0, atol=1e-14)
+        # brute force, query by query over the kept keys written out by hand
+        for i in range(n_q):
+            cols = [t for t in range(n) if keep[i // 16, t // 16]]
+            ob, lb = O.attend_brute_force(q[i:i + 1], K[cols], V[cols], 0.31)
+            np.testing.assert_allclose(o1[i], ob[0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(l1[i], lb[0], rtol=0, atol=1e-13)
+
+
+def test_block_sparse_batched_equals_per_row():
+    """Batched paged form vs each row alone on its gathered keys."""
+    c = W.make_paged_case("bs-oracle", 530, [20, 47, 0, 33], 4, 2, 16, "bf16")
+    rng = _rng(531)
+    n_q = 20
+    q = W.to_storage(rng.standard_normal((n_q, 4, 16), dtype=np.float32), "bf16")
+    keep = rng.random((4, 2, 4)) < 0.5
+    out, lse = O.decode_paged_block_sparse(c.k_pool, c.v_pool, "bf16", c.block_tables,
+                                           c.kv_lens - 1, q, c.scale, keep, shared_q=True)
+    for b in range(4):
+        K, V = O.gather_paged(c.k_pool, c.v_pool, "bf16", c.block_tables[b], c.kv_lens[b] - 1)
+        o, l = O.attend_block_sparse(O.storage_to_f64(q, "bf16"), K, V, c.scale, keep[b])
+        np.testing.assert_array_equal(out[b], o)
+        np.testing.assert_array_equal(lse[b], l)
