@@ -11,13 +11,15 @@
  *   - batched single-token decode attention over the paged cache with GQA and an online softmax
  *     ("NeuroGrid releases", v0.7.0 and v0.6.0 "Flash Decode Attention Kernel"); with several
  *     queries per row it is the ragged multi-query cross-attention of the "cortex-engine
- *     write-up", kernels section (block-sparse cross-attention);
+ *     write-up", kernels section, which pa_decode_attention_block_sparse also runs under a
+ *     caller's boolean (query block x key block) mask (block-sparse cross-attention);
  *   - the lockstep form over right-padded per-row KV with one padding gap per row
  *     ("helexa PR #121", commit "slice 1": assemble_batch, batch_decode_mask).
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host). The caller owns every buffer; the library
- *     allocates nothing, keeps no global state and never synchronises (except pa_alloc_pool, which
+ *     allocates nothing, keeps no state beyond a host-side cache of per-kernel occupancy figures
+ *     (filled on first use, thread-safe) and never synchronises (except pa_alloc_pool, which
  *     waits for its own table upload). Work is enqueued on `stream` and returns at once.
  *   - Validation of host-side arguments happens before any HIP call; a failed check returns an
  *     error code and launches nothing. A failed launch returns PA_ERR_HIP. No C++ exception
@@ -146,6 +148,28 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
                               int32_t max_kv_len, float scale, void* workspace,
                               size_t workspace_bytes, size_t* workspace_needed /* host */,
                               float* out, float* lse, hipStream_t stream);
+
+/* Block-sparse multi-query decode attention over the paged cache ("cortex-engine write-up",
+ * kernels section, block-sparse cross-attention: a boolean tile mask computed outside the kernel;
+ * tiles whose mask is false are skipped; a query left with no key gives zeros, not NaN).
+ *
+ * As pa_decode_attention (same q, q_row_stride, block_tables, kv_lens, out and lse contracts),
+ * plus block_mask: uint8 [batch][ceil(n_q / 16)][mask_kv_blocks] (device). Query i of row b
+ * attends exactly to the keys of the 16-token blocks j (tokens 16j .. 16j + 15, j < ceil(kv_len /
+ * 16)) with block_mask[b][i / 16][j] != 0; a query with no such key gets out = 0 and lse = -inf.
+ * mask_kv_blocks is the row stride of the mask, >= ceil(max_kv_len / 16). Every query head of a
+ * query shares the query's mask. Runs on the matrix cores for any n_q >= 1; a row is never split,
+ * so no workspace is needed. Dropped blocks are neither read nor computed.
+ * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, block_mask, out); PA_ERR_SHAPE (as for
+ * pa_decode_attention, and mask_kv_blocks < max(1, ceil(max_kv_len / 16))); PA_ERR_UNSUPPORTED
+ * (fp32 pool). batch == 0 is a no-op. */
+pa_status pa_decode_attention_block_sparse(const pa_pool* pool, const void* q,
+                                           int64_t q_row_stride, int32_t n_q, int32_t num_q_heads,
+                                           const int32_t* block_tables, int32_t bt_stride,
+                                           const int32_t* kv_lens, int32_t batch,
+                                           int32_t max_kv_len, float scale,
+                                           const uint8_t* block_mask, int32_t mask_kv_blocks,
+                                           float* out, float* lse, hipStream_t stream);
 
 /* Lockstep decode over right-padded KV (PA_PADDED pool).
  *

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSU
 PA_F32, PA_BF16 = 0, 1
 PA_PAGED, PA_PADDED = 0, 1
 
-EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded")
+EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
+           "pa_decode_attention_block_sparse")
 
 
 class PaError(RuntimeError):
@@ -70,6 +71,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_attention_padded.argtypes = [ctypes.POINTER(Pool), _P, _I32, _I32, _P, _P, _I32,
                                                ctypes.c_float, _P, ctypes.c_size_t, _SIZE_P, _P,
                                                _P, _P]
+    lib.pa_decode_attention_block_sparse.argtypes = [ctypes.POINTER(Pool), _P, ctypes.c_int64,
+                                                     _I32, _I32, _P, _I32, _P, _I32, _I32,
+                                                     ctypes.c_float, _P, _I32, _P, _P, _P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -145,6 +149,22 @@ def pa_decode_attention(pool: Pool, q, q_row_stride: int, n_q: int, num_q_heads:
                                  _ptr(lse), _stream(stream))
     _check("pa_decode_attention", st)
     return need.value
+
+
+def pa_decode_attention_block_sparse(pool: Pool, q, q_row_stride: int, n_q: int,
+                                     num_q_heads: int, block_tables, bt_stride: int, kv_lens,
+                                     batch: int, max_kv_len: int, scale: float, block_mask,
+                                     mask_kv_blocks: int, out=None, lse=None, stream=None) -> None:
+    """Enqueue the block-sparse multi-query decode (block_mask: uint8 device
+    [batch][ceil(n_q / 16)][mask_kv_blocks])."""
+    lib = load_library()
+    st = lib.pa_decode_attention_block_sparse(ctypes.byref(pool), _ptr(q), q_row_stride, n_q,
+                                              num_q_heads, _ptr(block_tables), bt_stride,
+                                              _ptr(kv_lens), batch, max_kv_len,
+                                              ctypes.c_float(scale), _ptr(block_mask),
+                                              mask_kv_blocks, _ptr(out), _ptr(lse),
+                                              _stream(stream))
+    _check("pa_decode_attention_block_sparse", st)
 
 
 def pa_decode_attention_padded(pool: Pool, q, num_q_heads: int, batch: int, gap_start, gap_end,

@@ -226,6 +226,57 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   return map_hip(e);
 }
 
+extern "C" pa_status pa_decode_attention_block_sparse(
+    const pa_pool* pool, const void* q, int64_t q_row_stride, int32_t n_q, int32_t num_q_heads,
+    const int32_t* block_tables, int32_t bt_stride, const int32_t* kv_lens, int32_t batch,
+    int32_t max_kv_len, float scale, const uint8_t* block_mask, int32_t mask_kv_blocks,
+    float* out, float* lse, hipStream_t stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  const pa_pool_desc& d = pool->desc;
+  if (d.layout != PA_PAGED) return PA_ERR_SHAPE;
+  if (q == nullptr || block_tables == nullptr || kv_lens == nullptr || out == nullptr ||
+      block_mask == nullptr)
+    return PA_ERR_NULL;
+  if (batch < 0 || batch > pa::kMaxGridYZ || n_q < 1 || bt_stride < 1 || max_kv_len < 0 ||
+      q_row_stride < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_kv_len > (int64_t)bt_stride * pa::kBlock) return PA_ERR_SHAPE;
+  const int64_t kv_blocks = ((int64_t)max_kv_len + pa::kBlock - 1) / pa::kBlock;
+  if (mask_kv_blocks < 1 || (int64_t)mask_kv_blocks < kv_blocks) return PA_ERR_SHAPE;
+  if (d.dtype != PA_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core path: bf16 only
+  if (!q_aligned(q, q_row_stride, d.dtype)) return PA_ERR_SHAPE;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+
+  pa::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.layout = PA_PAGED;
+  a.dtype = d.dtype;
+  a.H_kv = d.num_kv_heads;
+  a.H_q = num_q_heads;
+  a.D = d.head_dim;
+  a.n_q = n_q;
+  a.num_blocks = d.num_blocks;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.q = q;
+  a.q_row_stride = q_row_stride;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.kv_lens = kv_lens;
+  a.batch = batch;
+  a.max_kv_len = max_kv_len;
+  a.s_max = 1;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.block_mask = block_mask;
+  a.mask_kv_blocks = mask_kv_blocks;
+  return map_hip(pa::launch_decode_mq(a, stream));
+}
+
 extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
                                                 int32_t num_q_heads, int32_t batch,
                                                 const int32_t* gap_start, const int32_t* gap_end,

@@ -74,6 +74,9 @@ struct DecodeArgs {
   float* part_lse;  // [batch][n_q*H_q][s_max] (log2 domain)
   int* counter;     // work counter of the persistent decode kernel (0 between calls), or NULL
   int mq_tiles;     // multi-query path: 16-row query tiles per (row, KV head)
+  // block-sparse multi-query path: keep flags [batch][ceil(n_q / 16)][mask_kv_blocks], or NULL
+  const uint8_t* block_mask;
+  int mask_kv_blocks;
 };
 
 // Workspace of a decode call (0 bytes when no row can split):

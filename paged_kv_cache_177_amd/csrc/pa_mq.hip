@@ -55,12 +55,13 @@ __device__ __forceinline__ float bf16_value(unsigned short b) {
 template <int D>
 struct MqSmem {
   unsigned short v[kWaves][kBlock * D];  // each wave's staged V block
+  int kept[kWaves][64];                  // block-sparse: each wave's kept blocks of its window
   float o[kWaves][D][kTileRows];
   float m[kWaves][kTileRows];
   float l[kWaves][kTileRows];
 };
 
-template <int D>
+template <int D, bool SPARSE>
 // D = 32 (the latent cross-attention shape) is held to 7 waves per SIMD (72 registers, no spills):
 // nearly a whole launch of that workload is resident at once. (8 waves spill; measured slower.)
 __attribute__((amdgpu_waves_per_eu(D == 32 ? 7 : 1)))
@@ -220,25 +221,58 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     const int pb = bt[idx < a.bt_stride ? idx : a.bt_stride - 1];
     return (unsigned)pb < (unsigned)a.num_blocks ? pb : 0;
   };
+  // block-sparse: this tile's keep flags (one per 16-token key block); all rows of a 16-row tile
+  // belong to one block of 16 queries, tile / G
+  const uint8_t* keep_row = nullptr;
+  if constexpr (SPARSE) {
+    const int n_qb = (a.n_q + kTileRows - 1) / kTileRows;
+    keep_row = a.block_mask + ((size_t)row * n_qb + tile / G) * a.mask_kv_blocks;
+  }
+  auto window_keep = [&](int w0, int cnt) {
+    const int idx = wave + (w0 + lane) * kWaves;
+    return lane < cnt && idx < a.mask_kv_blocks && keep_row[idx] != 0;
+  };
   int ids = window_ids(0, 64);
+  bool keep0 = false;
+  if constexpr (SPARSE) keep0 = window_keep(0, 64);
   const int n = clampi(a.kv_lens[row], 0, a.max_kv_len);
   const int nblk = (n + kBlock - 1) / kBlock;
   const int my = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;
   for (int w0 = 0; w0 < my; w0 += 64) {
     const int cnt = my - w0 < 64 ? my - w0 : 64;
     if (w0 > 0) ids = window_ids(w0, cnt);
-    auto id_at = [&](int j) { return __builtin_amdgcn_readlane(ids, j < cnt ? j : cnt - 1); };
-    auto blk_at = [&](int j) { return wave + (w0 + j) * kWaves; };
+    // the window's blocks to visit, in order: all of them, or (block-sparse) the kept ones,
+    // compacted so that lane j holds the window position of the j-th kept block
+    int nv = cnt;
+    int pos = lane;
+    if constexpr (SPARSE) {
+      const bool k = (w0 > 0 ? window_keep(w0, cnt) : keep0) && lane < cnt;
+      const unsigned long long kept = __builtin_amdgcn_ballot_w64(k);
+      nv = __builtin_popcountll(kept);
+      const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(kept >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((unsigned)kept, 0));
+      if (k) sm.kept[wave][rank] = lane;
+      __builtin_amdgcn_wave_barrier();
+      pos = lane < nv ? sm.kept[wave][lane] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (nv == 0) continue;
+    }
+    auto pos_at = [&](int j) {
+      const int jj = j < nv ? j : nv - 1;
+      return SPARSE ? __builtin_amdgcn_readlane(pos, jj) : jj;
+    };
+    auto id_at = [&](int j) { return __builtin_amdgcn_readlane(ids, pos_at(j)); };
+    auto blk_at = [&](int j) { return wave + (w0 + pos_at(j)) * kWaves; };
     Frag f0, f1, f2;
     load(f0, id_at(0));
     load(f1, id_at(1));
-    for (int j = 0; j < cnt; j += 3) {
+    for (int j = 0; j < nv; j += 3) {
       load(f2, id_at(j + 2));
       step(f0, blk_at(j), n);
       load(f0, id_at(j + 3));
-      if (j + 1 < cnt) step(f1, blk_at(j + 1), n);
+      if (j + 1 < nv) step(f1, blk_at(j + 1), n);
       load(f1, id_at(j + 4));
-      if (j + 2 < cnt) step(f2, blk_at(j + 2), n);
+      if (j + 2 < nv) step(f2, blk_at(j + 2), n);
     }
   }
 
@@ -278,6 +312,25 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   }
 }
 
+template <bool SPARSE>
+hipError_t launch_mq(const DecodeArgs& b, dim3 grid, hipStream_t stream) {
+  switch (b.D) {
+    case 32:
+      hipLaunchKernelGGL((mq_paged_mfma_kernel<32, SPARSE>), grid, dim3(64 * kWaves), 0, stream, b);
+      break;
+    case 64:
+      hipLaunchKernelGGL((mq_paged_mfma_kernel<64, SPARSE>), grid, dim3(64 * kWaves), 0, stream, b);
+      break;
+    case 128:
+      hipLaunchKernelGGL((mq_paged_mfma_kernel<128, SPARSE>), grid, dim3(64 * kWaves), 0, stream,
+                         b);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream) {
@@ -288,20 +341,8 @@ hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream) {
   const long long wgs = (long long)b.mq_tiles * a.H_kv * a.batch;
   if (wgs * 64 * kWaves > 0xffffffffLL) return hipErrorInvalidValue;  // grid x holds < 2^32 threads
   const dim3 grid((unsigned)wgs);
-  switch (a.D) {
-    case 32:
-      hipLaunchKernelGGL(mq_paged_mfma_kernel<32>, grid, dim3(64 * kWaves), 0, stream, b);
-      break;
-    case 64:
-      hipLaunchKernelGGL(mq_paged_mfma_kernel<64>, grid, dim3(64 * kWaves), 0, stream, b);
-      break;
-    case 128:
-      hipLaunchKernelGGL(mq_paged_mfma_kernel<128>, grid, dim3(64 * kWaves), 0, stream, b);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return b.block_mask != nullptr ? launch_mq<true>(b, grid, stream)
+                                 : launch_mq<false>(b, grid, stream);
 }
 
 }  // namespace pa

@@ -242,3 +242,19 @@ def test_multi_query_needs_bf16():
         B.pa_decode_attention(p, FAKE, 0, 16, 8, FAKE, 64, FAKE, 4, 1000, 0.125, out=FAKE,
                               query_workspace=True)
     assert e.value.status == B.PA_ERR_UNSUPPORTED
+
+
+def test_block_sparse_argument_errors():
+    lib = B.load_library()
+    p = _fake_pool()
+    call = lambda **kw: lib.pa_decode_attention_block_sparse(  # noqa: E731
+        ctypes.byref(kw.get("pool", p)), FAKE, 0, kw.get("n_q", 32), 32, FAKE, 64, FAKE,
+        kw.get("batch", 4), kw.get("max_len", 1000), ctypes.c_float(0.125),
+        kw.get("mask", FAKE), kw.get("width", 63), FAKE, None, None)
+    assert call(mask=None) == B.PA_ERR_NULL
+    assert call(width=62) == B.PA_ERR_SHAPE        # < ceil(1000 / 16) = 63 key blocks
+    assert call(width=0, max_len=0) == B.PA_ERR_SHAPE
+    assert call(n_q=0) == B.PA_ERR_SHAPE
+    assert call(batch=65536) == B.PA_ERR_SHAPE
+    assert call(pool=_fake_pool(dtype="f32")) == B.PA_ERR_UNSUPPORTED
+    assert call(batch=0) == B.PA_OK                # empty batch: a no-op, no launch

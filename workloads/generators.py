@@ -342,6 +342,8 @@ class MQCase:
     q: np.ndarray                # [n_q][H][dh] storage, shared by every sample
     scale: float
     seed: int = 0
+    token_bins: list | None = None  # per sample: the time bin of each token, in token order
+    n_bins: int = 0                 # time bins of the window
 
     @property
     def batch(self) -> int:
@@ -388,6 +390,7 @@ def mq(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 13
     k_pool = np.full(shape, POISON_BF16, dtype=np.uint16)
     v_pool = np.full(shape, POISON_BF16, dtype=np.uint16)
     off = 0
+    token_bins = []
     for b in range(batch):
         bt[b, : nblk[b]] = perm[off: off + nblk[b]]
         off += nblk[b]
@@ -396,6 +399,7 @@ def mq(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 13
         reps = c[bins, neurons]
         bins = np.repeat(bins, reps)
         neurons = np.repeat(neurons, reps)
+        token_bins.append(bins.astype(np.int32))
         vals = np.minimum(np.repeat(reps, reps), 4)
         x = n_emb[neurons] + t_emb[bins] + v_emb[vals - 1]
         kk = to_storage((kv_gain * (x @ w_k)).reshape(-1, num_heads, dh), dtype)
@@ -406,4 +410,5 @@ def mq(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 13
         v_pool[blk, :, t % BLOCK_SIZE, :] = vv
     return MQCase(name="mq", dtype=dtype, num_heads=num_heads, head_dim=dh, n_q=n_latents,
                   num_blocks=num_blocks, poison_block=poison, kv_lens=kv_lens, block_tables=bt,
-                  k_pool=k_pool, v_pool=v_pool, q=q, scale=fp32_scale(dh), seed=seed)
+                  k_pool=k_pool, v_pool=v_pool, q=q, scale=fp32_scale(dh), seed=seed,
+                  token_bins=token_bins, n_bins=n_bins)
