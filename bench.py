@@ -36,10 +36,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="b128", choices=["b128", "long", "mq", "b16"],
+    p.add_argument("--workload", default="b128", choices=["b128", "long", "mq", "mq-sparse", "b16"],
                    help="b128 is the reported workload; long (B=4 long-context split-K), mq "
-                        "(latent cross-attention on the matrix cores) and b16 (the B=16 "
-                        "lockstep step, paged and right-padded) measure the other paths")
+                        "(latent cross-attention on the matrix cores; mq-sparse under the "
+                        "temporal block mask) and b16 (the B=16 lockstep step, paged and "
+                        "right-padded) measure the other paths")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="cache-flush write between the extra flushed decode timings")
@@ -83,16 +84,22 @@ def blas_threads() -> int:
     return int(max(blas)) if blas else 1
 
 
-def cpu_baseline_mq(case, flops: float, budget_s: float = 10.0, max_reps: int = 3):
-    """The oracle on the full multi-query workload (all rows, shared latent queries)."""
+def cpu_baseline_mq(case, flops: float, keep=None, budget_s: float = 10.0, max_reps: int = 3):
+    """The oracle on the full multi-query workload (all rows, shared latent queries); with
+    ``keep``, its block-sparse form under that mask."""
     import oracle as O
 
     times = []
     t_start = time.perf_counter()
     while len(times) < max_reps and (time.perf_counter() - t_start) < budget_s:
         t0 = time.perf_counter()
-        O.decode_paged(case.k_pool, case.v_pool, case.dtype, case.block_tables, case.kv_lens,
-                       case.q, case.scale, shared_q=True)
+        if keep is None:
+            O.decode_paged(case.k_pool, case.v_pool, case.dtype, case.block_tables, case.kv_lens,
+                           case.q, case.scale, shared_q=True)
+        else:
+            O.decode_paged_block_sparse(case.k_pool, case.v_pool, case.dtype, case.block_tables,
+                                        case.kv_lens, case.q, case.scale, keep.astype(bool),
+                                        shared_q=True)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     cores = blas_threads()
@@ -130,22 +137,50 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix-core peak
 
 def main_mq(args):
     """Latent cross-attention on the matrix cores: 16 rows x 256 shared latent queries over ragged
-    spike-token keys (8 heads of 32), one pa_decode_attention call per step."""
+    spike-token keys (8 heads of 32), one pa_decode_attention call per step. mq-sparse runs
+    pa_decode_attention_block_sparse under the temporal-overlap block mask instead; its FLOP count
+    is that of the kept (query, key) pairs."""
+    import numpy as np
     import torch
 
     import workloads as W
+    from paged_kv_cache_177_amd import binding as B
+    from paged_kv_cache_177_amd.masks import temporal_block_mask
     from paged_kv_cache_177_amd.runner import MultiQueryStep
 
     torch.cuda.set_device(0)
     case = W.mq()
     r = MultiQueryStep(case, device="cuda:0")
     stream = torch.cuda.current_stream()
+    sparse = args.workload == "mq-sparse"
     flops = 4.0 * case.n_q * float(case.kv_lens.sum()) * case.num_heads * case.head_dim
+    kept_frac = 1.0
+    if sparse:
+        keep = temporal_block_mask(case.token_bins, case.n_q, case.n_bins, halo=1)
+        # kept (query, key) pairs: per row, per query block, the valid keys of its kept blocks
+        pairs = 0
+        for b in range(case.batch):
+            n = int(case.kv_lens[b])
+            per_block = np.minimum(16, n - 16 * np.arange(keep.shape[2])).clip(0)
+            for qb in range(keep.shape[1]):
+                nq = min(16, case.n_q - 16 * qb)
+                pairs += nq * int((keep[b, qb] * per_block).sum())
+        kept_frac = pairs / (case.n_q * float(case.kv_lens.sum()))
+        flops = 4.0 * pairs * case.num_heads * case.head_dim
+        mask_dev = torch.from_numpy(keep).to("cuda:0")
+
+        def call():
+            B.pa_decode_attention_block_sparse(r.kv.pool, r.q, 0, case.n_q, case.num_heads,
+                                               r.block_tables, r.bt_stride, r.kv_lens, r.batch,
+                                               r.max_kv_len, case.scale, mask_dev, keep.shape[2],
+                                               out=r.out, lse=r.lse)
+    else:
+        call = r.decode
     t_w = time.perf_counter()
     done = 0
     while done < args.warmup or time.perf_counter() - t_w < 1.0:
         for _ in range(10):
-            r.decode()
+            call()
         done += 10
         torch.cuda.synchronize()
     # back-to-back calls between one pair of events: the average is the kernel's launch duration
@@ -155,7 +190,7 @@ def main_mq(args):
     t0 = time.perf_counter()
     a.record(stream)
     for _ in range(args.steps):
-        r.decode()
+        call()
     b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -163,7 +198,8 @@ def main_mq(args):
     avg_ms = a.elapsed_time(b) / args.steps
     achieved = flops / (avg_ms * 1e-3) / 1e12
     out = {
-        "metric": "multi-query latent cross-attention TFLOP/s + us/call, 16 x 256 queries, bf16",
+        "metric": ("multi-query latent cross-attention TFLOP/s + us/call, 16 x 256 queries, bf16"
+                   + (", block-sparse (temporal mask; kept pairs)" if sparse else "")),
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -181,16 +217,19 @@ def main_mq(args):
                                 f"(sum {int(case.kv_lens.sum())}), 16-token blocks, seed "
                                 f"{case.seed}"),
                    "global_batch": len(case.kv_lens), "flops_per_step": flops,
-                   "step": "one multi-query pa_decode_attention call"},
+                   "step": ("one pa_decode_attention_block_sparse call" if sparse else
+                            "one multi-query pa_decode_attention call"),
+                   "kept_pair_fraction": round(kept_frac, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "mq_paged_mfma_kernel", "flops_per_launch": flops,
+                     "kernel": "mq_paged_mfma_kernel<32, " + ("true>" if sparse else "false>"),
+                     "flops_per_launch": flops,
                      "avg_launch_us": round(avg_ms * 1e3, 2)},
         "detail": {"us_per_call": round(avg_ms * 1e3, 2), "source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_mq(case, flops)
+        out["cpu_baseline"] = cpu_baseline_mq(case, flops, keep=keep if sparse else None)
     print(json.dumps(out), flush=True)
 
 
@@ -300,7 +339,7 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "mq":
+    if args.workload in ("mq", "mq-sparse"):
         main_mq(args)
         return
     if args.workload == "b16":
