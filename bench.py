@@ -233,11 +233,76 @@ def main_mq(args):
     print(json.dumps(out), flush=True)
 
 
+def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64):
+    """The paged B=16 step captured as a graph (append + decode + merge + on-device advance) and
+    replayed. Block tables are filled for ``ahead`` positions past each row's start; positions are
+    reset (outside the timed replays) every ``reset_every`` warm-up replays."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_177_amd import binding as B
+    from paged_kv_cache_177_amd.runner import PagedLockstepGraph, to_torch
+
+    assert args.steps <= reset_every <= ahead
+    n0 = plan.n_ctx0.astype(np.int32)
+    case = W.make_paged_case("b16-graph", plan.seed, n0, plan.num_q_heads, plan.num_kv_heads,
+                             plan.head_dim, plan.dtype, rope_theta=plan.rope_theta,
+                             rope_max_pos=int(n0.max()) + ahead + 2,
+                             pool_factor=1.5, bt_stride=(int(n0.max()) + ahead + 16) // 16)
+    # extend every row's table with free blocks for the positions ahead
+    bt = case.block_tables.copy()
+    used = set(int(x) for x in bt.ravel())
+    free = [i for i in range(case.num_blocks) if i not in used]
+    for b in range(case.batch):
+        have = int((case.kv_lens[b] + 15) // 16)
+        need = (int(n0[b]) + ahead + 16) // 16
+        for j in range(have, need):
+            bt[b, j] = free.pop()
+    desc = B.make_desc("paged", case.dtype, case.num_kv_heads, case.head_dim,
+                       num_blocks=case.num_blocks, rope_max_pos=case.rope_max_pos,
+                       rope_theta=case.rope_theta)
+    pool = B.alloc_pool(desc, device="cuda:0")
+    pool.k.copy_(to_torch(case.k_pool, case.dtype))
+    pool.v.copy_(to_torch(case.v_pool, case.dtype))
+    start = torch.from_numpy(n0.copy()).to("cuda:0")
+    g = PagedLockstepGraph(pool, torch.from_numpy(bt).to("cuda:0"), start.clone(),
+                           case.num_q_heads, int(n0.max()) + ahead + 1, case.scale,
+                           device="cuda:0")
+    g.k_new.copy_(to_torch(case.k_new, case.dtype))
+    g.v_new.copy_(to_torch(case.v_new, case.dtype))
+    g.q_in.copy_(to_torch(case.q, case.dtype))
+
+    def reset():
+        g.positions.copy_(start)
+        g.kv_lens.copy_(start + 1)
+
+    g.step()
+    reset()
+    torch.cuda.synchronize()
+    g.capture()
+    count = [0]
+
+    def replay():
+        if count[0] == reset_every:
+            reset()
+            count[0] = 0
+        g.replay()
+        count[0] += 1
+
+    # timed() warms up (with resets), then times args.steps replays from a fresh reset
+    def timed_from_reset(fn):
+        return timed(fn, before_timed=lambda: (reset(), count.__setitem__(0, 0)))
+
+    return timed_from_reset(replay)
+
+
 def main_b16(args):
     """The B=16 lockstep step at the protocol's starting geometry (contexts of seed 1, 32/8 heads,
     D=64, bf16, RoPE theta 1e6): append_kv (keys, values and query rotation) + decode + merge, in
-    the paged form and in the right-padded form. A step moves ~36 MB and is launch-bound, so the
-    line reports microseconds per step, timed over back-to-back steps between one pair of events."""
+    the paged form and in the right-padded form, and the paged step replayed from a graph (with the
+    on-device advance). A step moves ~36 MB and is launch-bound, so the line reports microseconds
+    per step, timed over back-to-back steps between one pair of events."""
     import numpy as np
     import torch
 
@@ -278,7 +343,7 @@ def main_b16(args):
                                      pc.kv_cols, pc.scale, workspace=ws if need else None,
                                      out=out, lse=lse)
 
-    def timed(fn):
+    def timed(fn, before_timed=None):
         t_w = time.perf_counter()
         done = 0
         while done < args.warmup or time.perf_counter() - t_w < 1.0:
@@ -286,6 +351,8 @@ def main_b16(args):
                 fn()
             done += 10
             torch.cuda.synchronize()
+        if before_timed is not None:
+            before_timed()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -298,6 +365,7 @@ def main_b16(args):
 
     wall_paged, ev_paged = timed(paged.step)
     wall_padded, ev_padded = timed(padded_step)
+    wall_graph, ev_graph = graph_step_timing(args, plan, timed)
     out_line = {
         "metric": "B=16 lockstep decode step us (append + decode + merge), paged, bf16",
         "value": round(ev_paged, 2),
@@ -326,6 +394,8 @@ def main_b16(args):
                    "paged_us_per_step_wall": round(wall_paged, 2),
                    "padded_us_per_step_events": round(ev_padded, 2),
                    "padded_us_per_step_wall": round(wall_padded, 2),
+                   "graph_us_per_step_events": round(ev_graph, 2),
+                   "graph_us_per_step_wall": round(wall_graph, 2),
                    "source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:

@@ -149,6 +149,18 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
                               size_t workspace_bytes, size_t* workspace_needed /* host */,
                               float* out, float* lse, hipStream_t stream);
 
+/* Advance a lockstep batch by one token, on the device ("NeuroGrid releases", v0.8.0: the whole
+ * decode step replayed as a graph, with position and kv_len read from device buffers and an
+ * add-one kernel computing kv_len = position + 1 on the GPU).
+ *
+ * For b < batch: positions[b] += 1; then, when kv_lens != NULL, kv_lens[b] = positions[b] + 1;
+ * when dest != NULL, dest[b] += 1 (all int32, device). With it a captured step (append at the
+ * positions, decode over kv_lens, advance) replays with no host work between tokens; the caller
+ * keeps the block tables filled for the positions ahead. Positions must stay below 2^31 - 2.
+ * Errors: PA_ERR_NULL (positions); PA_ERR_SHAPE (batch < 0). batch == 0 is a no-op. */
+pa_status pa_advance_lockstep(int32_t* positions, int32_t* kv_lens, int32_t* dest, int32_t batch,
+                              hipStream_t stream);
+
 /* Block-sparse multi-query decode attention over the paged cache ("cortex-engine write-up",
  * kernels section, block-sparse cross-attention: a boolean tile mask computed outside the kernel;
  * tiles whose mask is false are skipped; a query left with no key gives zeros, not NaN).

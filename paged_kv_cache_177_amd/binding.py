@@ -23,7 +23,7 @@ PA_F32, PA_BF16 = 0, 1
 PA_PAGED, PA_PADDED = 0, 1
 
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
-           "pa_decode_attention_block_sparse")
+           "pa_decode_attention_block_sparse", "pa_advance_lockstep")
 
 
 class PaError(RuntimeError):
@@ -74,6 +74,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_attention_block_sparse.argtypes = [ctypes.POINTER(Pool), _P, ctypes.c_int64,
                                                      _I32, _I32, _P, _I32, _P, _I32, _I32,
                                                      ctypes.c_float, _P, _I32, _P, _P, _P]
+    lib.pa_advance_lockstep.argtypes = [_P, _P, _P, _I32, _P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -165,6 +166,15 @@ def pa_decode_attention_block_sparse(pool: Pool, q, q_row_stride: int, n_q: int,
                                               mask_kv_blocks, _ptr(out), _ptr(lse),
                                               _stream(stream))
     _check("pa_decode_attention_block_sparse", st)
+
+
+def pa_advance_lockstep(positions, kv_lens=None, dest=None, batch: int | None = None,
+                        stream=None) -> None:
+    """Enqueue positions += 1, kv_lens = positions + 1, dest += 1 (int32 device tensors)."""
+    lib = load_library()
+    n = positions.shape[0] if batch is None else batch
+    st = lib.pa_advance_lockstep(_ptr(positions), _ptr(kv_lens), _ptr(dest), n, _stream(stream))
+    _check("pa_advance_lockstep", st)
 
 
 def pa_decode_attention_padded(pool: Pool, q, num_q_heads: int, batch: int, gap_start, gap_end,

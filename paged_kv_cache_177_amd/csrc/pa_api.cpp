@@ -226,6 +226,14 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   return map_hip(e);
 }
 
+extern "C" pa_status pa_advance_lockstep(int32_t* positions, int32_t* kv_lens, int32_t* dest,
+                                         int32_t batch, hipStream_t stream) {
+  if (positions == nullptr) return PA_ERR_NULL;
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  return map_hip(pa::launch_advance(positions, kv_lens, dest, batch, stream));
+}
+
 extern "C" pa_status pa_decode_attention_block_sparse(
     const pa_pool* pool, const void* q, int64_t q_row_stride, int32_t n_q, int32_t num_q_heads,
     const int32_t* block_tables, int32_t bt_stride, const int32_t* kv_lens, int32_t batch,

@@ -116,7 +116,26 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int log
   }
 }
 
+// Advance a lockstep batch by one token: position += 1, kv_len = position + 1, dest += 1
+// (unsigned arithmetic: a position at the int32 limit wraps instead of overflowing).
+__global__ __launch_bounds__(256) void advance_kernel(int32_t* positions, int32_t* kv_lens,
+                                                      int32_t* dest, int batch) {
+  const int b = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (b >= batch) return;
+  const uint32_t p = (uint32_t)positions[b] + 1u;
+  positions[b] = (int32_t)p;
+  if (kv_lens != nullptr) kv_lens[b] = (int32_t)(p + 1u);
+  if (dest != nullptr) dest[b] = (int32_t)((uint32_t)dest[b] + 1u);
+}
+
 }  // namespace
+
+hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(advance_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream,
+                     positions, kv_lens, dest, batch);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int heads = 2 * a.H_kv + (a.q_in != nullptr ? a.H_q : 0);

@@ -103,6 +103,8 @@ inline void carve_workspace(void* ws, int batch, int n_q, int H_q, int D, int s_
 
 // ---- launchers (each returns the hipGetLastError of its launches) -----------------------------
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
+                          hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream);      // n_q > 1
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);

@@ -161,3 +161,66 @@ class PaddedLockstep:
                                      scale, workspace=self._ws if need > 0 else None, out=out,
                                      lse=lse, stream=self.stream)
         return out, lse
+
+
+class PagedLockstepGraph:
+    """One paged lockstep decode step -- append at the rows' positions, decode over kv_lens (+ the
+    log-sum-exp merge), then pa_advance_lockstep (position += 1, kv_len = position + 1) --
+    recorded once as a HIP graph and replayed per token ("NeuroGrid releases", v0.8.0: the decode
+    step replayed as a graph, lengths and positions in device buffers).
+
+    The caller writes each token's keys, values and queries into ``k_new``, ``v_new`` and ``q_in``
+    (in place) and keeps ``block_tables`` filled for the positions ahead; ``max_kv_len`` is the
+    host bound for every replay (it sizes the launch and the workspace). Run ``step()`` once
+    before ``capture()`` so that every kernel has been loaded."""
+
+    def __init__(self, pool, block_tables, positions, num_q_heads: int, max_kv_len: int,
+                 scale: float, device: str = "cuda"):
+        d = pool.pool.desc
+        self.pool = pool
+        self.H_q, self.H_kv, self.D = num_q_heads, d.num_kv_heads, d.head_dim
+        self.dtype = "bf16" if d.dtype == B.PA_BF16 else "f32"
+        tdt = torch.bfloat16 if d.dtype == B.PA_BF16 else torch.float32
+        self.batch = int(positions.shape[0])
+        self.block_tables = block_tables
+        self.bt_stride = int(block_tables.shape[1])
+        self.positions = positions
+        self.kv_lens = (positions + 1).to(torch.int32)
+        self.max_kv_len = int(max_kv_len)
+        self.scale = float(scale)
+        self.k_new = torch.zeros((self.batch, self.H_kv, self.D), dtype=tdt, device=device)
+        self.v_new = torch.zeros_like(self.k_new)
+        self.q_in = torch.zeros((self.batch, self.H_q, self.D), dtype=tdt, device=device)
+        self.q_out = torch.zeros_like(self.q_in)
+        self.out = torch.zeros((self.batch, self.H_q, self.D), dtype=torch.float32, device=device)
+        self.lse = torch.zeros((self.batch, self.H_q), dtype=torch.float32, device=device)
+        need = B.pa_decode_attention(pool.pool, self.q_out, self.H_q * self.D, 1, self.H_q,
+                                     block_tables, self.bt_stride, self.kv_lens, self.batch,
+                                     self.max_kv_len, self.scale, out=self.out,
+                                     query_workspace=True)
+        # zero-filled before first use (the work counter); every step leaves it at zero again
+        self.workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+        self._need = need
+        self.graph = None
+
+    def step(self):
+        rope = self.pool.pool.desc.rope_max_pos > 0
+        B.pa_append_kv(self.pool.pool, self.block_tables, self.bt_stride, self.positions, None,
+                       self.k_new, self.v_new, self.q_in if rope else None,
+                       self.q_out if rope else None, self.H_q if rope else 0, self.batch)
+        q = self.q_out if rope else self.q_in
+        B.pa_decode_attention(self.pool.pool, q, self.H_q * self.D, 1, self.H_q,
+                              self.block_tables, self.bt_stride, self.kv_lens, self.batch,
+                              self.max_kv_len, self.scale,
+                              workspace=self.workspace if self._need else None, out=self.out,
+                              lse=self.lse)
+        B.pa_advance_lockstep(self.positions, self.kv_lens, None, self.batch)
+
+    def capture(self):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        self.graph = g
+
+    def replay(self):
+        self.graph.replay()

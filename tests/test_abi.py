@@ -258,3 +258,10 @@ def test_block_sparse_argument_errors():
     assert call(batch=65536) == B.PA_ERR_SHAPE
     assert call(pool=_fake_pool(dtype="f32")) == B.PA_ERR_UNSUPPORTED
     assert call(batch=0) == B.PA_OK                # empty batch: a no-op, no launch
+
+
+def test_advance_lockstep_argument_errors():
+    lib = B.load_library()
+    assert lib.pa_advance_lockstep(None, None, None, 4, None) == B.PA_ERR_NULL
+    assert lib.pa_advance_lockstep(FAKE, None, None, -1, None) == B.PA_ERR_SHAPE
+    assert lib.pa_advance_lockstep(FAKE, None, None, 0, None) == B.PA_OK  # no launch

@@ -207,3 +207,93 @@ def test_b16_lockstep_protocol():
             np.testing.assert_array_equal(to_numpy(L.kv.v, "bf16"), vpad)
         log(f"[lockstep] step {s} ok max_err={mx:.2e} mean_err={mean:.2e} "
             f"free_blocks={P.alloc.num_free}")
+
+
+def test_b16_graph_replay_matches_eager():
+    """The paged B=16 step captured as a graph (append + decode + merge + on-device advance) and
+    replayed 24 times: each replay gives the eager step's bits, the pools end identical, and the
+    last step matches the oracle. Between replays the inputs are written in place and other eager
+    work runs, as in a serving loop."""
+    from paged_kv_cache_177_amd.runner import PagedLockstepGraph
+
+    plan = W.b16_plan()
+    steps = 24
+    H_q, H, D, scale = plan.num_q_heads, plan.num_kv_heads, plan.head_dim, plan.scale
+    P = PagedSide(plan)
+    n0 = plan.n_ctx0.astype(np.int32)
+    for sid in range(16):
+        P.seq[sid].ensure_token(int(n0[sid]) + steps - 1, P.alloc)
+    bt = block_table_array([P.seq[sid] for sid in range(16)], P.stride, P.poison)
+    max_len = int(n0.max()) + steps
+    ins = [[plan.step_inputs(sid, s) for sid in range(16)] for s in range(steps)]
+
+    def make(pool):
+        return PagedLockstepGraph(pool, torch.from_numpy(bt).cuda(),
+                                  torch.from_numpy(n0.copy()).cuda(), H_q, max_len, scale)
+
+    def load_inputs(r, s):
+        r.q_in.copy_(to_torch(_stack([x[0] for x in ins[s]]), "bf16"))
+        r.k_new.copy_(to_torch(_stack([x[1] for x in ins[s]]), "bf16"))
+        r.v_new.copy_(to_torch(_stack([x[2] for x in ins[s]]), "bf16"))
+
+    # eager reference on the side's own pool
+    eager = make(P.dev)
+    ref = []
+    for s in range(steps):
+        load_inputs(eager, s)
+        eager.step()
+        torch.cuda.synchronize()
+        ref.append((eager.out.clone(), eager.lse.clone()))
+
+    # graph run on a fresh copy of the initial pool
+    desc = B.make_desc("paged", "bf16", H, D, num_blocks=plan.num_blocks,
+                       rope_max_pos=plan.rope_max_pos, rope_theta=plan.rope_theta)
+    pool2 = B.alloc_pool(desc)
+    pool2.k.copy_(to_torch(P.k, "bf16"))
+    pool2.v.copy_(to_torch(P.v, "bf16"))
+    g = make(pool2)
+    g.capture()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for s in range(steps):
+        load_inputs(g, s)
+        g.replay()
+        scratch.add_(1.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(g.out, ref[s][0]), f"replay {s} out"
+        assert torch.equal(g.lse, ref[s][1]), f"replay {s} lse"
+    log(f"[graph] {steps} replays match the eager steps bit for bit")
+    # bit patterns (the pools hold NaN poison, which never compares equal as a value)
+    assert torch.equal(pool2.k.view(torch.int16), P.dev.k.view(torch.int16))
+    assert torch.equal(pool2.v.view(torch.int16), P.dev.v.view(torch.int16))
+    np.testing.assert_array_equal(g.positions.cpu().numpy(), n0 + steps)
+    np.testing.assert_array_equal(g.kv_lens.cpu().numpy(), n0 + steps + 1)
+
+    # the oracle, replaying the same appends on its own pool, at the last step
+    cos, sin = O.rope_tables(plan.rope_theta, plan.head_dim, plan.rope_max_pos)
+    k_h, v_h = P.k, P.v
+    for s in range(steps):
+        pos = n0 + s
+        q = _stack([x[0] for x in ins[s]])
+        k_h, v_h, q2 = O.append_kv(k_h, v_h, "bf16", "paged", bt, pos, pos,
+                                   _stack([x[1] for x in ins[s]]), _stack([x[2] for x in ins[s]]),
+                                   cos, sin, q_in=q)
+    o_ref, l_ref = O.decode_paged(k_h, v_h, "bf16", bt, n0 + steps, q2, scale)
+    assert_attention_close(g.out.cpu().numpy(), o_ref[:, 0], "bf16", "graph last step")
+    assert_attention_close(g.lse.cpu().numpy(), l_ref[:, 0], "bf16", "graph last step lse")
+    np.testing.assert_array_equal(to_numpy(pool2.k, "bf16"), k_h)
+    np.testing.assert_array_equal(to_numpy(pool2.v, "bf16"), v_h)
+
+
+def test_advance_lockstep_closed_form():
+    """position += 1, kv_len = position + 1, dest += 1, for each row; rows past batch untouched."""
+    pos = torch.tensor([0, 5, 17, 2047, 99, 7], dtype=torch.int32, device="cuda")
+    kv = torch.full((6,), -1, dtype=torch.int32, device="cuda")
+    dest = torch.tensor([10, 20, 30, 40, 50, 60], dtype=torch.int32, device="cuda")
+    B.pa_advance_lockstep(pos, kv, dest, batch=5)
+    torch.cuda.synchronize()
+    assert pos.tolist() == [1, 6, 18, 2048, 100, 7]
+    assert kv.tolist() == [2, 7, 19, 2049, 101, -1]
+    assert dest.tolist() == [11, 21, 31, 41, 51, 60]
+    B.pa_advance_lockstep(pos, None, None)  # positions only
+    torch.cuda.synchronize()
+    assert pos.tolist() == [2, 7, 19, 2049, 101, 8]
