@@ -14,6 +14,7 @@ from .reference import (  # noqa: F401
     f32_to_storage,
     rope_tables,
     rope_rotate_f32,
+    rms_norm_head_f32,
     append_kv,
     gather_paged,
     gather_padded_columns,

@@ -124,18 +124,47 @@ def rope_rotate_f32(x32: np.ndarray, c32: np.ndarray, s32: np.ndarray) -> np.nda
 
 
 # --------------------------------------------------------------------------------------------
+# Per-head QK RMSNorm [NG-0.7 LFM2]
+# --------------------------------------------------------------------------------------------
+def rms_norm_head_f32(x32: np.ndarray, w32: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head RMSNorm on a query or key head before RoPE [NG-0.7 LFM2]: y = x * r * w with
+    r = 1 / sqrt(mean(x^2) + eps), in fp32.
+
+    The pages fix no arithmetic; the reading taken (the library's contract, chosen so that results
+    reproduce bit for bit): every product, sum, quotient and square root is a separate correctly
+    rounded fp32 operation, y_i = (x_i * r) * w_i, mean = ss / D, and the sum of squares ss runs
+    over the rotate-half pairs first, s_i = x_i * x_i + x_{i+D/2} * x_{i+D/2} (i < D/2), then a
+    pairwise tree over i that adds neighbours at every level: (s_0 + s_1), (s_2 + s_3), ..., then
+    those sums in pairs, and so on. x32 (..., D); w32 (D,); eps a float (rounded to fp32)."""
+    x = np.asarray(x32, dtype=np.float32)
+    w = np.asarray(w32, dtype=np.float32)
+    D = x.shape[-1]
+    half = D // 2
+    s = np.add(np.multiply(x[..., :half], x[..., :half]), np.multiply(x[..., half:], x[..., half:]))
+    while s.shape[-1] > 1:
+        s = np.add(s[..., 0::2], s[..., 1::2])
+    ss = s[..., 0]
+    ms = np.divide(ss, np.float32(D))
+    r = np.divide(np.float32(1.0), np.sqrt(np.add(ms, np.float32(eps))))
+    return np.multiply(np.multiply(x, r[..., None]), w).astype(np.float32)
+
+
+# --------------------------------------------------------------------------------------------
 # append_kv [HX-1], [NG-0.7]
 # --------------------------------------------------------------------------------------------
 def append_kv(k_pool, v_pool, dtype, layout, block_tables, positions, dest, k_new, v_new,
-              cos=None, sin=None, q_in=None):
+              cos=None, sin=None, q_in=None, q_norm_w=None, k_norm_w=None, norm_eps=None):
     """One new token per row, written into copies of the pools.
 
     Row b's key is rotated at its logical position ``positions[b]`` (when tables are given), rounded
     to the storage dtype and stored with its value at token index ``dest[b]``: slot
     (block_tables[b][dest // 16], dest % 16) for the paged layout, column ``dest`` for the padded
     one. The value is stored unchanged. ``q_in`` (if given) is rotated at the same positions.
-    Returns (k_pool', v_pool', q_out or None).
+    With ``k_norm_w``/``q_norm_w`` (fp32 (D,)) and ``norm_eps``, every key head (and query head) is
+    RMS-normalised first (``rms_norm_head_f32``), then rotated [NG-0.7 LFM2: per-head RMSNorm on
+    Q/K before RoPE]. Returns (k_pool', v_pool', q_out or None).
     """
+    norm = k_norm_w is not None
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     B = len(positions)
@@ -147,9 +176,13 @@ def append_kv(k_pool, v_pool, dtype, layout, block_tables, positions, dest, k_ne
         p = int(positions[b])
         t = int(dest[b])
         kb = np.asarray(k_new[b])
-        if rope:
+        if rope or norm:
             x = storage_to_f64(kb, dtype).astype(np.float32)  # exact widening
-            kb = f32_to_storage(rope_rotate_f32(x, cos[p][None, :], sin[p][None, :]), dtype)
+            if norm:
+                x = rms_norm_head_f32(x, k_norm_w, norm_eps)
+            if rope:
+                x = rope_rotate_f32(x, cos[p][None, :], sin[p][None, :])
+            kb = f32_to_storage(x, dtype)
         if layout == "paged":
             blk = int(block_tables[b][t // BLOCK])
             k_out[blk, :, t % BLOCK, :] = kb
@@ -159,9 +192,13 @@ def append_kv(k_pool, v_pool, dtype, layout, block_tables, positions, dest, k_ne
             v_out[b, :, t, :] = v_new[b]
         else:
             raise ValueError(layout)
-        if q_in is not None and rope:
+        if q_in is not None and (rope or norm):
             xq = storage_to_f64(np.asarray(q_in[b]), dtype).astype(np.float32)
-            q_out[b] = f32_to_storage(rope_rotate_f32(xq, cos[p][None, :], sin[p][None, :]), dtype)
+            if norm:
+                xq = rms_norm_head_f32(xq, q_norm_w, norm_eps)
+            if rope:
+                xq = rope_rotate_f32(xq, cos[p][None, :], sin[p][None, :])
+            q_out[b] = f32_to_storage(xq, dtype)
     return k_out, v_out, q_out
 
 

@@ -542,3 +542,81 @@ def test_block_sparse_batched_equals_per_row():
         o, l = O.attend_block_sparse(O.storage_to_f64(q, "bf16"), K, V, c.scale, keep[b])
         np.testing.assert_array_equal(out[b], o)
         np.testing.assert_array_equal(lse[b], l)
+
+
+# ---------------------------------------------------------------------------------------------
+# Per-head QK RMSNorm (before RoPE)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_rms_norm_close_to_fp64_and_torch(D):
+    """Within a few fp32 ulp of the fp64 formula, and of torch's CPU rms_norm (a library routine
+    with its own reduction order)."""
+    rng = _rng(600 + D)
+    x = (rng.standard_normal((40, 4, D)) * rng.uniform(0.01, 30, (40, 4, 1))).astype(np.float32)
+    w = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    eps = 1e-5
+    y = O.rms_norm_head_f32(x, w, eps)
+    x64 = x.astype(np.float64)
+    y64 = x64 / np.sqrt((x64 ** 2).mean(axis=-1, keepdims=True) + np.float64(np.float32(eps))) \
+        * w.astype(np.float64)
+    ulp = np.spacing(np.abs(y64).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(y - y64) <= 4 * ulp)
+    yt = torch.nn.functional.rms_norm(torch.from_numpy(x), (D,), torch.from_numpy(w), eps).numpy()
+    assert np.all(np.abs(y - yt) <= 4 * ulp)
+    # the RMS of the output (with unit weights) is 1 up to eps
+    y1 = O.rms_norm_head_f32(x, np.ones(D, np.float32), 0.0)
+    np.testing.assert_allclose(np.sqrt((y1.astype(np.float64) ** 2).mean(axis=-1)), 1.0,
+                               rtol=1e-6)
+
+
+def test_rms_norm_closed_forms():
+    D = 64
+    w = np.ones(D, np.float32)
+    # a constant head c = +-2^k normalises to +-1 exactly (eps = 0)
+    for c in [1.0, -4.0, 0.25, 1024.0]:
+        y = O.rms_norm_head_f32(np.full(D, c, np.float32), w, 0.0)
+        np.testing.assert_array_equal(y, np.full(D, np.sign(c), np.float32))
+    # scaling the input by a power of two leaves the output unchanged bit for bit (eps = 0)
+    rng = _rng(610)
+    x = rng.standard_normal((10, D)).astype(np.float32)
+    wr = rng.uniform(0.5, 2, D).astype(np.float32)
+    np.testing.assert_array_equal(O.rms_norm_head_f32(x * np.float32(8.0), wr, 0.0),
+                                  O.rms_norm_head_f32(x, wr, 0.0))
+    # the weight multiplies each element: weight 2^k scales the output by 2^k exactly
+    np.testing.assert_array_equal(O.rms_norm_head_f32(x, wr * np.float32(4.0), 1e-5),
+                                  O.rms_norm_head_f32(x, wr, 1e-5) * np.float32(4.0))
+    # a zero head gives zeros (eps > 0), never NaN
+    assert np.all(O.rms_norm_head_f32(np.zeros(D, np.float32), wr, 1e-6) == 0)
+
+
+def test_append_with_qk_norm_normalises_then_rotates():
+    """The stored key is RoPE(RMSNorm(k)), the query the same with its own weight; the value is
+    untouched; without tables the key is only normalised."""
+    c = W.make_paged_case("qkn", 620, [5, 17, 33], 4, 2, 64, "bf16", rope_theta=1e4)
+    rng = _rng(621)
+    wq = rng.uniform(0.5, 2, 64).astype(np.float32)
+    wk = rng.uniform(0.5, 2, 64).astype(np.float32)
+    cos, sin = O.rope_tables(1e4, 64, c.rope_max_pos)
+    k2, v2, q2 = O.append_kv(c.k_pool, c.v_pool, "bf16", "paged", c.block_tables, c.positions,
+                             c.dest, c.k_new, c.v_new, cos, sin, q_in=c.q, q_norm_w=wq,
+                             k_norm_w=wk, norm_eps=1e-5)
+    for b in range(3):
+        t = int(c.dest[b])
+        blk = c.block_tables[b][t // 16]
+        xk = O.storage_to_f64(c.k_new[b], "bf16").astype(np.float32)
+        p = int(c.positions[b])
+        want = O.f32_to_storage(O.rope_rotate_f32(O.rms_norm_head_f32(xk, wk, 1e-5),
+                                                  cos[p][None], sin[p][None]), "bf16")
+        np.testing.assert_array_equal(k2[blk, :, t % 16, :], want)
+        np.testing.assert_array_equal(v2[blk, :, t % 16, :], c.v_new[b])
+        xq = O.storage_to_f64(c.q[b], "bf16").astype(np.float32)
+        np.testing.assert_array_equal(
+            q2[b], O.f32_to_storage(O.rope_rotate_f32(O.rms_norm_head_f32(xq, wq, 1e-5),
+                                                      cos[p][None], sin[p][None]), "bf16"))
+    # normalised keys have RMS ~ |w| before rounding: with unit weights, RMS 1 within bf16
+    k3, _, _ = O.append_kv(c.k_pool, c.v_pool, "bf16", "paged", c.block_tables, c.positions,
+                           c.dest, c.k_new, c.v_new, k_norm_w=np.ones(64, np.float32),
+                           norm_eps=0.0)
+    t = int(c.dest[0])
+    kk = O.storage_to_f64(k3[c.block_tables[0][t // 16], :, t % 16, :], "bf16")
+    np.testing.assert_allclose(np.sqrt((kk ** 2).mean(axis=-1)), 1.0, rtol=1e-2)
