@@ -117,6 +117,26 @@ pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t
                        const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
                        int32_t batch, hipStream_t stream);
 
+/* Append one token per row, with per-head RMSNorm of the new key (and query) before RoPE
+ * ("NeuroGrid releases", v0.7.0 LFM2 notes: QK LayerNorm, per-head RMSNorm on Q/K before RoPE).
+ *
+ * As pa_append_kv, except that every key head x (D elements, fp32 from the pool dtype) -- and every
+ * query head when q_in is given -- is first replaced by y_i = (x_i * r) * w_i with
+ * r = 1 / sqrt(ss / D + eps), w = k_norm_weight (queries: q_norm_weight), fp32 [D] device arrays.
+ * Every operation is a separate correctly rounded fp32 operation, and the sum of squares ss is
+ * formed over the rotate-half pairs first, s_i = x_i*x_i + x_{i+D/2}*x_{i+D/2} (i < D/2), then as a
+ * pairwise tree of neighbours ((s_0 + s_1), (s_2 + s_3), ..., then those in pairs, ...), so the
+ * stored bits are reproducible. The result is then rotated as in pa_append_kv (or, on a pool
+ * without RoPE tables, stored as is). Values are not normalised.
+ * Errors: as pa_append_kv; PA_ERR_NULL also for k_norm_weight, or q_norm_weight when q_in is
+ * given; PA_ERR_SHAPE for eps negative or not finite. */
+pa_status pa_append_kv_qk_norm(const pa_pool* pool, const int32_t* block_tables,
+                               int32_t bt_stride, const int32_t* positions, const int32_t* dest,
+                               const void* k_new, const void* v_new, const void* q_in,
+                               void* q_out, int32_t num_q_heads, int32_t batch,
+                               const float* q_norm_weight, const float* k_norm_weight, float eps,
+                               hipStream_t stream);
+
 /* Paged decode attention.
  *
  * q: [batch][n_q][num_q_heads][D] in the pool dtype; row b starts at element b * q_row_stride

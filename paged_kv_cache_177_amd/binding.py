@@ -23,7 +23,7 @@ PA_F32, PA_BF16 = 0, 1
 PA_PAGED, PA_PADDED = 0, 1
 
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
-           "pa_decode_attention_block_sparse", "pa_advance_lockstep")
+           "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm")
 
 
 class PaError(RuntimeError):
@@ -75,6 +75,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                      _I32, _I32, _P, _I32, _P, _I32, _I32,
                                                      ctypes.c_float, _P, _I32, _P, _P, _P]
     lib.pa_advance_lockstep.argtypes = [_P, _P, _P, _I32, _P]
+    lib.pa_append_kv_qk_norm.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _P, _P, _P, _P, _P,
+                                         _I32, _I32, _P, _P, ctypes.c_float, _P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -166,6 +168,18 @@ def pa_decode_attention_block_sparse(pool: Pool, q, q_row_stride: int, n_q: int,
                                               mask_kv_blocks, _ptr(out), _ptr(lse),
                                               _stream(stream))
     _check("pa_decode_attention_block_sparse", st)
+
+
+def pa_append_kv_qk_norm(pool: Pool, block_tables, bt_stride: int, positions, dest, k_new,
+                         v_new, q_in, q_out, num_q_heads: int, batch: int, q_norm_weight,
+                         k_norm_weight, eps: float, stream=None) -> None:
+    lib = load_library()
+    st = lib.pa_append_kv_qk_norm(ctypes.byref(pool), _ptr(block_tables), bt_stride,
+                                  _ptr(positions), _ptr(dest), _ptr(k_new), _ptr(v_new),
+                                  _ptr(q_in), _ptr(q_out), num_q_heads, batch,
+                                  _ptr(q_norm_weight), _ptr(k_norm_weight), ctypes.c_float(eps),
+                                  _stream(stream))
+    _check("pa_append_kv_qk_norm", st)
 
 
 def pa_advance_lockstep(positions, kv_lens=None, dest=None, batch: int | None = None,

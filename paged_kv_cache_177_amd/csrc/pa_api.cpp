@@ -117,11 +117,13 @@ extern "C" pa_status pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size
   return PA_OK;
 }
 
-extern "C" pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables,
-                                  int32_t bt_stride, const int32_t* positions, const int32_t* dest,
-                                  const void* k_new, const void* v_new, const void* q_in,
-                                  void* q_out, int32_t num_q_heads, int32_t batch,
-                                  hipStream_t stream) {
+namespace {
+
+pa_status append_common(const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
+                        const int32_t* positions, const int32_t* dest, const void* k_new,
+                        const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
+                        int32_t batch, const float* q_norm_w, const float* k_norm_w,
+                        float norm_eps, hipStream_t stream) {
   pa_status s = check_pool(pool);
   if (s != PA_OK) return s;
   const pa_pool_desc& d = pool->desc;
@@ -159,7 +161,35 @@ extern "C" pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tabl
   a.q_in = q_in;
   a.q_out = q_out;
   a.batch = batch;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.norm_eps = norm_eps;
   return map_hip(pa::launch_append(a, stream));
+}
+
+}  // namespace
+
+extern "C" pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables,
+                                  int32_t bt_stride, const int32_t* positions, const int32_t* dest,
+                                  const void* k_new, const void* v_new, const void* q_in,
+                                  void* q_out, int32_t num_q_heads, int32_t batch,
+                                  hipStream_t stream) {
+  return append_common(pool, block_tables, bt_stride, positions, dest, k_new, v_new, q_in, q_out,
+                       num_q_heads, batch, nullptr, nullptr, 0.f, stream);
+}
+
+extern "C" pa_status pa_append_kv_qk_norm(const pa_pool* pool, const int32_t* block_tables,
+                                          int32_t bt_stride, const int32_t* positions,
+                                          const int32_t* dest, const void* k_new,
+                                          const void* v_new, const void* q_in, void* q_out,
+                                          int32_t num_q_heads, int32_t batch,
+                                          const float* q_norm_weight, const float* k_norm_weight,
+                                          float eps, hipStream_t stream) {
+  if (k_norm_weight == nullptr || (q_in != nullptr && q_norm_weight == nullptr))
+    return PA_ERR_NULL;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return PA_ERR_SHAPE;
+  return append_common(pool, block_tables, bt_stride, positions, dest, k_new, v_new, q_in, q_out,
+                       num_q_heads, batch, q_norm_weight, k_norm_weight, eps, stream);
 }
 
 extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,

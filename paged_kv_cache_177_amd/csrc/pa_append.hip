@@ -51,40 +51,70 @@ __device__ __forceinline__ void rotate_pair(float x_lo, float x_hi, float c, flo
 
 // Grid (ceil(heads * D/2 / 256), batch): blockIdx.y is the row, so its position, destination and
 // block-table entry are workgroup-uniform loads issued at once; the index inside the row needs only
-// shifts (D/2 is a power of two).
-template <typename T>
+// shifts (D/2 is a power of two). The D/2 lanes of one head are consecutive and aligned inside a
+// wave, which is what the per-head RMSNorm (NORM) reduces over: the sum of squares of the
+// rotate-half pairs, then a butterfly with lane strides 1, 2, 4, ... -- fp32 addition commutes,
+// so every lane ends with the same sum, formed as a pairwise tree of neighbours.
+template <typename T, bool NORM>
 __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int log2_half) {
+#pragma clang fp contract(off)
   const int half = 1 << log2_half;
   const int heads = 2 * a.H_kv + (a.q_in != nullptr ? a.H_q : 0);
   const int idx = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   const int b = (int)blockIdx.y;
-  if (idx >= heads * half) return;
+  const bool live = idx < heads * half;
   const int i = idx & (half - 1);
-  const int hh = idx >> log2_half;
+  const int hh = live ? idx >> log2_half : 0;
+  const bool is_q = hh >= 2 * a.H_kv;
+  const bool is_v = !is_q && hh >= a.H_kv;
+  const int h = is_q ? hh - 2 * a.H_kv : (is_v ? hh - a.H_kv : hh);
 
   const bool rope = a.cos != nullptr;
   int pos = a.positions[b];
   if (rope) pos = clampi(pos, 0, a.rope_max_pos - 1);
 
-  if (hh >= 2 * a.H_kv) {  // query head: rotate into q_out
-    const int h = hh - 2 * a.H_kv;
-    const size_t base = ((size_t)b * a.H_q + h) * a.D;
-    const T* src = reinterpret_cast<const T*>(a.q_in) + base;
-    T* dst = reinterpret_cast<T*>(a.q_out) + base;
+  const T* src = is_q ? reinterpret_cast<const T*>(a.q_in) + ((size_t)b * a.H_q + h) * a.D
+                      : reinterpret_cast<const T*>(is_v ? a.v_new : a.k_new) +
+                            ((size_t)b * a.H_kv + h) * a.D;
+  float x_lo = 0.f, x_hi = 0.f;
+  if (live && !is_v) {
+    x_lo = to_f32(src[i]);
+    x_hi = to_f32(src[i + half]);
+  }
+  if constexpr (NORM) {
+    // every lane takes part (no lane has returned yet); a head's lanes never mix with another's
+    float ss = x_lo * x_lo + x_hi * x_hi;
+    for (int m = 1; m < half; m <<= 1) ss = ss + __shfl_xor(ss, m);
+    const float ms = ss / (float)a.D;
+    const float r = 1.0f / sqrtf(ms + a.norm_eps);
+    if (live && !is_v) {
+      const float* w = is_q ? a.q_norm_w : a.k_norm_w;
+      x_lo = (x_lo * r) * w[i];
+      x_hi = (x_hi * r) * w[i + half];
+    }
+  }
+  if (!live) return;
+
+  // rotated (and/or normalised) values, or the raw bits when neither applies
+  auto store_pair = [&](T* dst) {
     if (rope) {
       float r_lo, r_hi;
-      rotate_pair(to_f32(src[i]), to_f32(src[i + half]), a.cos[(size_t)pos * half + i],
-                  a.sin[(size_t)pos * half + i], &r_lo, &r_hi);
+      rotate_pair(x_lo, x_hi, a.cos[(size_t)pos * half + i], a.sin[(size_t)pos * half + i], &r_lo,
+                  &r_hi);
       dst[i] = from_f32<T>(r_lo);
       dst[i + half] = from_f32<T>(r_hi);
+    } else if (NORM) {
+      dst[i] = from_f32<T>(x_lo);
+      dst[i + half] = from_f32<T>(x_hi);
     } else {
       copy_pair(src, dst, i, half);
     }
+  };
+
+  if (is_q) {  // query head: into q_out
+    store_pair(reinterpret_cast<T*>(a.q_out) + ((size_t)b * a.H_q + h) * a.D);
     return;
   }
-
-  const bool is_v = hh >= a.H_kv;
-  const int h = is_v ? hh - a.H_kv : hh;
   int t = a.dest != nullptr ? a.dest[b] : a.positions[b];
   size_t slot_base;  // element offset of [.., h, slot/column, 0]
   if (a.layout == PA_PAGED) {
@@ -96,24 +126,11 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int log
     t = clampi(t, 0, a.seq_cap - 1);
     slot_base = (((size_t)b * a.H_kv + h) * a.seq_cap + t) * a.D;
   }
-  const size_t src_base = ((size_t)b * a.H_kv + h) * a.D;
   if (is_v) {
-    const T* src = reinterpret_cast<const T*>(a.v_new) + src_base;
-    T* dst = reinterpret_cast<T*>(a.v) + slot_base;
-    copy_pair(src, dst, i, half);
+    copy_pair(src, reinterpret_cast<T*>(a.v) + slot_base, i, half);
     return;
   }
-  const T* src = reinterpret_cast<const T*>(a.k_new) + src_base;
-  T* dst = reinterpret_cast<T*>(a.k) + slot_base;
-  if (rope) {
-    float r_lo, r_hi;
-    rotate_pair(to_f32(src[i]), to_f32(src[i + half]), a.cos[(size_t)pos * half + i],
-                a.sin[(size_t)pos * half + i], &r_lo, &r_hi);
-    dst[i] = from_f32<T>(r_lo);
-    dst[i + half] = from_f32<T>(r_hi);
-  } else {
-    copy_pair(src, dst, i, half);
-  }
+  store_pair(reinterpret_cast<T*>(a.k) + slot_base);
 }
 
 // Advance a lockstep batch by one token: position += 1, kv_len = position + 1, dest += 1
@@ -145,10 +162,19 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   while ((1 << log2_half) < half) ++log2_half;
   if ((1 << log2_half) != half) return hipErrorInvalidValue;  // head_dim is 32, 64 or 128
   const dim3 grid((unsigned)((heads * half + 255) / 256), (unsigned)a.batch);
-  if (a.dtype == PA_F32)
-    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(256), 0, stream, a, log2_half);
-  else
-    hipLaunchKernelGGL(append_kernel<__bf16>, grid, dim3(256), 0, stream, a, log2_half);
+  const bool norm = a.k_norm_w != nullptr;
+  if (a.dtype == PA_F32) {
+    if (norm)
+      hipLaunchKernelGGL((append_kernel<float, true>), grid, dim3(256), 0, stream, a, log2_half);
+    else
+      hipLaunchKernelGGL((append_kernel<float, false>), grid, dim3(256), 0, stream, a, log2_half);
+  } else {
+    if (norm)
+      hipLaunchKernelGGL((append_kernel<__bf16, true>), grid, dim3(256), 0, stream, a, log2_half);
+    else
+      hipLaunchKernelGGL((append_kernel<__bf16, false>), grid, dim3(256), 0, stream, a,
+                         log2_half);
+  }
   return hipGetLastError();
 }
 

@@ -48,6 +48,10 @@ struct AppendArgs {
   const void* q_in;  // NULL: no queries
   void* q_out;
   int batch;
+  // per-head RMSNorm before RoPE: weights [D] fp32 (k_norm_w NULL: no normalisation)
+  const float* q_norm_w;
+  const float* k_norm_w;
+  float norm_eps;
 };
 
 struct DecodeArgs {

@@ -265,3 +265,18 @@ def test_advance_lockstep_argument_errors():
     assert lib.pa_advance_lockstep(None, None, None, 4, None) == B.PA_ERR_NULL
     assert lib.pa_advance_lockstep(FAKE, None, None, -1, None) == B.PA_ERR_SHAPE
     assert lib.pa_advance_lockstep(FAKE, None, None, 0, None) == B.PA_OK  # no launch
+
+
+def test_append_qk_norm_argument_errors():
+    lib = B.load_library()
+    p = _fake_pool(rope_max_pos=100, rope_theta=1e4)
+    call = lambda **kw: lib.pa_append_kv_qk_norm(  # noqa: E731
+        ctypes.byref(p), FAKE, 8, FAKE, None, FAKE, FAKE, kw.get("qi", None), kw.get("qo", None),
+        32, kw.get("batch", 0), kw.get("wq", FAKE), kw.get("wk", FAKE),
+        ctypes.c_float(kw.get("eps", 1e-5)), None)
+    assert call(wk=None) == B.PA_ERR_NULL
+    assert call(qi=FAKE, qo=FAKE, wq=None) == B.PA_ERR_NULL  # queries need their weight
+    assert call(wq=None) == B.PA_OK                           # no queries: no query weight
+    assert call(eps=-1.0) == B.PA_ERR_SHAPE
+    assert call(eps=float("nan")) == B.PA_ERR_SHAPE
+    assert call(batch=-1) == B.PA_ERR_SHAPE
