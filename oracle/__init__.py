@@ -32,4 +32,6 @@ from .reference import (  # noqa: F401
     padded_valid_columns,
     extract_row_padded,
     assemble_padded,
+    spike_embed_f32,
+    tokenize_kv,
 )

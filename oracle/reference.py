@@ -20,6 +20,9 @@ Sources (page title, then section):
   [CX-K]    cortex-engine write-up, kernels section, block-sparse cross-attention: FlashAttention-2
             style online softmax (running max, log-sum, output statistics); a fully masked row
             yields zeros, not NaN; many latent queries attend to ragged spike tokens.
+  [CX-T]    cortex-engine write-up, model section and kernels section (fused spike tokenizer):
+            each spike event (neuron_id, time_bin, value) becomes the sum of three embedding-table
+            rows, one per field, giving a flat, ragged sequence of tokens per sample.
 
 Storage conventions (the pages fix only "16-token blocks"; the rest is this library's contract):
   paged pool   K, V each [num_blocks][H_kv][16][D]; token t of row b lives at
@@ -494,3 +497,47 @@ def decode_paged_block_sparse(k_pool, v_pool, dtype, block_tables, kv_lens, q, s
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+# --------------------------------------------------------------------------------------------
+# Fused spike tokenizer + K/V projection into the paged pool [CX-T], [NG-0.7]
+# --------------------------------------------------------------------------------------------
+def spike_embed_f32(n_emb, t_emb, v_emb, neuron_ids, time_bins, value_ids):
+    """Token embeddings [CX-T]: x = (n_emb[neuron] + t_emb[bin]) + v_emb[value], each sum one
+    fp32 operation in this order (tables fp32 (rows, Dm))."""
+    n = np.asarray(n_emb, dtype=np.float32)[np.asarray(neuron_ids)]
+    t = np.asarray(t_emb, dtype=np.float32)[np.asarray(time_bins)]
+    v = np.asarray(v_emb, dtype=np.float32)[np.asarray(value_ids)]
+    return np.add(np.add(n, t), v).astype(np.float32)
+
+
+def tokenize_kv(k_pool, v_pool, n_emb, t_emb, v_emb, w_k, w_v, offsets, neuron_ids, time_bins,
+                value_ids, block_tables):
+    """Write the keys and values of every spike token into copies of the bf16 paged pools.
+
+    Row b's tokens are its events offsets[b] .. offsets[b+1] - 1, in order; token t goes to slot
+    (block_tables[b][t // 16], t % 16) [NG-0.7]. Its embedding x ([CX-T], ``spike_embed_f32``) is
+    rounded to bf16 (the matrix-core input); key = x . W_k^T and value = x . W_v^T with the bf16
+    weights [H * dh][Dm], summed in fp64 (the exact real value up to fp64 rounding), then rounded
+    to bf16 (through fp32) and split into heads of dh. Returns (k_pool', v_pool', kexact, vexact, sumabs):
+    the fp64 products before rounding and, per output, sum_i |x_i w_i| (for error bounds)."""
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    H, dh = k_pool.shape[1], k_pool.shape[3]
+    x = spike_embed_f32(n_emb, t_emb, v_emb, neuron_ids, time_bins, value_ids)
+    xb = storage_to_f64(f32_to_storage(x, "bf16"), "bf16")  # bf16 input, exact in fp64
+    wk = storage_to_f64(np.asarray(w_k), "bf16")
+    wv = storage_to_f64(np.asarray(w_v), "bf16")
+    kx = xb @ wk.T  # (E, H * dh) fp64
+    vx = xb @ wv.T
+    sabs = np.abs(xb) @ np.maximum(np.abs(wk), np.abs(wv)).T
+    kb = f32_to_storage(kx.astype(np.float32), "bf16")
+    vb = f32_to_storage(vx.astype(np.float32), "bf16")
+    offsets = np.asarray(offsets)
+    for b in range(len(offsets) - 1):
+        for e in range(int(offsets[b]), int(offsets[b + 1])):
+            t = e - int(offsets[b])
+            blk = int(block_tables[b][t // BLOCK])
+            k_out[blk, :, t % BLOCK, :] = kb[e].reshape(H, dh)
+            v_out[blk, :, t % BLOCK, :] = vb[e].reshape(H, dh)
+    return k_out, v_out, kx, vx, sabs

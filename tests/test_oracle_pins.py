@@ -620,3 +620,81 @@ def test_append_with_qk_norm_normalises_then_rotates():
     t = int(c.dest[0])
     kk = O.storage_to_f64(k3[c.block_tables[0][t // 16], :, t % 16, :], "bf16")
     np.testing.assert_allclose(np.sqrt((kk ** 2).mean(axis=-1)), 1.0, rtol=1e-2)
+
+
+# ---------------------------------------------------------------------------------------------
+# Fused spike tokenizer + K/V projection
+# ---------------------------------------------------------------------------------------------
+def _tok_case(rng, E_rows, Dm=64, H=2, dh=32):
+    n_emb = rng.normal(0, 0.5, (13, Dm)).astype(np.float32)
+    t_emb = rng.normal(0, 0.5, (9, Dm)).astype(np.float32)
+    v_emb = rng.normal(0, 0.5, (4, Dm)).astype(np.float32)
+    offsets = np.concatenate([[0], np.cumsum(E_rows)]).astype(np.int32)
+    E = int(offsets[-1])
+    nid = rng.integers(0, 13, E).astype(np.int32)
+    tb = np.sort(rng.integers(0, 9, E)).astype(np.int32)
+    vid = rng.integers(0, 4, E).astype(np.int32)
+    wk = W.to_storage(rng.normal(0, 0.2, (H * dh, Dm)).astype(np.float32), "bf16")
+    wv = W.to_storage(rng.normal(0, 0.2, (H * dh, Dm)).astype(np.float32), "bf16")
+    return n_emb, t_emb, v_emb, offsets, nid, tb, vid, wk, wv
+
+
+def test_spike_embedding_sums_three_rows_in_order():
+    rng = _rng(800)
+    n_emb, t_emb, v_emb, _, nid, tb, vid, _, _ = _tok_case(rng, [20])
+    x = O.spike_embed_f32(n_emb, t_emb, v_emb, nid, tb, vid)
+    ref = (n_emb[nid].astype(np.float64) + t_emb[tb] + v_emb[vid])
+    np.testing.assert_allclose(x, ref, rtol=0, atol=1e-6)
+    # the order is (n + t) + v: values where the other groupings round differently
+    big = np.full((1, 4), 1.0, np.float32)
+    x2 = O.spike_embed_f32(big, np.full((1, 4), 2.0 ** -24, np.float32),
+                           np.full((1, 4), 2.0 ** -24, np.float32), [0], [0], [0])
+    assert np.all(x2 == np.float32(1.0))  # 1 + 2^-24 rounds to 1, twice; n + (t + v) would not
+    # library routine: torch embedding lookups in fp64
+    te = (torch.nn.functional.embedding(torch.from_numpy(nid.astype(np.int64)),
+                                        torch.from_numpy(n_emb.astype(np.float64)))
+          + torch.nn.functional.embedding(torch.from_numpy(tb.astype(np.int64)),
+                                          torch.from_numpy(t_emb.astype(np.float64)))
+          + torch.nn.functional.embedding(torch.from_numpy(vid.astype(np.int64)),
+                                          torch.from_numpy(v_emb.astype(np.float64))))
+    np.testing.assert_allclose(x, te.numpy(), rtol=0, atol=1e-6)
+
+
+def test_tokenize_kv_slots_projection_and_closed_forms():
+    rng = _rng(810)
+    E_rows = [5, 0, 37, 16]
+    n_emb, t_emb, v_emb, off, nid, tb, vid, wk, wv = _tok_case(rng, E_rows)
+    c = W.make_paged_case("tok", 811, [e - 1 if e else 0 for e in E_rows], 2, 2, 32, "bf16")
+    k2, v2, kx, vx, sabs = O.tokenize_kv(c.k_pool, c.v_pool, n_emb, t_emb, v_emb, wk, wv, off,
+                                         nid, tb, vid, c.block_tables)
+    # exactly the events' slots changed (the pools hold NaN poison elsewhere: compare bits)
+    changed = np.zeros(c.k_pool.shape[:1] + (16,), bool)
+    for b in range(4):
+        for t in range(E_rows[b]):
+            changed[c.block_tables[b][t // 16], t % 16] = True
+    same_k = np.all(k2 == c.k_pool, axis=(1, 3))  # (blocks, 16)
+    assert np.array_equal(~same_k, changed)
+    # library routine: torch linear in fp64 on the bf16-rounded embeddings
+    x = O.spike_embed_f32(n_emb, t_emb, v_emb, nid, tb, vid)
+    xb = torch.from_numpy(O.storage_to_f64(O.f32_to_storage(x, "bf16"), "bf16"))
+    tk = torch.nn.functional.linear(xb, torch.from_numpy(O.storage_to_f64(wk, "bf16")))
+    np.testing.assert_allclose(kx, tk.numpy(), rtol=0, atol=1e-12)
+    # row 2, token 20 -> its block 1, slot 4; heads split the 64 outputs in order
+    e = int(off[2]) + 20
+    blk = c.block_tables[2][1]
+    np.testing.assert_array_equal(k2[blk, 1, 4, :],
+                                  O.f32_to_storage(kx[e, 32:].astype(np.float32), "bf16"))
+    np.testing.assert_array_equal(v2[blk, 0, 4, :],
+                                  O.f32_to_storage(vx[e, :32].astype(np.float32), "bf16"))
+    # identity projection: the key is the bf16-rounded embedding itself; doubling the weights
+    # doubles every key exactly
+    eye = W.to_storage(np.eye(64, dtype=np.float32), "bf16")
+    k3, _, kx3, _, _ = O.tokenize_kv(c.k_pool, c.v_pool, n_emb, t_emb, v_emb, eye, eye, off, nid,
+                                     tb, vid, c.block_tables)
+    np.testing.assert_array_equal(O.f32_to_storage(kx3.astype(np.float32), "bf16"),
+                                  O.f32_to_storage(x, "bf16"))
+    two = W.to_storage(2 * O.storage_to_f64(wk, "bf16").astype(np.float32), "bf16")
+    _, _, kx4, _, _ = O.tokenize_kv(c.k_pool, c.v_pool, n_emb, t_emb, v_emb, two, wv, off, nid,
+                                    tb, vid, c.block_tables)
+    np.testing.assert_array_equal(kx4, 2 * kx)
+    assert np.all(sabs >= np.abs(kx) - 1e-12)
