@@ -512,7 +512,7 @@ def spike_embed_f32(n_emb, t_emb, v_emb, neuron_ids, time_bins, value_ids):
 
 
 def tokenize_kv(k_pool, v_pool, n_emb, t_emb, v_emb, w_k, w_v, offsets, neuron_ids, time_bins,
-                value_ids, block_tables):
+                value_ids, block_tables, max_events=None):
     """Write the keys and values of every spike token into copies of the bf16 paged pools.
 
     Row b's tokens are its events offsets[b] .. offsets[b+1] - 1, in order; token t goes to slot
@@ -520,7 +520,8 @@ def tokenize_kv(k_pool, v_pool, n_emb, t_emb, v_emb, w_k, w_v, offsets, neuron_i
     rounded to bf16 (the matrix-core input); key = x . W_k^T and value = x . W_v^T with the bf16
     weights [H * dh][Dm], summed in fp64 (the exact real value up to fp64 rounding), then rounded
     to bf16 (through fp32) and split into heads of dh. Returns (k_pool', v_pool', kexact, vexact, sumabs):
-    the fp64 products before rounding and, per output, sum_i |x_i w_i| (for error bounds)."""
+    the fp64 products before rounding and, per output, sum_i |x_i w_i| (for error bounds).
+    With ``max_events``, a row's tokens past that count are not written."""
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     H, dh = k_pool.shape[1], k_pool.shape[3]
@@ -537,6 +538,8 @@ def tokenize_kv(k_pool, v_pool, n_emb, t_emb, v_emb, w_k, w_v, offsets, neuron_i
     for b in range(len(offsets) - 1):
         for e in range(int(offsets[b]), int(offsets[b + 1])):
             t = e - int(offsets[b])
+            if max_events is not None and t >= max_events:
+                break
             blk = int(block_tables[b][t // BLOCK])
             k_out[blk, :, t % BLOCK, :] = kb[e].reshape(H, dh)
             v_out[blk, :, t % BLOCK, :] = vb[e].reshape(H, dh)

@@ -23,7 +23,8 @@ PA_F32, PA_BF16 = 0, 1
 PA_PAGED, PA_PADDED = 0, 1
 
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
-           "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm")
+           "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm",
+           "pa_tokenize_kv")
 
 
 class PaError(RuntimeError):
@@ -75,6 +76,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                      _I32, _I32, _P, _I32, _P, _I32, _I32,
                                                      ctypes.c_float, _P, _I32, _P, _P, _P]
     lib.pa_advance_lockstep.argtypes = [_P, _P, _P, _I32, _P]
+    lib.pa_tokenize_kv.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _I32, _P, _I32, _I32, _P,
+                                   _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P]
     lib.pa_append_kv_qk_norm.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _P, _P, _P, _P, _P,
                                          _I32, _I32, _P, _P, ctypes.c_float, _P]
     for name in EXPORTS:
@@ -180,6 +183,20 @@ def pa_append_kv_qk_norm(pool: Pool, block_tables, bt_stride: int, positions, de
                                   _ptr(q_norm_weight), _ptr(k_norm_weight), ctypes.c_float(eps),
                                   _stream(stream))
     _check("pa_append_kv_qk_norm", st)
+
+
+def pa_tokenize_kv(pool: Pool, neuron_table, time_table, value_table, w_k, w_v, offsets,
+                   neuron_ids, time_bins, value_ids, block_tables, bt_stride: int, batch: int,
+                   max_events: int, stream=None) -> None:
+    """Tables: fp32 [rows][model_dim] tensors; w_k/w_v: bf16 [H * dh][model_dim]."""
+    lib = load_library()
+    st = lib.pa_tokenize_kv(ctypes.byref(pool), _ptr(neuron_table), neuron_table.shape[0],
+                            _ptr(time_table), time_table.shape[0], _ptr(value_table),
+                            value_table.shape[0], neuron_table.shape[1], _ptr(w_k), _ptr(w_v),
+                            _ptr(offsets), _ptr(neuron_ids), _ptr(time_bins), _ptr(value_ids),
+                            neuron_ids.shape[0], _ptr(block_tables), bt_stride, batch, max_events,
+                            _stream(stream))
+    _check("pa_tokenize_kv", st)
 
 
 def pa_advance_lockstep(positions, kv_lens=None, dest=None, batch: int | None = None,

@@ -256,6 +256,63 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
   return map_hip(e);
 }
 
+extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_table,
+                                    int32_t neuron_rows, const float* time_table,
+                                    int32_t time_rows, const float* value_table,
+                                    int32_t value_rows, int32_t model_dim, const void* w_k,
+                                    const void* w_v, const int32_t* offsets,
+                                    const int32_t* neuron_ids, const int32_t* time_bins,
+                                    const int32_t* value_ids, int32_t num_events,
+                                    const int32_t* block_tables, int32_t bt_stride,
+                                    int32_t batch, int32_t max_events, hipStream_t stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  const pa_pool_desc& d = pool->desc;
+  if (d.layout != PA_PAGED) return PA_ERR_SHAPE;
+  if (neuron_table == nullptr || time_table == nullptr || value_table == nullptr ||
+      w_k == nullptr || w_v == nullptr || offsets == nullptr || neuron_ids == nullptr ||
+      time_bins == nullptr || value_ids == nullptr || block_tables == nullptr)
+    return PA_ERR_NULL;
+  if (d.dtype != PA_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core path: bf16 pool
+  if (model_dim < 32 || model_dim % 32 != 0 || model_dim > pa::tokenize_max_model_dim())
+    return PA_ERR_UNSUPPORTED;
+  if (neuron_rows < 1 || time_rows < 1 || value_rows < 1) return PA_ERR_SHAPE;
+  if (batch < 0 || batch > pa::kMaxGridYZ || bt_stride < 1 || max_events < 0 || num_events < 0)
+    return PA_ERR_SHAPE;
+  if ((int64_t)max_events > (int64_t)bt_stride * pa::kBlock) return PA_ERR_SHAPE;
+  const uintptr_t align = (uintptr_t)neuron_table | (uintptr_t)time_table |
+                          (uintptr_t)value_table | (uintptr_t)w_k | (uintptr_t)w_v;
+  if (align % 16 != 0) return PA_ERR_SHAPE;  // 16-byte vector loads
+  if (batch == 0 || max_events == 0 || num_events == 0) return PA_OK;
+
+  pa::TokenizeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.H = d.num_kv_heads;
+  a.dh = d.head_dim;
+  a.model_dim = model_dim;
+  a.num_blocks = d.num_blocks;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.n_emb = neuron_table;
+  a.t_emb = time_table;
+  a.v_emb = value_table;
+  a.neuron_rows = neuron_rows;
+  a.time_rows = time_rows;
+  a.value_rows = value_rows;
+  a.w_k = w_k;
+  a.w_v = w_v;
+  a.offsets = offsets;
+  a.neuron_ids = neuron_ids;
+  a.time_bins = time_bins;
+  a.value_ids = value_ids;
+  a.num_events = num_events;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.batch = batch;
+  a.max_events = max_events;
+  return map_hip(pa::launch_tokenize(a, stream));
+}
+
 extern "C" pa_status pa_advance_lockstep(int32_t* positions, int32_t* kv_lens, int32_t* dest,
                                          int32_t batch, hipStream_t stream) {
   if (positions == nullptr) return PA_ERR_NULL;

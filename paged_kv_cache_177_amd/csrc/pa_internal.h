@@ -106,7 +106,30 @@ inline void carve_workspace(void* ws, int batch, int n_q, int H_q, int D, int s_
 }
 
 // ---- launchers (each returns the hipGetLastError of its launches) -----------------------------
+struct TokenizeArgs {
+  int H, dh, model_dim, num_blocks;
+  void* k;  // bf16 pool
+  void* v;
+  const float* n_emb;  // [neuron_rows][model_dim]
+  const float* t_emb;  // [time_rows][model_dim]
+  const float* v_emb;  // [value_rows][model_dim]
+  int neuron_rows, time_rows, value_rows;
+  const void* w_k;  // bf16 [H * dh][model_dim]
+  const void* w_v;
+  const int32_t* offsets;  // [batch + 1]
+  const int32_t* neuron_ids;
+  const int32_t* time_bins;
+  const int32_t* value_ids;
+  int num_events;  // length of the id arrays
+  const int32_t* block_tables;
+  int bt_stride;
+  int batch;
+  int max_events;
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_tokenize(const TokenizeArgs& a, hipStream_t stream);
+int tokenize_max_model_dim();
 hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
                           hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1

@@ -280,3 +280,21 @@ def test_append_qk_norm_argument_errors():
     assert call(eps=-1.0) == B.PA_ERR_SHAPE
     assert call(eps=float("nan")) == B.PA_ERR_SHAPE
     assert call(batch=-1) == B.PA_ERR_SHAPE
+
+
+def test_tokenize_argument_errors():
+    lib = B.load_library()
+    p = _fake_pool()  # paged bf16, 8 KV heads of 64
+    call = lambda **kw: lib.pa_tokenize_kv(  # noqa: E731
+        ctypes.byref(kw.get("pool", p)), kw.get("tab", FAKE), 10, FAKE, 10, FAKE, 4,
+        kw.get("dm", 256), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("ne", 500), FAKE, 64,
+        kw.get("batch", 4), kw.get("me", 100), None)
+    assert call(tab=None) == B.PA_ERR_NULL
+    assert call(dm=48) == B.PA_ERR_UNSUPPORTED     # not a multiple of 32
+    assert call(dm=1024) == B.PA_ERR_UNSUPPORTED   # above the LDS tile
+    assert call(me=64 * 16 + 1) == B.PA_ERR_SHAPE  # more events than the table rows hold
+    assert call(tab=FAKE + 4) == B.PA_ERR_SHAPE    # misaligned table
+    assert call(pool=_fake_pool(dtype="f32")) == B.PA_ERR_UNSUPPORTED
+    assert call(ne=-1) == B.PA_ERR_SHAPE
+    assert call(batch=0) == B.PA_OK
+    assert call(ne=0) == B.PA_OK

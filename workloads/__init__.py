@@ -23,5 +23,7 @@ from .generators import (  # noqa: F401
     b128,
     long_context,
     mq,
+    mq_tokenizer,
+    TokenizerCase,
     fp32_scale,
 )

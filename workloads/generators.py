@@ -412,3 +412,88 @@ def mq(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 13
                   num_blocks=num_blocks, poison_block=poison, kv_lens=kv_lens, block_tables=bt,
                   k_pool=k_pool, v_pool=v_pool, q=q, scale=fp32_scale(dh), seed=seed,
                   token_bins=token_bins, n_bins=n_bins)
+
+
+@dataclass
+class TokenizerCase:
+    """Raw spike events and the tokenizer's tables and weights, for the fused tokenizer + K/V
+    projection (the same recipe as ``mq``: tables N(0, 0.02), projections N(0, 1/model_dim), but
+    the weights stored bf16 in a linear layer's [out][in] layout and the events kept as ids)."""
+    name: str
+    n_emb: np.ndarray            # fp32 [neurons][Dm]
+    t_emb: np.ndarray            # fp32 [bins][Dm]
+    v_emb: np.ndarray            # fp32 [4][Dm], row = value - 1
+    w_k: np.ndarray              # bf16 bits [H * dh][Dm]
+    w_v: np.ndarray
+    offsets: np.ndarray          # int32 [B + 1]
+    neuron_ids: np.ndarray       # int32 [E]
+    time_bins: np.ndarray
+    value_ids: np.ndarray        # value - 1
+    num_heads: int
+    head_dim: int
+    num_blocks: int
+    poison_block: int
+    block_tables: np.ndarray
+    k_pool: np.ndarray           # poisoned bf16 pools [num_blocks][H][16][dh]
+    v_pool: np.ndarray
+    q: np.ndarray                # latent queries [n_q][H][dh] bf16, shared by every row
+    scale: float
+
+    @property
+    def batch(self) -> int:
+        return len(self.offsets) - 1
+
+    @property
+    def kv_lens(self) -> np.ndarray:
+        return np.diff(self.offsets).astype(np.int32)
+
+
+def mq_tokenizer(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 137,
+                 n_bins: int = 120, rate: float = 0.05, model_dim: int = 256,
+                 num_heads: int = 8) -> TokenizerCase:
+    """Spike events (Poisson(rate) counts per (neuron, bin) cell; one token per spike, ordered by
+    bin then neuron; value = min(count, 4)) with the tables, bf16 projection weights and latent
+    queries of the multi-query workload's recipe, and an empty shuffled pool for the tokens."""
+    rng = np.random.default_rng(seed)
+    counts = rng.poisson(rate, (batch, n_neurons, n_bins))
+    n_emb = rng.normal(0.0, 0.02, (n_neurons, model_dim)).astype(np.float32)
+    t_emb = rng.normal(0.0, 0.02, (n_bins, model_dim)).astype(np.float32)
+    v_emb = rng.normal(0.0, 0.02, (4, model_dim)).astype(np.float32)
+    w_q = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    w_k = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    w_v = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    latents = rng.normal(0.0, 0.02, (n_latents, model_dim)).astype(np.float32)
+    dh = model_dim // num_heads
+    q = to_storage((latents @ w_q).reshape(n_latents, num_heads, dh), "bf16")
+    nids, tbs, vids, offs = [], [], [], [0]
+    for b in range(batch):
+        c = counts[b].T  # (bins, neurons)
+        bins, neurons = np.nonzero(c)
+        reps = c[bins, neurons]
+        nids.append(np.repeat(neurons, reps))
+        tbs.append(np.repeat(bins, reps))
+        vids.append(np.minimum(np.repeat(reps, reps), 4) - 1)
+        offs.append(offs[-1] + int(reps.sum()))
+    offsets = np.asarray(offs, dtype=np.int32)
+    kv_lens = np.diff(offsets)
+    nblk = (kv_lens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    num_blocks = int(math.ceil(1.25 * int(nblk.sum()))) + 1
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    poison = int(perm[-1])
+    stride = max(1, int(nblk.max(initial=1)))
+    bt = np.full((batch, stride), poison, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        bt[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    shape = (num_blocks, num_heads, BLOCK_SIZE, dh)
+    return TokenizerCase(
+        name="mq-tokenizer", n_emb=n_emb, t_emb=t_emb, v_emb=v_emb,
+        w_k=to_storage(np.ascontiguousarray(w_k.T), "bf16"),
+        w_v=to_storage(np.ascontiguousarray(w_v.T), "bf16"),
+        offsets=offsets, neuron_ids=np.concatenate(nids).astype(np.int32),
+        time_bins=np.concatenate(tbs).astype(np.int32),
+        value_ids=np.concatenate(vids).astype(np.int32), num_heads=num_heads, head_dim=dh,
+        num_blocks=num_blocks, poison_block=poison, block_tables=bt,
+        k_pool=np.full(shape, POISON_BF16, dtype=np.uint16),
+        v_pool=np.full(shape, POISON_BF16, dtype=np.uint16), q=q, scale=fp32_scale(dh))
