@@ -36,11 +36,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="b128", choices=["b128", "long", "mq", "mq-sparse", "b16"],
+    p.add_argument("--workload", default="b128",
+                   choices=["b128", "long", "mq", "mq-sparse", "b16", "mq-tokenize"],
                    help="b128 is the reported workload; long (B=4 long-context split-K), mq "
                         "(latent cross-attention on the matrix cores; mq-sparse under the "
-                        "temporal block mask) and b16 (the B=16 lockstep step, paged and "
-                        "right-padded) measure the other paths")
+                        "temporal block mask), b16 (the B=16 lockstep step, paged and "
+                        "right-padded) and mq-tokenize (the fused spike tokenizer + K/V "
+                        "projection) measure the other paths")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="cache-flush write between the extra flushed decode timings")
@@ -231,6 +233,119 @@ def main_mq(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_mq(case, flops, keep=keep if sparse else None)
     print(json.dumps(out), flush=True)
+
+
+def main_tokenize(args):
+    """Fused spike tokenizer + K/V projection into the paged pool: 16 rows of raw spike events
+    (neuron, time bin, value), one pa_tokenize_kv call per step. The kernel's floor is HBM: every
+    token writes H * dh keys and as many values (bf16) and reads its three ids; the tables and the
+    two projection matrices are read once. The matrix-core FLOPs are reported beside it."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_177_amd import binding as B
+    from paged_kv_cache_177_amd.runner import to_torch
+
+    torch.cuda.set_device(0)
+    c = W.mq_tokenizer()
+    desc = B.make_desc("paged", "bf16", c.num_heads, c.head_dim, num_blocks=c.num_blocks)
+    pool = B.alloc_pool(desc)
+    pool.k.copy_(to_torch(c.k_pool, "bf16"))
+    pool.v.copy_(to_torch(c.v_pool, "bf16"))
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    n_emb, t_emb, v_emb = d(c.n_emb), d(c.t_emb), d(c.v_emb)
+    # weights packed once into matrix-core fragment order (outside the timed calls, as a server
+    # would at load time)
+    w_k = B.pa_pack_projection(to_torch(c.w_k, "bf16").cuda())
+    w_v = B.pa_pack_projection(to_torch(c.w_v, "bf16").cuda())
+    offsets, nid, tb, vid = d(c.offsets), d(c.neuron_ids), d(c.time_bins), d(c.value_ids)
+    bt = d(c.block_tables)
+    me = int(c.kv_lens.max())
+    E = int(c.offsets[-1])
+    N = c.num_heads * c.head_dim
+    Dm = c.n_emb.shape[1]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.pa_tokenize_kv(pool.pool, n_emb, t_emb, v_emb, w_k, w_v, offsets, nid, tb, vid, bt,
+                         c.block_tables.shape[1], c.batch, me)
+
+    # algorithmic bytes: K and V slots written (bf16), three int32 ids per token, the two bf16
+    # weight matrices and the three fp32 tables once, the offsets and the block-table entries used
+    used_blocks = int(sum((int(n) + 15) // 16 for n in c.kv_lens))
+    nbytes = float(E * (2 * N * 2 + 3 * 4) + 2 * N * Dm * 2 +
+                   (c.n_emb.size + c.t_emb.size + c.v_emb.size) * 4 + (c.batch + 1) * 4 +
+                   used_blocks * 4)
+    flops = 2.0 * E * Dm * 2 * N
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < 1.0:
+        for _ in range(10):
+            call()
+        done += 10
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(args.steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    avg_ms = a.elapsed_time(b) / args.steps
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    out = {
+        "metric": "spike tokens tokenized and projected into the paged K/V pool per second, bf16",
+        "value": round(E / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{c.name}: B={c.batch} rows of spike events "
+                                f"{int(c.kv_lens.min())}..{me} (sum {E}), model dim {Dm}, "
+                                f"{c.num_heads} heads of {c.head_dim}, 16-token blocks"),
+                   "global_batch": c.batch, "bytes_per_step": nbytes, "flops_per_step": flops,
+                   "step": "one pa_tokenize_kv call"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tokenize_kv_kernel", "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(avg_ms * 1e3, 2)},
+        "detail": {"us_per_call": round(avg_ms * 1e3, 2),
+                   "mfma_tflops": round(flops / (avg_ms * 1e-3) / 1e12, 1),
+                   "mfma_frac": round(flops / (avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_tokenize(c, E)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_tokenize(c, E: int, budget_s: float = 10.0, max_reps: int = 200):
+    """The oracle's tokenize_kv on the full workload (embed, fp64 projection, pool writes)."""
+    import oracle as O
+
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_start) < budget_s:
+        t0 = time.perf_counter()
+        O.tokenize_kv(c.k_pool, c.v_pool, c.n_emb, c.t_emb, c.v_emb, c.w_k, c.w_v, c.offsets,
+                      c.neuron_ids, c.time_bins, c.value_ids, c.block_tables)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    cores = blas_threads()
+    return {"value": E / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"full {c.name} workload ({c.batch} rows, {E} tokens) in fp64 numpy, "
+                       f"median of {len(times)} run(s), {t:.2f} s each; host affinity "
+                       f"{len(os.sched_getaffinity(0))} cores, BLAS threads {cores}")}
 
 
 def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64):
@@ -444,6 +559,8 @@ def main():
     if args.workload in ("mq", "mq-sparse"):
         main_mq(args)
         return
+    if args.workload == "mq-tokenize":
+        return main_tokenize(args)
     if args.workload == "b16":
         main_b16(args)
         return

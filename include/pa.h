@@ -169,6 +169,20 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
                               size_t workspace_bytes, size_t* workspace_needed /* host */,
                               float* out, float* lse, hipStream_t stream);
 
+/* Projection weights in matrix-core fragment order, for pa_tokenize_kv (a layout of this library,
+ * not of the pages: one A-operand fragment of the 16x16x32 bf16 matrix-core product is 64 lanes x
+ * 16 contiguous bytes, so the tokenizer reads each with one coalesced 1 KB load).
+ * w: bf16 [out_features][in_features] (a linear layer's weight), device. packed: device, as many
+ * bytes, must not overlap w; on return
+ *   packed[((tile * (in_features / 32) + kc) * 64 + lane) * 8 + j]
+ *     = w[16 tile + lane % 16][32 kc + 8 (lane / 16) + j]
+ * for tile < out_features / 16, kc < in_features / 32, lane < 64, j < 8 (a permutation: values
+ * are copied bit for bit). Asynchronous on stream.
+ * Errors: PA_ERR_NULL; PA_ERR_SHAPE (out_features not a positive multiple of 16, in_features not a
+ * positive multiple of 32, a pointer not 16-byte aligned, overlapping buffers). */
+pa_status pa_pack_projection(const void* w, int32_t out_features, int32_t in_features,
+                             void* packed, hipStream_t stream);
+
 /* Spike tokens straight into the paged pool: the fused three-table tokenizer and K/V projection
  * ("cortex-engine write-up", model section and kernels section, fused spike tokenizer: each spike
  * event (neuron_id, time_bin, value) is the sum of three embedding-table rows; "NeuroGrid
@@ -179,21 +193,23 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
  * (more are ignored). Offsets are clamped into [0, num_events].
  * Token t (0-based within the row) has the embedding x = (neuron_table[neuron_ids[e]] +
  * time_table[time_bins[e]]) + value_table[value_ids[e]] (fp32 tables [rows][model_dim], each sum
- * one fp32 operation; ids clamped into their tables), rounded to bf16. Its key is x . w_k^T and
- * its value x . w_v^T (bf16 weights [H_kv * head_dim][model_dim], the layout of a linear layer's
+ * one fp32 operation; ids clamped into their tables), rounded to bf16. Its key is x . W_k^T and
+ * its value x . W_v^T (bf16 weights [H_kv * head_dim][model_dim], the layout of a linear layer's
  * weight; products summed in fp32 on the matrix cores, in an unspecified order), rounded to bf16
  * and stored as heads of head_dim at slot (block_tables[b * bt_stride + t / 16], t % 16). Only the
  * rows' token slots are written. The embeddings never reach memory.
- * Requirements: a PA_PAGED bf16 pool; model_dim a multiple of 32 in [32, 512]; tables and weights
- * 16-byte aligned; max_events <= bt_stride * 16.
+ * w_k_packed / w_v_packed are W_k and W_v as pa_pack_projection leaves them (device, H_kv *
+ * head_dim * model_dim bf16 each); pack once, reuse for every call.
+ * Requirements: a PA_PAGED bf16 pool; model_dim a multiple of 32 in [32, 512]; tables and packed
+ * weights 16-byte aligned; max_events <= bt_stride * 16.
  * Errors: PA_ERR_NULL (any pointer); PA_ERR_UNSUPPORTED (fp32 pool, model_dim out of range);
  * PA_ERR_SHAPE (layout not PA_PAGED, table rows < 1, batch < 0 or > 65535, bt_stride < 1,
  * num_events < 0, max_events < 0 or > bt_stride * 16, misaligned tables or weights). batch == 0,
  * num_events == 0 or max_events == 0 is a no-op. */
 pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_table, int32_t neuron_rows,
                          const float* time_table, int32_t time_rows, const float* value_table,
-                         int32_t value_rows, int32_t model_dim, const void* w_k, const void* w_v,
-                         const int32_t* offsets, const int32_t* neuron_ids,
+                         int32_t value_rows, int32_t model_dim, const void* w_k_packed,
+                         const void* w_v_packed, const int32_t* offsets, const int32_t* neuron_ids,
                          const int32_t* time_bins, const int32_t* value_ids,
                          int32_t num_events, const int32_t* block_tables, int32_t bt_stride,
                          int32_t batch, int32_t max_events, hipStream_t stream);

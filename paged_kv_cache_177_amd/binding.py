@@ -24,7 +24,7 @@ PA_PAGED, PA_PADDED = 0, 1
 
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
            "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm",
-           "pa_tokenize_kv")
+           "pa_tokenize_kv", "pa_pack_projection")
 
 
 class PaError(RuntimeError):
@@ -78,6 +78,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_advance_lockstep.argtypes = [_P, _P, _P, _I32, _P]
     lib.pa_tokenize_kv.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _I32, _P, _I32, _I32, _P,
                                    _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P]
+    lib.pa_pack_projection.argtypes = [_P, _I32, _I32, _P, _P]
     lib.pa_append_kv_qk_norm.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _P, _P, _P, _P, _P,
                                          _I32, _I32, _P, _P, ctypes.c_float, _P]
     for name in EXPORTS:
@@ -185,14 +186,29 @@ def pa_append_kv_qk_norm(pool: Pool, block_tables, bt_stride: int, positions, de
     _check("pa_append_kv_qk_norm", st)
 
 
-def pa_tokenize_kv(pool: Pool, neuron_table, time_table, value_table, w_k, w_v, offsets,
-                   neuron_ids, time_bins, value_ids, block_tables, bt_stride: int, batch: int,
-                   max_events: int, stream=None) -> None:
-    """Tables: fp32 [rows][model_dim] tensors; w_k/w_v: bf16 [H * dh][model_dim]."""
+def pa_pack_projection(w, packed=None, stream=None):
+    """Pack a bf16 [out_features][in_features] weight into matrix-core fragment order (a new
+    tensor of the same size unless ``packed`` is given); returns the packed tensor."""
+    import torch
+
+    lib = load_library()
+    if packed is None:
+        packed = torch.empty_like(w)
+    st = lib.pa_pack_projection(_ptr(w), w.shape[0], w.shape[1], _ptr(packed), _stream(stream))
+    _check("pa_pack_projection", st)
+    return packed
+
+
+def pa_tokenize_kv(pool: Pool, neuron_table, time_table, value_table, w_k_packed, w_v_packed,
+                   offsets, neuron_ids, time_bins, value_ids, block_tables, bt_stride: int,
+                   batch: int, max_events: int, stream=None) -> None:
+    """Tables: fp32 [rows][model_dim] tensors; w_k_packed/w_v_packed: the bf16 [H * dh][model_dim]
+    weights after pa_pack_projection."""
     lib = load_library()
     st = lib.pa_tokenize_kv(ctypes.byref(pool), _ptr(neuron_table), neuron_table.shape[0],
                             _ptr(time_table), time_table.shape[0], _ptr(value_table),
-                            value_table.shape[0], neuron_table.shape[1], _ptr(w_k), _ptr(w_v),
+                            value_table.shape[0], neuron_table.shape[1], _ptr(w_k_packed),
+                            _ptr(w_v_packed),
                             _ptr(offsets), _ptr(neuron_ids), _ptr(time_bins), _ptr(value_ids),
                             neuron_ids.shape[0], _ptr(block_tables), bt_stride, batch, max_events,
                             _stream(stream))

@@ -259,8 +259,9 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
 extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_table,
                                     int32_t neuron_rows, const float* time_table,
                                     int32_t time_rows, const float* value_table,
-                                    int32_t value_rows, int32_t model_dim, const void* w_k,
-                                    const void* w_v, const int32_t* offsets,
+                                    int32_t value_rows, int32_t model_dim,
+                                    const void* w_k_packed, const void* w_v_packed,
+                                    const int32_t* offsets,
                                     const int32_t* neuron_ids, const int32_t* time_bins,
                                     const int32_t* value_ids, int32_t num_events,
                                     const int32_t* block_tables, int32_t bt_stride,
@@ -270,8 +271,9 @@ extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_tab
   const pa_pool_desc& d = pool->desc;
   if (d.layout != PA_PAGED) return PA_ERR_SHAPE;
   if (neuron_table == nullptr || time_table == nullptr || value_table == nullptr ||
-      w_k == nullptr || w_v == nullptr || offsets == nullptr || neuron_ids == nullptr ||
-      time_bins == nullptr || value_ids == nullptr || block_tables == nullptr)
+      w_k_packed == nullptr || w_v_packed == nullptr || offsets == nullptr ||
+      neuron_ids == nullptr || time_bins == nullptr || value_ids == nullptr ||
+      block_tables == nullptr)
     return PA_ERR_NULL;
   if (d.dtype != PA_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core path: bf16 pool
   if (model_dim < 32 || model_dim % 32 != 0 || model_dim > pa::tokenize_max_model_dim())
@@ -281,7 +283,8 @@ extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_tab
     return PA_ERR_SHAPE;
   if ((int64_t)max_events > (int64_t)bt_stride * pa::kBlock) return PA_ERR_SHAPE;
   const uintptr_t align = (uintptr_t)neuron_table | (uintptr_t)time_table |
-                          (uintptr_t)value_table | (uintptr_t)w_k | (uintptr_t)w_v;
+                          (uintptr_t)value_table | (uintptr_t)w_k_packed |
+                          (uintptr_t)w_v_packed;
   if (align % 16 != 0) return PA_ERR_SHAPE;  // 16-byte vector loads
   if (batch == 0 || max_events == 0 || num_events == 0) return PA_OK;
 
@@ -299,8 +302,8 @@ extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_tab
   a.neuron_rows = neuron_rows;
   a.time_rows = time_rows;
   a.value_rows = value_rows;
-  a.w_k = w_k;
-  a.w_v = w_v;
+  a.w_k = w_k_packed;
+  a.w_v = w_v_packed;
   a.offsets = offsets;
   a.neuron_ids = neuron_ids;
   a.time_bins = time_bins;
@@ -311,6 +314,18 @@ extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_tab
   a.batch = batch;
   a.max_events = max_events;
   return map_hip(pa::launch_tokenize(a, stream));
+}
+
+extern "C" pa_status pa_pack_projection(const void* w, int32_t out_features, int32_t in_features,
+                                        void* packed, hipStream_t stream) {
+  if (w == nullptr || packed == nullptr) return PA_ERR_NULL;
+  if (out_features < 16 || out_features % 16 != 0 || in_features < 32 || in_features % 32 != 0)
+    return PA_ERR_SHAPE;
+  if (((uintptr_t)w | (uintptr_t)packed) % 16 != 0) return PA_ERR_SHAPE;
+  const uintptr_t bytes = (uintptr_t)out_features * (uintptr_t)in_features * 2;
+  const uintptr_t wa = (uintptr_t)w, pb = (uintptr_t)packed;
+  if (wa < pb + bytes && pb < wa + bytes) return PA_ERR_SHAPE;  // overlapping buffers
+  return map_hip(pa::launch_pack_projection(w, packed, out_features, in_features, stream));
 }
 
 extern "C" pa_status pa_advance_lockstep(int32_t* positions, int32_t* kv_lens, int32_t* dest,

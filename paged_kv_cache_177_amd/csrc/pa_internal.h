@@ -114,7 +114,7 @@ struct TokenizeArgs {
   const float* t_emb;  // [time_rows][model_dim]
   const float* v_emb;  // [value_rows][model_dim]
   int neuron_rows, time_rows, value_rows;
-  const void* w_k;  // bf16 [H * dh][model_dim]
+  const void* w_k;  // bf16 [H * dh][model_dim], packed by launch_pack_projection
   const void* w_v;
   const int32_t* offsets;  // [batch + 1]
   const int32_t* neuron_ids;
@@ -130,6 +130,8 @@ struct TokenizeArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_tokenize(const TokenizeArgs& a, hipStream_t stream);
 int tokenize_max_model_dim();
+hipError_t launch_pack_projection(const void* w, void* packed, int out_features, int in_features,
+                                  hipStream_t stream);
 hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
                           hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1

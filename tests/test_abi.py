@@ -298,3 +298,16 @@ def test_tokenize_argument_errors():
     assert call(ne=-1) == B.PA_ERR_SHAPE
     assert call(batch=0) == B.PA_OK
     assert call(ne=0) == B.PA_OK
+
+
+def test_pack_projection_argument_errors():
+    lib = B.load_library()
+    call = lambda w=FAKE, o=256, i=256, pk=FAKE + (1 << 20): lib.pa_pack_projection(  # noqa: E731
+        w, o, i, pk, None)
+    assert call(w=None) == B.PA_ERR_NULL
+    assert call(pk=None) == B.PA_ERR_NULL
+    assert call(o=24) == B.PA_ERR_SHAPE            # out_features not a multiple of 16
+    assert call(o=0) == B.PA_ERR_SHAPE
+    assert call(i=48) == B.PA_ERR_SHAPE            # in_features not a multiple of 32
+    assert call(w=FAKE + 8) == B.PA_ERR_SHAPE      # misaligned
+    assert call(pk=FAKE + 1024) == B.PA_ERR_SHAPE  # overlaps w (256 x 256 x 2 bytes)

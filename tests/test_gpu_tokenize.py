@@ -25,7 +25,8 @@ def _run(c, max_events=None):
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     me = int(c.kv_lens.max(initial=0)) if max_events is None else max_events
     B.pa_tokenize_kv(pool.pool, d(c.n_emb), d(c.t_emb), d(c.v_emb),
-                     to_torch(c.w_k, "bf16").cuda(), to_torch(c.w_v, "bf16").cuda(),
+                     B.pa_pack_projection(to_torch(c.w_k, "bf16").cuda()),
+                     B.pa_pack_projection(to_torch(c.w_v, "bf16").cuda()),
                      d(c.offsets), d(c.neuron_ids), d(c.time_bins), d(c.value_ids),
                      d(c.block_tables), c.block_tables.shape[1], c.batch, me)
     torch.cuda.synchronize()
@@ -108,3 +109,17 @@ def test_tokenize_ragged_edges_and_truncation():
     _check(c, pool)
     pool = _run(c, max_events=20)
     _check(c, pool, max_events=20)
+
+
+def test_pack_projection_layout():
+    """pa_pack_projection is a bit-for-bit permutation into the documented fragment order: packed
+    [((tile * (in / 32) + kc) * 64 + lane) * 8 + j] = w[16 tile + lane % 16][32 kc + 8 (lane / 16)
+    + j]; checked against the same index map written with numpy reshapes (and two sizes)."""
+    rng = np.random.default_rng(11)
+    for out_f, in_f in ((256, 256), (48, 96)):
+        w = rng.integers(0, 1 << 16, size=(out_f, in_f), dtype=np.uint16)
+        got = B.pa_pack_projection(torch.from_numpy(w.view(np.int16)).cuda()).cpu().numpy()
+        got = got.view(np.uint16).reshape(-1)
+        # w[tile, r, kc, g, j] with row 16 tile + r, input 32 kc + 8 g + j -> [tile, kc, g, r, j]
+        ref = w.reshape(out_f // 16, 16, in_f // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+        assert np.array_equal(got, ref), (out_f, in_f)
