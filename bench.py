@@ -52,14 +52,22 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(*names: str) -> str:
+    """sha256 prefix of the named kernel sources (file names under csrc/; all sources if none):
+    ties a committed counter summary to the code of the kernels it measured."""
     from paged_kv_cache_177_amd.build import sources
 
     h = hashlib.sha256()
     for s in sources():
+        if names and os.path.basename(s) not in names:
+            continue
         with open(s, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# the decode call's kernels (decode_vector_kernel, decode_persistent_kernel, lse_reduce_kernel)
+DECODE_SOURCES = ("pa_decode.hip", "pa_internal.h")
 
 
 def read_traffic(src_hash: str):
@@ -86,7 +94,7 @@ def blas_threads() -> int:
     return int(max(blas)) if blas else 1
 
 
-def cpu_baseline_mq(case, flops: float, keep=None, budget_s: float = 10.0, max_reps: int = 3):
+def cpu_baseline_mq(case, flops: float, keep=None, budget_s: float = 10.0, max_reps: int = 50):
     """The oracle on the full multi-query workload (all rows, shared latent queries); with
     ``keep``, its block-sparse form under that mask."""
     import oracle as O
@@ -111,7 +119,7 @@ def cpu_baseline_mq(case, flops: float, keep=None, budget_s: float = 10.0, max_r
                        f"affinity {len(os.sched_getaffinity(0))} cores, BLAS threads {cores}")}
 
 
-def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 3):
+def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 50):
     """The oracle (as it stands) on the full workload's decode: gather every row through its block
     table and run two-pass fp64 attention. Repeated until ~budget_s of CPU work, median taken."""
     import oracle as O
@@ -228,7 +236,8 @@ def main_mq(args):
                      "kernel": "mq_paged_mfma_kernel<32, " + ("true>" if sparse else "false>"),
                      "flops_per_launch": flops,
                      "avg_launch_us": round(avg_ms * 1e3, 2)},
-        "detail": {"us_per_call": round(avg_ms * 1e3, 2), "source_hash": kernel_source_hash()},
+        "detail": {"us_per_call": round(avg_ms * 1e3, 2),
+                   "source_hash": kernel_source_hash("pa_mq.hip", "pa_internal.h")},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_mq(case, flops, keep=keep if sparse else None)
@@ -322,7 +331,7 @@ def main_tokenize(args):
         "detail": {"us_per_call": round(avg_ms * 1e3, 2),
                    "mfma_tflops": round(flops / (avg_ms * 1e-3) / 1e12, 1),
                    "mfma_frac": round(flops / (avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "source_hash": kernel_source_hash()},
+                   "source_hash": kernel_source_hash("pa_tokenize.hip", "pa_internal.h")},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_tokenize(c, E)
@@ -622,7 +631,7 @@ def main():
     del flush
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(*DECODE_SOURCES)
     traffic = read_traffic(src_hash) if args.workload == "b128" else None
     out = {
         "metric": METRIC if args.workload == "b128" else METRIC_LONG,
