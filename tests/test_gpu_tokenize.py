@@ -123,3 +123,19 @@ def test_pack_projection_layout():
         # w[tile, r, kc, g, j] with row 16 tile + r, input 32 kc + 8 g + j -> [tile, kc, g, r, j]
         ref = w.reshape(out_f // 16, 16, in_f // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
         assert np.array_equal(got, ref), (out_f, in_f)
+
+
+@pytest.mark.parametrize("model_dim,num_heads,head_dim", [
+    (96, 3, 32),    # odd number of 32-input steps (a padding step); tiles dead inside a group
+    (32, 1, 32),    # one step; four of the eight waves own no tile
+    (64, 2, 64),
+    (512, 8, 128),  # 16 steps per tile; four tile groups per wave
+])
+def test_tokenize_shapes(model_dim, num_heads, head_dim):
+    """Other model widths and head shapes against the oracle: every written value within the
+    bound, every other slot untouched."""
+    c = W.mq_tokenizer(seed=31, batch=3, n_neurons=60, n_bins=80, model_dim=model_dim,
+                       num_heads=num_heads, head_dim=head_dim)
+    log(f"[tokenize] Dm={model_dim} H={num_heads} dh={head_dim} events={int(c.offsets[-1])}")
+    pool = _run(c)
+    _check(c, pool)

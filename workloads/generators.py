@@ -450,20 +450,23 @@ class TokenizerCase:
 
 def mq_tokenizer(seed: int = 4, batch: int = 16, n_latents: int = 256, n_neurons: int = 137,
                  n_bins: int = 120, rate: float = 0.05, model_dim: int = 256,
-                 num_heads: int = 8) -> TokenizerCase:
+                 num_heads: int = 8, head_dim: int | None = None) -> TokenizerCase:
     """Spike events (Poisson(rate) counts per (neuron, bin) cell; one token per spike, ordered by
     bin then neuron; value = min(count, 4)) with the tables, bf16 projection weights and latent
-    queries of the multi-query workload's recipe, and an empty shuffled pool for the tokens."""
+    queries of the multi-query workload's recipe, and an empty shuffled pool for the tokens.
+    The projections map model_dim to num_heads * head_dim (head_dim defaults to
+    model_dim / num_heads, the square case)."""
     rng = np.random.default_rng(seed)
+    dh = model_dim // num_heads if head_dim is None else head_dim
+    out = num_heads * dh
     counts = rng.poisson(rate, (batch, n_neurons, n_bins))
     n_emb = rng.normal(0.0, 0.02, (n_neurons, model_dim)).astype(np.float32)
     t_emb = rng.normal(0.0, 0.02, (n_bins, model_dim)).astype(np.float32)
     v_emb = rng.normal(0.0, 0.02, (4, model_dim)).astype(np.float32)
-    w_q = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
-    w_k = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
-    w_v = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, model_dim)).astype(np.float32)
+    w_q = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, out)).astype(np.float32)
+    w_k = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, out)).astype(np.float32)
+    w_v = rng.normal(0.0, 1.0 / math.sqrt(model_dim), (model_dim, out)).astype(np.float32)
     latents = rng.normal(0.0, 0.02, (n_latents, model_dim)).astype(np.float32)
-    dh = model_dim // num_heads
     q = to_storage((latents @ w_q).reshape(n_latents, num_heads, dh), "bf16")
     nids, tbs, vids, offs = [], [], [], [0]
     for b in range(batch):
