@@ -4,16 +4,19 @@
 // a FlashAttention-2 style online softmax; a fully masked row gives zeros).
 //
 // Query "rows" of KV head g are the (query i, head h) pairs with h in g's group: r = i * G + (h - gG).
-// One workgroup (4 waves) takes 16 query rows of one (row b, KV head g); its waves split the row's
-// 16-token key blocks round-robin (two blocks in flight per wave while one is computed) and merge
-// through LDS at the end. Per block, per wave:
+// One workgroup (4 waves) takes 16 QT query rows of one (row b, KV head g); its waves split the
+// row's 16-token key blocks round-robin (two blocks in flight per wave while one is computed) and
+// merge through LDS at the end. Each wave carries the QT sub-tiles of 16 query rows through every
+// block it reads, so a block's loads, its V staging and its V^T fragments serve 16 QT queries.
+// Per block, per wave and sub-tile:
 //   S^T[16 keys][16 q] = K[16 keys][D] . Q^T[D][16 q]   v_mfma_f32_16x16x32_bf16, D/32 steps
 //       K is the A operand straight from the block (lane: key l%16, 8 dims), Q^T the B operand
 //       (lane: query l%16, 8 dims); the result puts query l%16 in lane l, keys 4(l/16)..+3.
 //   online softmax per query: lane-local, plus two cross-lane steps for the block maximum;
 //   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   v_mfma_f32_16x16x16_bf16, D/16 steps
 //       P^T is the B operand exactly as the first product left it (query l%16, keys 4(l/16)..);
-//       V^T (lane: dim l%16, keys 4(l/16)..) is read transposed from the block staged in LDS.
+//       V^T (lane: dim l%16, keys 4(l/16)..) comes from the block staged in LDS with one
+//       ds_read_b64_tr_b16 per 16 dims (the gfx950 transposing LDS read).
 //       P is split into bf16 hi + lo parts (two products), so the weights keep ~16 bits.
 // Query rows therefore sit in the same lanes in S^T and O^T: rescales and the final division are
 // lane-local.
@@ -25,7 +28,10 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -44,31 +50,48 @@ __device__ __forceinline__ float swap_halves32(float x) { return __shfl_xor(x, 3
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// fp32 -> bf16 bits, round to nearest even (hardware conversion)
-__device__ __forceinline__ unsigned short bf16_bits(float x) {
-  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ float bf16_value(unsigned short b) {
-  return __uint_as_float((unsigned)b << 16);
+// Two fp32 weights -> their bf16 hi parts (RNE, one packed conversion) and the bf16 of what the
+// hi parts leave over: p ~ hi + lo to ~16 bits.
+__device__ __forceinline__ void split_bf16x2(float p0, float p1, unsigned& hi, unsigned& lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t));
+  const f32x2_t h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{p0, p1} - h, bf16x2_t));
 }
 
-template <int D>
+// ds_read_b64_tr_b16: within each 16-lane quarter-wave, lanes 4j .. 4j + 3 name (with 8-byte
+// addresses, 4 elements each) row j of a 4 x 16 block of 16-bit elements, and lane l receives
+// element l of rows 0 .. 3.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(
+          (__attribute__((address_space(3))) const unsigned short*)p));
+}
+
+template <int D, int QT>
 struct MqSmem {
   unsigned short v[kWaves][kBlock * D];  // each wave's staged V block
   int kept[kWaves][64];                  // block-sparse: each wave's kept blocks of its window
-  float o[kWaves][D][kTileRows];
-  float m[kWaves][kTileRows];
-  float l[kWaves][kTileRows];
+  float o[kWaves][QT][D][kTileRows];
+  float m[kWaves][QT][kTileRows];
+  float l[kWaves][QT][kTileRows];
 };
 
+// query sub-tiles per wave: two for the dense D = 32 kernel (the latent cross-attention shape);
+// one elsewhere (the block-sparse skip decision is per block of 16 queries, and wider heads would
+// need too many registers)
 template <int D, bool SPARSE>
-// D = 32 (the latent cross-attention shape) is held to 7 waves per SIMD (72 registers, no spills):
-// nearly a whole launch of that workload is resident at once. (8 waves spill; measured slower.)
-__attribute__((amdgpu_waves_per_eu(D == 32 ? 7 : 1)))
+constexpr int mq_qt() { return (D == 32 && !SPARSE) ? 2 : 1; }
+
+template <int D, bool SPARSE>
+// D = 32 (the latent cross-attention shape) keeps several waves per SIMD: 7 with one sub-tile (72
+// registers), 4 with two (128); nearly a whole launch of that workload is then resident at once.
+__attribute__((amdgpu_waves_per_eu(D == 32 ? (mq_qt<D, SPARSE>() == 2 ? 4 : 7) : 1)))
 __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const DecodeArgs a) {
   constexpr int KC = D / 32;  // k-steps of the score product
   constexpr int NH = D / 16;  // dim tiles of the output product
-  __shared__ MqSmem<D> sm;
+  constexpr int QT = mq_qt<D, SPARSE>();
+  constexpr int TR = kTileRows * QT;  // query rows of a workgroup
+  __shared__ MqSmem<D, QT> sm;
   int tile, g, row;
   {
     // Workgroups are dealt to the 8 XCDs round-robin by index. All query tiles of one (row, KV
@@ -91,25 +114,27 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;  // query row inside the tile (S^T / O^T column)
+  const int col = lane & 15;  // query row inside a sub-tile (S^T / O^T column)
   const int grp = lane >> 4;  // key group: keys 4*grp .. 4*grp+3 of a block
   const int G = a.H_q / a.H_kv;
   const int R = a.n_q * G;  // query rows of this KV head
-  const int r = tile * kTileRows + col;
-  const bool row_ok = r < R;
-  const int qi = row_ok ? r / G : 0;
-  const int qh = g * G + (row_ok ? r % G : 0);
 
-  // Q^T fragments (B operand): query r, dims 32c + 8 grp .. +7; zero for rows past R
-  bf16x8_t qf[KC];
-  {
+  // Q^T fragments (B operand) of sub-tile u: query row tile * TR + 16 u + col, dims 32c + 8 grp
+  // .. +7; zero for rows past R
+  bf16x8_t qf[QT][KC];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int r = tile * TR + kTileRows * u + col;
+    const bool row_ok = r < R;
+    const int qi = row_ok ? r / G : 0;
+    const int qh = g * G + (row_ok ? r % G : 0);
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (size_t)row * a.q_row_stride +
                        ((size_t)qi * a.H_q + qh) * D + 8 * grp;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       u32x4_t x = {0u, 0u, 0u, 0u};
       if (row_ok) x = *reinterpret_cast<const u32x4_t*>(qp + 32 * c);
-      qf[c] = __builtin_bit_cast(bf16x8_t, x);
+      qf[u][c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
   const int* bt = a.block_tables + (size_t)row * a.bt_stride;
@@ -117,10 +142,17 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v);
   const float qk_scale = a.scale * kLog2e;
 
-  float m = kNegInf, l = 0.f;
-  f32x4_t o[NH];
+  float m[QT], l[QT];
+  f32x4_t o[QT][NH];
 #pragma unroll
-  for (int t = 0; t < NH; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < QT; ++u) {
+    m[u] = kNegInf;
+    l[u] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NH; ++t) o[u][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // this lane's address for the transposed V^T reads: key 4 grp + col / 4, dims 4 (col % 4) ..
+  const unsigned short* vtr = sm.v[wave] + (4 * grp + col / 4) * D + 4 * (col % 4);
 
   // K fragment (A operand): key col of the block, dims 32c + 8 grp; V: 16 contiguous bytes per lane
   // at lane * 8 elements (its transpose is read back from LDS)
@@ -148,65 +180,67 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     for (int c = 0; c < D / 32; ++c) vs[lane + 64 * c] = f.v[c];
     __builtin_amdgcn_wave_barrier();
 
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[c]), qf[c], s,
-                                                  0, 0, 0);
     const int key0 = blk * kBlock + 4 * grp;
     bool valid[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      valid[j] = !MASK || key0 + j < n;
-      if (MASK) s[j] = valid[j] ? s[j] : kNegInf;
-    }
-    // The running max of a query is shared by its four key groups (lanes col + 16 grp). It is
-    // raised, to the block maximum over all 16 keys, only when some lane's own keys beat it by
-    // more than kRescale; otherwise the block needs no cross-lane step at all.
-    const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (__builtin_amdgcn_ballot_w64(lm * qk_scale > m + kRescale) != 0) {
-      float bm = fmaxf(lm, swap_rows16(lm));
-      bm = fmaxf(bm, swap_halves32(bm));
-      const float bms = bm * qk_scale;
-      if (bms > m + kRescale) {
-        const float al = exp2_fast(m - bms);
-        l *= al;
+    for (int j = 0; j < 4; ++j) valid[j] = !MASK || key0 + j < n;
+    s16x4_t p_hi[QT], p_lo[QT];
 #pragma unroll
-        for (int t = 0; t < NH; ++t) o[t] *= al;
-        m = bms;
+    for (int u = 0; u < QT; ++u) {
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[c]),
+                                                    qf[u][c], s, 0, 0, 0);
+      if (MASK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[j] = valid[j] ? s[j] : kNegInf;
       }
-    }
-    s16x4_t p_hi, p_lo;
+      // The running max of a query is shared by its four key groups (lanes col + 16 grp). It is
+      // raised, to the block maximum over all 16 keys, only when some lane's own keys beat it by
+      // more than kRescale; otherwise the block needs no cross-lane step at all.
+      const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      if (__builtin_amdgcn_ballot_w64(lm * qk_scale > m[u] + kRescale) != 0) {
+        float bm = fmaxf(lm, swap_rows16(lm));
+        bm = fmaxf(bm, swap_halves32(bm));
+        const float bms = bm * qk_scale;
+        if (bms > m[u] + kRescale) {
+          const float al = exp2_fast(m[u] - bms);
+          l[u] *= al;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float p = exp2_fast(fmaf(s[j], qk_scale, -m));
-      if (MASK) p = valid[j] ? p : 0.f;  // a zero scale would make -inf * 0 a NaN
-      l += p;
-      const unsigned short h = bf16_bits(p);
-      p_hi[j] = (short)h;
-      p_lo[j] = (short)bf16_bits(p - bf16_value(h));
-    }
-    // V^T fragments: dim 16t + col, keys 4 grp .. +3 (masked keys read as zero)
-    const unsigned short* vsh = sm.v[wave];
-#pragma unroll
-    for (int t = 0; t < NH; ++t) {
-      s16x4_t vt;
+          for (int t = 0; t < NH; ++t) o[u][t] *= al;
+          m[u] = bms;
+        }
+      }
+      float p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const unsigned short x = vsh[(4 * grp + j) * D + 16 * t + col];
-        vt[j] = (!MASK || valid[j]) ? (short)x : (short)0;
+        p[j] = exp2_fast(fmaf(s[j], qk_scale, -m[u]));
+        if (MASK) p[j] = valid[j] ? p[j] : 0.f;  // a zero scale would make -inf * 0 a NaN
+        l[u] += p[j];
       }
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_hi, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_lo, o[t], 0, 0, 0);
+      unsigned h01, h23, l01, l23;
+      split_bf16x2(p[0], p[1], h01, l01);
+      split_bf16x2(p[2], p[3], h23, l23);
+      p_hi[u] = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
+      p_lo[u] = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
+    }
+    // V^T fragments: dim 16t + col, keys 4 grp .. +3 (masked keys read as zero), shared by the
+    // sub-tiles
+#pragma unroll
+    for (int t = 0; t < NH; ++t) {
+      s16x4_t vt = lds_read_tr16(vtr + 16 * t);
+      if (MASK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vt[j] = valid[j] ? vt[j] : (short)0;
+      }
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_hi[u], o[u][t], 0, 0, 0);
+        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_lo[u], o[u][t], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_wave_barrier();
-  };
-  // full blocks take the unmasked form; the row's partial last block the masked one
-  auto step = [&](const Frag& f, int blk, int n) {
-    if ((blk + 1) * kBlock <= n)
-      compute(std::false_type{}, f, blk, n);
-    else
-      compute(std::true_type{}, f, blk, n);
   };
 
   // This wave's blocks are wave, wave + 4, ...; they are taken in windows of up to 64, whose block
@@ -236,8 +270,10 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   bool keep0 = false;
   if constexpr (SPARSE) keep0 = window_keep(0, 64);
   const int n = clampi(a.kv_lens[row], 0, a.max_kv_len);
-  const int nblk = (n + kBlock - 1) / kBlock;
-  const int my = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  // The loop below takes only full blocks, so it runs the unmasked compute alone; the row's
+  // partial last block (if any) is done after it by the wave that owns it.
+  const int nfull = n / kBlock;
+  const int my = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
   for (int w0 = 0; w0 < my; w0 += 64) {
     const int cnt = my - w0 < 64 ? my - w0 : 64;
     if (w0 > 0) ids = window_ids(w0, cnt);
@@ -268,41 +304,57 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     load(f1, id_at(1));
     for (int j = 0; j < nv; j += 3) {
       load(f2, id_at(j + 2));
-      step(f0, blk_at(j), n);
+      compute(std::false_type{}, f0, blk_at(j), n);
       load(f0, id_at(j + 3));
-      if (j + 1 < nv) step(f1, blk_at(j + 1), n);
+      if (j + 1 < nv) compute(std::false_type{}, f1, blk_at(j + 1), n);
       load(f1, id_at(j + 4));
-      if (j + 2 < nv) step(f2, blk_at(j + 2), n);
+      if (j + 2 < nv) compute(std::false_type{}, f2, blk_at(j + 2), n);
+    }
+  }
+  if (n % kBlock != 0 && nfull % kWaves == wave) {
+    // the partial last block, block nfull of the row (block-sparse: only if its tile keeps it)
+    bool take = true;
+    if constexpr (SPARSE) take = nfull < a.mask_kv_blocks && keep_row[nfull] != 0;
+    if (take) {
+      const int pb = bt[nfull < a.bt_stride ? nfull : a.bt_stride - 1];
+      Frag f;
+      load(f, (unsigned)pb < (unsigned)a.num_blocks ? pb : 0);
+      compute(std::true_type{}, f, nfull, n);
     }
   }
 
   // merge the key groups' partial sums, then the waves through LDS
-  l += swap_rows16(l);
-  l += swap_halves32(l);
 #pragma unroll
-  for (int t = 0; t < NH; ++t)
+  for (int u = 0; u < QT; ++u) {
+    l[u] += swap_rows16(l[u]);
+    l[u] += swap_halves32(l[u]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.o[wave][16 * t + 4 * grp + j][col] = o[t][j];
-  if (grp == 0) {
-    sm.m[wave][col] = m;
-    sm.l[wave][col] = l;
+    for (int t = 0; t < NH; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.o[wave][u][16 * t + 4 * grp + j][col] = o[u][t][j];
+    if (grp == 0) {
+      sm.m[wave][u][col] = m[u];
+      sm.l[wave][u][col] = l[u];
+    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kTileRows * D; idx += 64 * kWaves) {
+  for (int idx = threadIdx.x; idx < TR * D; idx += 64 * kWaves) {
     const int rr = idx / D;
     const int d = idx % D;
-    const int rg = tile * kTileRows + rr;
+    const int u = rr / kTileRows;
+    const int c = rr % kTileRows;
+    const int rg = tile * TR + rr;
     if (rg >= R) continue;
     float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][rr]);
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][u][c]);
     float A = 0.f, L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.m[w][rr];
+      const float mw = sm.m[w][u][c];
       const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - mx);
-      A = fmaf(f, sm.o[w][d][rr], A);
-      L = fmaf(f, sm.l[w][rr], L);
+      A = fmaf(f, sm.o[w][u][d][c], A);
+      L = fmaf(f, sm.l[w][u][c], L);
     }
     const int i = rg / G;
     const int h = g * G + rg % G;
@@ -331,13 +383,22 @@ hipError_t launch_mq(const DecodeArgs& b, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// query rows per workgroup of the kernel instantiation a launch will use
+int mq_tile_rows(int D, bool sparse) {
+  if (sparse) return kTileRows * (D == 32 ? mq_qt<32, true>() : D == 64 ? mq_qt<64, true>()
+                                                                        : mq_qt<128, true>());
+  return kTileRows * (D == 32 ? mq_qt<32, false>() : D == 64 ? mq_qt<64, false>()
+                                                             : mq_qt<128, false>());
+}
+
 }  // namespace
 
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype != PA_BF16) return hipErrorNotSupported;
   const int rows = a.n_q * (a.H_q / a.H_kv);
   DecodeArgs b = a;
-  b.mq_tiles = (rows + kTileRows - 1) / kTileRows;
+  const int tr = mq_tile_rows(a.D, a.block_mask != nullptr);
+  b.mq_tiles = (rows + tr - 1) / tr;
   const long long wgs = (long long)b.mq_tiles * a.H_kv * a.batch;
   if (wgs * 64 * kWaves > 0xffffffffLL) return hipErrorInvalidValue;  // grid x holds < 2^32 threads
   const dim3 grid((unsigned)wgs);
