@@ -96,13 +96,14 @@ class PagedStep:
 class MultiQueryStep:
     """Multi-query paged attention: n_q shared queries per row over ragged per-row keys.
 
-    ``case`` provides: dtype, num_heads, head_dim, n_q, num_blocks, kv_lens, block_tables,
-    k_pool, v_pool, q ([n_q][H][dh], shared by all rows), scale."""
+    ``case`` provides: dtype, num_heads (query heads), head_dim, n_q, num_blocks, kv_lens,
+    block_tables, k_pool and v_pool ([num_blocks][H_kv][16][dh]: the pool's head count is taken from
+    them), q ([n_q][H][dh], shared by all rows), scale."""
 
     def __init__(self, case, device: str = "cuda", stream=None):
         self.case = case
         self.stream = stream
-        desc = B.make_desc("paged", case.dtype, case.num_heads, case.head_dim,
+        desc = B.make_desc("paged", case.dtype, int(case.k_pool.shape[1]), case.head_dim,
                            num_blocks=case.num_blocks)
         self.kv = B.alloc_pool(desc, device=device, stream=stream)
         self.kv.k.copy_(to_torch(case.k_pool, case.dtype))

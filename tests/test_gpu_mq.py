@@ -54,10 +54,13 @@ def _random_mq(seed, kv, n_q, H_q, H_kv, D):
                     seed=seed)
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
-def test_mq_random_ragged(D):
+@pytest.mark.parametrize("D,H_q,H_kv,n_q", [
+    (32, 4, 4, 37), (64, 4, 4, 37), (128, 4, 4, 37),
+    (32, 8, 2, 13),  # GQA: a workgroup's two 16-row sub-tiles mix queries and heads; 26 of 32 rows
+])
+def test_mq_random_ragged(D, H_q, H_kv, n_q):
     kv = [1, 15, 16, 17, 300, 821, 1333]
-    c = _random_mq(40 + D, kv, 37, 4, 4, D)
+    c = _random_mq(40 + D + H_kv, kv, n_q, H_q, H_kv, D)
     check_mq(c)
 
 

@@ -337,7 +337,7 @@ class MQCase:
     poison_block: int
     kv_lens: np.ndarray          # int32[B] spike tokens per sample
     block_tables: np.ndarray
-    k_pool: np.ndarray           # [num_blocks][H][16][dh] storage
+    k_pool: np.ndarray           # [num_blocks][H_kv][16][dh] storage
     v_pool: np.ndarray
     q: np.ndarray                # [n_q][H][dh] storage, shared by every sample
     scale: float
@@ -348,6 +348,11 @@ class MQCase:
     @property
     def batch(self) -> int:
         return len(self.kv_lens)
+
+    @property
+    def num_kv_heads(self) -> int:
+        """KV heads of the pool (num_heads query heads share them in consecutive groups)."""
+        return int(self.k_pool.shape[1])
 
     @property
     def max_kv_len(self) -> int:
