@@ -14,7 +14,16 @@
  *     write-up", kernels section, which pa_decode_attention_block_sparse also runs under a
  *     caller's boolean (query block x key block) mask (block-sparse cross-attention);
  *   - the lockstep form over right-padded per-row KV with one padding gap per row
- *     ("helexa PR #121", commit "slice 1": assemble_batch, batch_decode_mask).
+ *     ("helexa PR #121", commit "slice 1": assemble_batch, batch_decode_mask);
+ *   - the append with a per-head RMSNorm of the keys (and queries) before the rotation
+ *     (pa_append_kv_qk_norm; "NeuroGrid releases", v0.7.0, LFM2 notes);
+ *   - advancing a lockstep batch's positions and lengths on the device, so a recorded decode step
+ *     can be replayed token after token (pa_advance_lockstep; "NeuroGrid releases", v0.8.0
+ *     "CUDA Graphs");
+ *   - spike events straight into the pool: the three-table tokenizer fused with the K/V
+ *     projection (pa_tokenize_kv; "cortex-engine write-up", model and kernels sections), with
+ *     pa_pack_projection to put its weights into the matrix cores' fragment order (a layout of
+ *     this library).
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host). The caller owns every buffer; the library
