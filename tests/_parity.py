@@ -28,7 +28,7 @@ def assert_attention_close(got, ref, dtype, what="out"):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     both_inf = np.isneginf(got) & np.isneginf(ref)
     assert not np.isnan(got).any(), f"{what}: NaN in GPU result"
-    d = np.where(both_inf, 0.0, np.abs(got - ref))
+    d = np.abs(np.subtract(got, ref, out=np.zeros_like(got), where=~both_inf))
     max_tol, mean_tol = TOL[dtype]
     assert d.max() <= max_tol, f"{what}: max abs err {d.max():.3e} > {max_tol}"
     assert d.mean() <= mean_tol, f"{what}: mean abs err {d.mean():.3e} > {mean_tol}"
