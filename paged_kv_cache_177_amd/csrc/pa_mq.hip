@@ -142,15 +142,22 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v);
   const float qk_scale = a.scale * kLog2e;
 
-  float m[QT], l[QT];
-  f32x4_t o[QT][NH];
+  // Per sub-tile: running max m (log2 units), its raise threshold in raw score units thr = (m +
+  // kRescale) / qk_scale (recomputed only when m moves), the output accumulators, and the row sums
+  // of P, which the matrix cores accumulate with the output: a constant A operand whose first row
+  // is all ones turns P^T into sum_k P[q][k] in element 0 of lanes 0 .. 15 (query = lane).
+  float m[QT], thr[QT];
+  f32x4_t o[QT][NH], ls[QT];
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     m[u] = kNegInf;
-    l[u] = 0.f;
+    thr[u] = kNegInf;
+    ls[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NH; ++t) o[u][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const short one = col == 0 ? (short)0x3F80 : (short)0;  // bf16 1.0 in row 0 of the A operand
+  const s16x4_t ones = {one, one, one, one};
   // this lane's address for the transposed V^T reads: key 4 grp + col / 4, dims 4 (col % 4) ..
   const unsigned short* vtr = sm.v[wave] + (4 * grp + col / 4) * D + 4 * (col % 4);
 
@@ -200,16 +207,17 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
       // raised, to the block maximum over all 16 keys, only when some lane's own keys beat it by
       // more than kRescale; otherwise the block needs no cross-lane step at all.
       const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      if (__builtin_amdgcn_ballot_w64(lm * qk_scale > m[u] + kRescale) != 0) {
+      if (__builtin_amdgcn_ballot_w64(lm > thr[u]) != 0) {
         float bm = fmaxf(lm, swap_rows16(lm));
         bm = fmaxf(bm, swap_halves32(bm));
         const float bms = bm * qk_scale;
         if (bms > m[u] + kRescale) {
           const float al = exp2_fast(m[u] - bms);
-          l[u] *= al;
+          ls[u][0] *= al;  // the row sums live in element 0 (the other elements are zero)
 #pragma unroll
           for (int t = 0; t < NH; ++t) o[u][t] *= al;
           m[u] = bms;
+          thr[u] = (bms + kRescale) / qk_scale;
         }
       }
       float p[4];
@@ -217,13 +225,14 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
       for (int j = 0; j < 4; ++j) {
         p[j] = exp2_fast(fmaf(s[j], qk_scale, -m[u]));
         if (MASK) p[j] = valid[j] ? p[j] : 0.f;  // a zero scale would make -inf * 0 a NaN
-        l[u] += p[j];
       }
       unsigned h01, h23, l01, l23;
       split_bf16x2(p[0], p[1], h01, l01);
       split_bf16x2(p[2], p[3], h23, l23);
       p_hi[u] = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
       p_lo[u] = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
+      ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_hi[u], ls[u], 0, 0, 0);
+      ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_lo[u], ls[u], 0, 0, 0);
     }
     // V^T fragments: dim 16t + col, keys 4 grp .. +3 (masked keys read as zero), shared by the
     // sub-tiles
@@ -323,18 +332,16 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     }
   }
 
-  // merge the key groups' partial sums, then the waves through LDS
+  // merge the waves through LDS
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
-    l[u] += swap_rows16(l[u]);
-    l[u] += swap_halves32(l[u]);
 #pragma unroll
     for (int t = 0; t < NH; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.o[wave][u][16 * t + 4 * grp + j][col] = o[u][t][j];
     if (grp == 0) {
       sm.m[wave][u][col] = m[u];
-      sm.l[wave][u][col] = l[u];
+      sm.l[wave][u][col] = ls[u][0];
     }
   }
   __syncthreads();
