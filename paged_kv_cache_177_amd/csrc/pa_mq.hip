@@ -191,24 +191,40 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     bool valid[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) valid[j] = !MASK || key0 + j < n;
-    s16x4_t p_hi[QT], p_lo[QT];
+    // V^T fragments (dim 16t + col, keys 4 grp .. +3; masked keys read as zero), shared by the
+    // sub-tiles; read now so that the LDS latency hides behind the score products
+    s16x4_t vt[NH];
+#pragma unroll
+    for (int t = 0; t < NH; ++t) vt[t] = lds_read_tr16(vtr + 16 * t);
+    // The sub-tiles' chains run side by side (their products, maxima, exponentials and
+    // conversions interleave), with one branch for the rare raise of a running max.
+    f32x4_t s[QT];
+    float lm[QT];
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+      s[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[c]),
-                                                    qf[u][c], s, 0, 0, 0);
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[c]),
+                                                       qf[u][c], s[u], 0, 0, 0);
+    }
+    bool any_raise = false;
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
       if (MASK) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[j] = valid[j] ? s[j] : kNegInf;
+        for (int j = 0; j < 4; ++j) s[u][j] = valid[j] ? s[u][j] : kNegInf;
       }
       // The running max of a query is shared by its four key groups (lanes col + 16 grp). It is
       // raised, to the block maximum over all 16 keys, only when some lane's own keys beat it by
       // more than kRescale; otherwise the block needs no cross-lane step at all.
-      const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      if (__builtin_amdgcn_ballot_w64(lm > thr[u]) != 0) {
-        float bm = fmaxf(lm, swap_rows16(lm));
+      lm[u] = fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3]));
+      any_raise = any_raise || lm[u] > thr[u];
+    }
+    if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        float bm = fmaxf(lm[u], swap_rows16(lm[u]));
         bm = fmaxf(bm, swap_halves32(bm));
         const float bms = bm * qk_scale;
         if (bms > m[u] + kRescale) {
@@ -220,10 +236,14 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
           thr[u] = (bms + kRescale) / qk_scale;
         }
       }
+    }
+    s16x4_t p_hi[QT], p_lo[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
       float p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = exp2_fast(fmaf(s[j], qk_scale, -m[u]));
+        p[j] = exp2_fast(fmaf(s[u][j], qk_scale, -m[u]));
         if (MASK) p[j] = valid[j] ? p[j] : 0.f;  // a zero scale would make -inf * 0 a NaN
       }
       unsigned h01, h23, l01, l23;
@@ -231,22 +251,22 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
       split_bf16x2(p[2], p[3], h23, l23);
       p_hi[u] = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
       p_lo[u] = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
+    }
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
       ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_hi[u], ls[u], 0, 0, 0);
       ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_lo[u], ls[u], 0, 0, 0);
     }
-    // V^T fragments: dim 16t + col, keys 4 grp .. +3 (masked keys read as zero), shared by the
-    // sub-tiles
 #pragma unroll
     for (int t = 0; t < NH; ++t) {
-      s16x4_t vt = lds_read_tr16(vtr + 16 * t);
       if (MASK) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vt[j] = valid[j] ? vt[j] : (short)0;
+        for (int j = 0; j < 4; ++j) vt[t][j] = valid[j] ? vt[t][j] : (short)0;
       }
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_hi[u], o[u][t], 0, 0, 0);
-        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p_lo[u], o[u][t], 0, 0, 0);
+        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_hi[u], o[u][t], 0, 0, 0);
+        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_lo[u], o[u][t], 0, 0, 0);
       }
     }
     __builtin_amdgcn_wave_barrier();
