@@ -244,6 +244,55 @@ def main_mq(args):
     print(json.dumps(out), flush=True)
 
 
+def read_ceiling_gbs(gib: int = 2, reps: int = 10, per_cu=(1.5, 2, 3, 4, 8)):
+    """The practical HBM read bandwidth on this GPU: the read probe (libpa_probe.so, a measuring
+    instrument outside the attention library) streams a `gib` GiB device buffer; for each grid
+    size in `per_cu` (workgroups per CU) the median of `reps` launches timed with HIP events, and
+    the best of those medians is returned with its grid. (The probe's rate depends on the grid:
+    on MI355X 1.5 workgroups per CU read fastest, ~7.3 TB/s.)"""
+    import ctypes
+
+    import torch
+
+    from paged_kv_cache_177_amd.build import PROBE_LIB
+
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: run the build first")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.pa_probe_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grids = [int(cus * m) for m in per_cu]
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def launch(grid):
+        rc = lib.pa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                               ctypes.c_void_p(sink.data_ptr()), grid,
+                               ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"pa_probe_read failed with HIP error {rc}")
+
+    best = (0.0, 0)
+    for grid in grids:
+        for _ in range(3):
+            launch(grid)
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(grid)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        best = max(best, (nbytes / (statistics.median(ts) * 1e-3) / 1e9, grid))
+    del buf, sink
+    return best
+
+
 def main_tokenize(args):
     """Fused spike tokenizer + K/V projection into the paged pool: 16 rows of raw spike events
     (neuron, time bin, value), one pa_tokenize_kv call per step. The kernel's floor is HBM: every
@@ -630,6 +679,9 @@ def main():
         fl.append(a.elapsed_time(b))
     del flush
 
+    # extra: the practical read ceiling of this GPU, measured in the same run
+    ceiling, ceiling_grid = read_ceiling_gbs()
+
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash(*DECODE_SOURCES)
     traffic = read_traffic(src_hash) if args.workload == "b128" else None
@@ -672,6 +724,9 @@ def main():
                    "decode_us_flushed_median": round(statistics.median(fl) * 1e3, 2),
                    "kv_gbs_flushed": round(kv_bytes / (statistics.median(fl) * 1e-3) / 1e9, 1),
                    "traffic_bytes_per_call": traffic,
+                   "hbm_read_ceiling_gbs": round(ceiling, 1),
+                   "hbm_read_ceiling_grid": ceiling_grid,
+                   "decode_pct_of_read_ceiling": round(100 * achieved / ceiling, 1),
                    "append_us": round(append_us, 2),
                    "append_qk_norm_us": round(append_norm_us, 2),
                    "source_hash": src_hash},

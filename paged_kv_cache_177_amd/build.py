@@ -1,7 +1,8 @@
 """Build libpa.so (gfx950) in-tree with hipcc.
 
 ``python -m paged_kv_cache_177_amd.build`` compiles every source under ``csrc/`` into
-``paged_kv_cache_177_amd/lib/libpa.so``. It always recompiles.
+``paged_kv_cache_177_amd/lib/libpa.so``, and the benchmark's read-ceiling probe under ``probe/``
+into ``lib/libpa_probe.so``. It always recompiles.
 """
 
 from __future__ import annotations
@@ -18,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libpa.so")
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(LIB_DIR, "libpa_probe.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -51,20 +54,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def probe_sources():
+    return sorted(os.path.join(PROBE_DIR, f) for f in os.listdir(PROBE_DIR) if f.endswith(".hip"))
+
+
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    srcs = sources()
+    psrcs = probe_sources()
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
