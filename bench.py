@@ -408,8 +408,10 @@ def cpu_baseline_tokenize(c, E: int, budget_s: float = 10.0, max_reps: int = 200
 
 def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64):
     """The paged B=16 step captured as a graph (append + decode + merge + on-device advance) and
-    replayed. Block tables are filled for ``ahead`` positions past each row's start; positions are
-    reset (outside the timed replays) every ``reset_every`` warm-up replays."""
+    replayed, and the same four calls issued one by one (the eager counterpart of the graph).
+    Block tables are filled for ``ahead`` positions past each row's start; positions are reset
+    (outside the timed steps) every ``reset_every`` warm-up steps. Returns ((wall, events) of the
+    replays, (wall, events) of the eager steps), in microseconds per step."""
     import numpy as np
     import torch
 
@@ -456,18 +458,24 @@ def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64
     g.capture()
     count = [0]
 
-    def replay():
-        if count[0] == reset_every:
-            reset()
-            count[0] = 0
-        g.replay()
-        count[0] += 1
+    def every(fn):
+        def run():
+            if count[0] == reset_every:
+                reset()
+                count[0] = 0
+            fn()
+            count[0] += 1
+        return run
 
-    # timed() warms up (with resets), then times args.steps replays from a fresh reset
+    # timed() warms up (with resets), then times args.steps steps from a fresh reset
     def timed_from_reset(fn):
+        count[0] = 0
+        reset()
         return timed(fn, before_timed=lambda: (reset(), count.__setitem__(0, 0)))
 
-    return timed_from_reset(replay)
+    graph = timed_from_reset(every(g.replay))
+    eager = timed_from_reset(every(g.step))
+    return graph, eager
 
 
 def append_timings(r, case, stream, calls: int = 50):
@@ -570,7 +578,7 @@ def main_b16(args):
 
     wall_paged, ev_paged = timed(paged.step)
     wall_padded, ev_padded = timed(padded_step)
-    wall_graph, ev_graph = graph_step_timing(args, plan, timed)
+    (wall_graph, ev_graph), (wall_g_eager, ev_g_eager) = graph_step_timing(args, plan, timed)
     out_line = {
         "metric": "B=16 lockstep decode step us (append + decode + merge), paged, bf16",
         "value": round(ev_paged, 2),
@@ -601,6 +609,8 @@ def main_b16(args):
                    "padded_us_per_step_wall": round(wall_padded, 2),
                    "graph_us_per_step_events": round(ev_graph, 2),
                    "graph_us_per_step_wall": round(wall_graph, 2),
+                   "graph_eager_us_per_step_events": round(ev_g_eager, 2),
+                   "graph_eager_us_per_step_wall": round(wall_g_eager, 2),
                    "source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:
