@@ -143,15 +143,17 @@ def rms_norm_head_f32(x32: np.ndarray, w32: np.ndarray, eps: float) -> np.ndarra
     w = np.asarray(w32, dtype=np.float32)
     D = x.shape[-1]
     half = D // 2
-    with np.errstate(over="ignore"):  # fp32 squares may overflow to inf, as they do on the GPU
+    # IEEE fp32 throughout, as on the GPU: squares may overflow to inf, and with eps = 0 an all-zero
+    # head gives 1 / sqrt(0) = inf and then 0 * inf = NaN; numpy's warnings for those are muted
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
         s = np.add(np.multiply(x[..., :half], x[..., :half]),
                    np.multiply(x[..., half:], x[..., half:]))
         while s.shape[-1] > 1:
             s = np.add(s[..., 0::2], s[..., 1::2])
-    ss = s[..., 0]
-    ms = np.divide(ss, np.float32(D))
-    r = np.divide(np.float32(1.0), np.sqrt(np.add(ms, np.float32(eps))))
-    return np.multiply(np.multiply(x, r[..., None]), w).astype(np.float32)
+        ss = s[..., 0]
+        ms = np.divide(ss, np.float32(D))
+        r = np.divide(np.float32(1.0), np.sqrt(np.add(ms, np.float32(eps))))
+        return np.multiply(np.multiply(x, r[..., None]), w).astype(np.float32)
 
 
 # --------------------------------------------------------------------------------------------
