@@ -311,3 +311,26 @@ def test_pack_projection_argument_errors():
     assert call(i=48) == B.PA_ERR_SHAPE            # in_features not a multiple of 32
     assert call(w=FAKE + 8) == B.PA_ERR_SHAPE      # misaligned
     assert call(pk=FAKE + 1024) == B.PA_ERR_SHAPE  # overlaps w (256 x 256 x 2 bytes)
+
+
+def test_read_probe_library_loads_and_rejects_bad_arguments():
+    """The benchmark's read-ceiling probe (a separate library, not part of the attention ABI)
+    exports what include/pa_probe.h declares and checks its arguments before launching."""
+    from paged_kv_cache_177_amd.build import PROBE_LIB
+
+    text = open(os.path.join(ROOT, "include", "pa_probe.h")).read()
+    declared = re.findall(r"^int\s+(\w+)\s*\(", text, flags=re.M)
+    assert declared == ["pa_probe_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    assert "pa_probe_read" in {line.split()[-1] for line in out.splitlines() if " T " in line}
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.c_int, ctypes.c_void_p]
+    lib.pa_probe_read.restype = ctypes.c_int
+    sink = FAKE + (1 << 20)
+    assert lib.pa_probe_read(None, 1024, sink, 4, None) != 0         # null buffer
+    assert lib.pa_probe_read(FAKE, 1000, sink, 4, None) != 0         # not a multiple of 16
+    assert lib.pa_probe_read(FAKE + 8, 1024, sink, 4, None) != 0     # misaligned
+    assert lib.pa_probe_read(FAKE, 1024, None, 4, None) != 0         # null sink
+    assert lib.pa_probe_read(FAKE, 1024, sink, 0, None) != 0         # empty grid
