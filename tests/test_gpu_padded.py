@@ -80,6 +80,15 @@ def test_ragged_padded_with_splits(D, G, dtype):
     run_and_check_padded(W.padded_from_paged(c, seq_cap=3100))
 
 
+def test_padded_large_grid():
+    """64 rows x 8 KV heads, up to 2 chunks each: a grid of a thousand workgroups, several per
+    compute unit, with gaps of every width."""
+    rng = np.random.default_rng(35)
+    n = np.concatenate([[0, 1, 1023, 1024, 2046], rng.integers(1, 2047, 59)])
+    c = W.make_paged_case("padded-wide", 35, n, 32, 8, 64, "bf16")
+    run_and_check_padded(W.padded_from_paged(c, seq_cap=2100))
+
+
 def test_uniform_lengths_have_no_gap():
     c = W.make_paged_case("uniform", 32, [300] * 6, 32, 8, 64, "bf16")
     pc = W.padded_from_paged(c)
