@@ -576,8 +576,18 @@ def main_b16(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e6 / args.steps, a.elapsed_time(b) * 1e3 / args.steps
 
-    wall_paged, ev_paged = timed(paged.step)
-    wall_padded, ev_padded = timed(padded_step)
+    def padded_fused_step():
+        B.pa_append_decode_attention_padded(L.kv.pool, pos, dest, k_new, v_new, q_in, q_rot,
+                                            pc.num_q_heads, gs, ge, pc.kv_cols, pc.batch,
+                                            pc.scale, workspace=ws if need else None, out=out,
+                                            lse=lse)
+
+    # the step as one fused call (append folded into the decode launch) + the merge, and as the
+    # separate calls: the same bits
+    wall_paged, ev_paged = timed(paged.fused_step)
+    wall_padded, ev_padded = timed(padded_fused_step)
+    wall_paged_sep, ev_paged_sep = timed(paged.step)
+    wall_padded_sep, ev_padded_sep = timed(padded_step)
     (wall_graph, ev_graph), (wall_g_eager, ev_g_eager) = graph_step_timing(args, plan, timed)
     out_line = {
         "metric": "B=16 lockstep decode step us (append + decode + merge), paged, bf16",
@@ -597,7 +607,9 @@ def main_b16(args):
                                 f"H_q=32, H_kv=8, D=64, 16-token blocks, RoPE theta 1e6, seed "
                                 f"{plan.seed}"),
                    "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
-                   "step": "append_kv (k, v, q rotation) + decode + lse merge"},
+                   "step": ("append_kv (k, v, q rotation) + decode + lse merge: "
+                            "pa_append_decode_attention (the append folded into the decode "
+                            "launch) + the merge kernel")},
         "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (ev_paged * 1e-6) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kv_bytes / (ev_paged * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -607,6 +619,10 @@ def main_b16(args):
                    "paged_us_per_step_wall": round(wall_paged, 2),
                    "padded_us_per_step_events": round(ev_padded, 2),
                    "padded_us_per_step_wall": round(wall_padded, 2),
+                   "paged_separate_calls_us_per_step_events": round(ev_paged_sep, 2),
+                   "paged_separate_calls_us_per_step_wall": round(wall_paged_sep, 2),
+                   "padded_separate_calls_us_per_step_events": round(ev_padded_sep, 2),
+                   "padded_separate_calls_us_per_step_wall": round(wall_padded_sep, 2),
                    "graph_us_per_step_events": round(ev_graph, 2),
                    "graph_us_per_step_wall": round(wall_graph, 2),
                    "graph_eager_us_per_step_events": round(ev_g_eager, 2),
@@ -652,25 +668,34 @@ def main():
     done = 0
     while done < args.warmup or time.perf_counter() - t_w < 1.0:
         for _ in range(10):
-            r.append()
-            r.decode()
+            r.fused_step()
         done += 10
         torch.cuda.synchronize()
 
-    # The timed steps: back to back with nothing in between (a pair of timing events around
-    # every call would add a few microseconds of GPU time to each step).
-    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ea.record(stream)
-    for _ in range(args.steps):
+    def timed_steps(step):
+        # back to back with nothing in between (a pair of timing events around every call would
+        # add a few microseconds of GPU time to each step)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ea.record(stream)
+        for _ in range(args.steps):
+            step()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, ea.elapsed_time(eb) / args.steps
+
+    def separate_step():
         r.append()
         r.decode()
-    eb.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    step_ev_ms = ea.elapsed_time(eb) / args.steps
+
+    # The timed steps: one pa_append_decode_attention call each (the append folded into the
+    # decode launch, then the merge). The same step as separate append and decode calls (the
+    # same bits) is timed next, for comparison.
+    ms_per_step, step_ev_ms = timed_steps(r.fused_step)
+    for _ in range(args.warmup):
+        separate_step()
+    sep_ms, sep_ev_ms = timed_steps(separate_step)
 
     # The decode call's duration for the roofline: the same number of decode calls back to back
     # between one pair of events, on the stream they run on.
@@ -737,7 +762,9 @@ def main():
                                 f"H_kv={case.num_kv_heads}, D={case.head_dim}, 16-token blocks, "
                                 f"shuffled pool of {case.num_blocks} blocks, seed {case.seed}"),
                    "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
-                   "step": "append_kv + decode + lse merge"},
+                   "step": ("append_kv + decode + lse merge: pa_append_decode_attention (the "
+                            "append folded into the decode launch where the split grid runs) + "
+                            "the merge kernel")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
@@ -750,6 +777,8 @@ def main():
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "detail": {"us_per_step": round(ms_per_step * 1e3, 2),
                    "us_per_step_events": round(step_ev_ms * 1e3, 2),
+                   "us_per_step_separate_calls": round(sep_ms * 1e3, 2),
+                   "us_per_step_separate_calls_events": round(sep_ev_ms * 1e3, 2),
                    "pct_hbm_peak_step": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9
                                               / HBM_PEAK_GBS, 2),
                    "decode_us_single_call_median": round(statistics.median(dec_ms) * 1e3, 2),

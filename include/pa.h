@@ -276,6 +276,52 @@ pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
                                      size_t* workspace_needed /* host */, float* out, float* lse,
                                      hipStream_t stream);
 
+/* Append and decode in one call: pa_append_kv followed by pa_decode_attention on the rotated
+ * queries, with the append folded into the decode's split kernel (helexa PR #121, commit
+ * "slice 1": per-row positions, keys stored post-RoPE; "NeuroGrid releases", v0.7.0: block-table
+ * slots; v0.6.0: the decode). One launch instead of two.
+ *
+ * Row b's new key k_new[b] and value v_new[b] ([H_kv][D], pool dtype) are stored at token index
+ * dest[b] (NULL: positions[b]) exactly as pa_append_kv stores them (same rotation, rounding,
+ * clamping), and the row then attends over its first kv_lens[b] tokens, which see the new token
+ * when dest[b] < kv_lens[b]. q: [batch][num_q_heads][D], pool dtype, the queries before rotation;
+ * on a pool with RoPE tables they are rotated at positions[b] exactly as pa_append_kv rotates
+ * them and the result is stored to q_out (same shape, required), otherwise q is used as given and
+ * copied to q_out when q_out is not NULL. q_out must not overlap q. Results (pool bits, q_out,
+ * out, lse) equal those of the two separate calls bit for bit.
+ * Where the decode would run its persistent kernel (rows long enough for many splits), the call
+ * runs the append kernel and then the decode: same results, two launches.
+ * Workspace, out, lse, kv_lens, max_kv_len and block tables as for pa_decode_attention (n_q = 1).
+ * Preconditions (clamped, not checked): as for both calls; in addition no row reads another row's
+ * destination slot (destination slots are private to their rows).
+ * Errors: those of pa_decode_attention with n_q = 1 and q_row_stride = num_q_heads * D; then
+ * PA_ERR_NULL (positions, k_new, v_new; q_out on a pool with RoPE tables); PA_ERR_SHAPE (k_new,
+ * v_new or q_out not 16-byte aligned, q_out overlapping q). */
+pa_status pa_append_decode_attention(const pa_pool* pool, const int32_t* block_tables,
+                                     int32_t bt_stride, const int32_t* positions,
+                                     const int32_t* dest, const void* k_new, const void* v_new,
+                                     const void* q, void* q_out, int32_t num_q_heads,
+                                     const int32_t* kv_lens, int32_t batch, int32_t max_kv_len,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     size_t* workspace_needed /* host */, float* out, float* lse,
+                                     hipStream_t stream);
+
+/* The lockstep form of pa_append_decode_attention over a PA_PADDED pool: pa_append_kv (new token
+ * at column dest[b], NULL: positions[b]) followed by pa_decode_attention_padded, in one launch.
+ * Arguments and results as for those two calls and pa_append_decode_attention; a destination
+ * column inside the row's gap or at or past kv_cols is written but not attended to.
+ * Errors: those of pa_decode_attention_padded, then those of pa_append_decode_attention's
+ * append half. */
+pa_status pa_append_decode_attention_padded(const pa_pool* padded_pool, const int32_t* positions,
+                                            const int32_t* dest, const void* k_new,
+                                            const void* v_new, const void* q, void* q_out,
+                                            int32_t num_q_heads, const int32_t* gap_start,
+                                            const int32_t* gap_end, int32_t kv_cols,
+                                            int32_t batch, float scale, void* workspace,
+                                            size_t workspace_bytes,
+                                            size_t* workspace_needed /* host */, float* out,
+                                            float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ PA_PAGED, PA_PADDED = 0, 1
 
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
            "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm",
-           "pa_tokenize_kv", "pa_pack_projection")
+           "pa_tokenize_kv", "pa_pack_projection", "pa_append_decode_attention",
+           "pa_append_decode_attention_padded")
 
 
 class PaError(RuntimeError):
@@ -81,6 +82,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_pack_projection.argtypes = [_P, _I32, _I32, _P, _P]
     lib.pa_append_kv_qk_norm.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _P, _P, _P, _P, _P,
                                          _I32, _I32, _P, _P, ctypes.c_float, _P]
+    lib.pa_append_decode_attention.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _P, _P, _P,
+                                               _P, _P, _I32, _P, _I32, _I32, ctypes.c_float, _P,
+                                               ctypes.c_size_t, _SIZE_P, _P, _P, _P]
+    lib.pa_append_decode_attention_padded.argtypes = [ctypes.POINTER(Pool), _P, _P, _P, _P, _P,
+                                                      _P, _I32, _P, _P, _I32, _I32,
+                                                      ctypes.c_float, _P, ctypes.c_size_t,
+                                                      _SIZE_P, _P, _P, _P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -236,6 +244,44 @@ def pa_decode_attention_padded(pool: Pool, q, num_q_heads: int, batch: int, gap_
                                         ctypes.byref(need) if query_workspace else None, _ptr(out),
                                         _ptr(lse), _stream(stream))
     _check("pa_decode_attention_padded", st)
+    return need.value
+
+
+def pa_append_decode_attention(pool: Pool, block_tables, bt_stride: int, positions, dest, k_new,
+                               v_new, q, q_out, num_q_heads: int, kv_lens, batch: int,
+                               max_kv_len: int, scale: float, workspace=None, out=None, lse=None,
+                               stream=None, query_workspace: bool = False) -> int:
+    """Append + decode in one call; with ``query_workspace`` only return the workspace bytes."""
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_append_decode_attention(ctypes.byref(pool), _ptr(block_tables), bt_stride,
+                                        _ptr(positions), _ptr(dest), _ptr(k_new), _ptr(v_new),
+                                        _ptr(q), _ptr(q_out), num_q_heads, _ptr(kv_lens), batch,
+                                        max_kv_len, ctypes.c_float(scale), _ptr(workspace),
+                                        ws_bytes, ctypes.byref(need) if query_workspace else None,
+                                        _ptr(out), _ptr(lse), _stream(stream))
+    _check("pa_append_decode_attention", st)
+    return need.value
+
+
+def pa_append_decode_attention_padded(pool: Pool, positions, dest, k_new, v_new, q, q_out,
+                                      num_q_heads: int, gap_start, gap_end, kv_cols: int,
+                                      batch: int, scale: float, workspace=None, out=None,
+                                      lse=None, stream=None,
+                                      query_workspace: bool = False) -> int:
+    """Lockstep append + padded decode in one call."""
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_append_decode_attention_padded(ctypes.byref(pool), _ptr(positions), _ptr(dest),
+                                               _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(q_out),
+                                               num_q_heads, _ptr(gap_start), _ptr(gap_end),
+                                               kv_cols, batch, ctypes.c_float(scale),
+                                               _ptr(workspace), ws_bytes,
+                                               ctypes.byref(need) if query_workspace else None,
+                                               _ptr(out), _ptr(lse), _stream(stream))
+    _check("pa_append_decode_attention_padded", st)
     return need.value
 
 

@@ -119,11 +119,13 @@ extern "C" pa_status pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size
 
 namespace {
 
-pa_status append_common(const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
-                        const int32_t* positions, const int32_t* dest, const void* k_new,
-                        const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
-                        int32_t batch, const float* q_norm_w, const float* k_norm_w,
-                        float norm_eps, hipStream_t stream) {
+// Validation and argument pack of an append (pa_append_kv, pa_append_kv_qk_norm, and the
+// fused-append call where it appends first).
+pa_status append_prepare(const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
+                         const int32_t* positions, const int32_t* dest, const void* k_new,
+                         const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
+                         int32_t batch, const float* q_norm_w, const float* k_norm_w,
+                         float norm_eps, pa::AppendArgs* out) {
   pa_status s = check_pool(pool);
   if (s != PA_OK) return s;
   const pa_pool_desc& d = pool->desc;
@@ -135,9 +137,8 @@ pa_status append_common(const pa_pool* pool, const int32_t* block_tables, int32_
   if (d.layout == PA_PADDED && batch > d.batch_cap) return PA_ERR_SHAPE;
   if (q_in != nullptr && (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0))
     return PA_ERR_SHAPE;
-  if (batch == 0) return PA_OK;
 
-  pa::AppendArgs a;
+  pa::AppendArgs& a = *out;
   std::memset(&a, 0, sizeof(a));
   a.layout = d.layout;
   a.dtype = d.dtype;
@@ -164,6 +165,19 @@ pa_status append_common(const pa_pool* pool, const int32_t* block_tables, int32_
   a.q_norm_w = q_norm_w;
   a.k_norm_w = k_norm_w;
   a.norm_eps = norm_eps;
+  return PA_OK;
+}
+
+pa_status append_common(const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
+                        const int32_t* positions, const int32_t* dest, const void* k_new,
+                        const void* v_new, const void* q_in, void* q_out, int32_t num_q_heads,
+                        int32_t batch, const float* q_norm_w, const float* k_norm_w,
+                        float norm_eps, hipStream_t stream) {
+  pa::AppendArgs a;
+  const pa_status s = append_prepare(pool, block_tables, bt_stride, positions, dest, k_new, v_new,
+                                     q_in, q_out, num_q_heads, batch, q_norm_w, k_norm_w,
+                                     norm_eps, &a);
+  if (s != PA_OK || batch == 0) return s;
   return map_hip(pa::launch_append(a, stream));
 }
 
@@ -192,13 +206,15 @@ extern "C" pa_status pa_append_kv_qk_norm(const pa_pool* pool, const int32_t* bl
                        num_q_heads, batch, q_norm_weight, k_norm_weight, eps, stream);
 }
 
-extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
-                                         int32_t n_q, int32_t num_q_heads,
-                                         const int32_t* block_tables, int32_t bt_stride,
-                                         const int32_t* kv_lens, int32_t batch,
-                                         int32_t max_kv_len, float scale, void* workspace,
-                                         size_t workspace_bytes, size_t* workspace_needed,
-                                         float* out, float* lse, hipStream_t stream) {
+namespace {
+
+// Validation and argument pack of the paged decode (pa_decode_attention and the fused-append
+// call); *need is the workspace the call requires.
+pa_status paged_decode_prepare(const pa_pool* pool, const void* q, int64_t q_row_stride,
+                               int32_t n_q, int32_t num_q_heads, const int32_t* block_tables,
+                               int32_t bt_stride, const int32_t* kv_lens, int32_t batch,
+                               int32_t max_kv_len, float scale, float* out, float* lse,
+                               pa::DecodeArgs* a, size_t* need) {
   pa_status s = check_pool(pool);
   if (s != PA_OK) return s;
   const pa_pool_desc& d = pool->desc;
@@ -218,42 +234,115 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
 
   const int s_max = n_q == 1 ? pa::num_splits(max_kv_len, pa::chunk_tokens(d.head_dim)) : 1;
   if (s_max > pa::kMaxGridYZ) return PA_ERR_SHAPE;
-  const size_t need = pa::decode_workspace_bytes(batch, n_q, num_q_heads, d.head_dim, s_max);
+  *need = pa::decode_workspace_bytes(batch, n_q, num_q_heads, d.head_dim, s_max);
+
+  std::memset(a, 0, sizeof(*a));
+  a->layout = PA_PAGED;
+  a->dtype = d.dtype;
+  a->H_kv = d.num_kv_heads;
+  a->H_q = num_q_heads;
+  a->D = d.head_dim;
+  a->n_q = n_q;
+  a->num_blocks = d.num_blocks;
+  a->k = pool->k;
+  a->v = pool->v;
+  a->q = q;
+  a->q_row_stride = q_row_stride;
+  a->block_tables = block_tables;
+  a->bt_stride = bt_stride;
+  a->kv_lens = kv_lens;
+  a->batch = batch;
+  a->max_kv_len = max_kv_len;
+  a->s_max = s_max;
+  a->scale = scale;
+  a->out = out;
+  a->lse = lse;
+  return PA_OK;
+}
+
+// Validation and argument pack of the right-padded lockstep decode.
+pa_status padded_decode_prepare(const pa_pool* padded_pool, const void* q, int32_t num_q_heads,
+                                int32_t batch, const int32_t* gap_start, const int32_t* gap_end,
+                                int32_t kv_cols, float scale, float* out, float* lse,
+                                pa::DecodeArgs* a, size_t* need) {
+  pa_status s = check_pool(padded_pool);
+  if (s != PA_OK) return s;
+  const pa_pool_desc& d = padded_pool->desc;
+  if (d.layout != PA_PADDED) return PA_ERR_SHAPE;
+  if (q == nullptr || gap_start == nullptr || gap_end == nullptr || out == nullptr)
+    return PA_ERR_NULL;
+  if (batch < 0 || batch > d.batch_cap || batch > pa::kMaxGridYZ || kv_cols < 0 ||
+      kv_cols > d.seq_cap)
+    return PA_ERR_SHAPE;
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int G = num_q_heads / d.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  const long long row_stride = (long long)num_q_heads * d.head_dim;
+  if (!q_aligned(q, row_stride, d.dtype)) return PA_ERR_SHAPE;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
+
+  const int s_max = pa::num_splits(kv_cols, pa::chunk_tokens(d.head_dim));
+  if (s_max > pa::kMaxGridYZ) return PA_ERR_SHAPE;
+  *need = pa::decode_workspace_bytes(batch, 1, num_q_heads, d.head_dim, s_max);
+
+  std::memset(a, 0, sizeof(*a));
+  a->layout = PA_PADDED;
+  a->dtype = d.dtype;
+  a->H_kv = d.num_kv_heads;
+  a->H_q = num_q_heads;
+  a->D = d.head_dim;
+  a->n_q = 1;
+  a->seq_cap = d.seq_cap;
+  a->k = padded_pool->k;
+  a->v = padded_pool->v;
+  a->q = q;
+  a->q_row_stride = row_stride;
+  a->gap_start = gap_start;
+  a->gap_end = gap_end;
+  a->kv_cols = kv_cols;
+  a->batch = batch;
+  a->max_kv_len = kv_cols;
+  a->s_max = s_max;
+  a->scale = scale;
+  a->out = out;
+  a->lse = lse;
+  return PA_OK;
+}
+
+// The workspace query, the capacity check and the launches of a prepared decode (the split
+// kernel or the multi-query kernel, then the log-sum-exp merge when rows can split).
+pa_status run_decode(pa::DecodeArgs& a, size_t need, void* workspace, size_t workspace_bytes,
+                     size_t* workspace_needed, hipStream_t stream) {
   if (workspace_needed != nullptr) {
     *workspace_needed = need;
     return PA_OK;
   }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_CAPACITY;
-  if (batch == 0) return PA_OK;
-
-  pa::DecodeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.layout = PA_PAGED;
-  a.dtype = d.dtype;
-  a.H_kv = d.num_kv_heads;
-  a.H_q = num_q_heads;
-  a.D = d.head_dim;
-  a.n_q = n_q;
-  a.num_blocks = d.num_blocks;
-  a.k = pool->k;
-  a.v = pool->v;
-  a.q = q;
-  a.q_row_stride = q_row_stride;
-  a.block_tables = block_tables;
-  a.bt_stride = bt_stride;
-  a.kv_lens = kv_lens;
-  a.batch = batch;
-  a.max_kv_len = max_kv_len;
-  a.s_max = s_max;
-  a.scale = scale;
-  a.out = out;
-  a.lse = lse;
+  if (a.batch == 0) return PA_OK;
   if (need > 0)
-    pa::carve_workspace(workspace, batch, n_q, num_q_heads, d.head_dim, s_max, &a.counter,
-                        &a.part_o, &a.part_lse);
-  hipError_t e = n_q == 1 ? pa::launch_decode_vector(a, stream) : pa::launch_decode_mq(a, stream);
-  if (e == hipSuccess && s_max > 1) e = pa::launch_lse_reduce(a, stream);
+    pa::carve_workspace(workspace, a.batch, a.n_q, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
+                        &a.part_lse);
+  hipError_t e = a.n_q == 1 ? pa::launch_decode_vector(a, stream) : pa::launch_decode_mq(a, stream);
+  if (e == hipSuccess && a.s_max > 1) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
+                                         int32_t n_q, int32_t num_q_heads,
+                                         const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* kv_lens, int32_t batch,
+                                         int32_t max_kv_len, float scale, void* workspace,
+                                         size_t workspace_bytes, size_t* workspace_needed,
+                                         float* out, float* lse, hipStream_t stream) {
+  pa::DecodeArgs a;
+  size_t need = 0;
+  const pa_status s = paged_decode_prepare(pool, q, q_row_stride, n_q, num_q_heads, block_tables,
+                                           bt_stride, kv_lens, batch, max_kv_len, scale, out, lse,
+                                           &a, &need);
+  if (s != PA_OK) return s;
+  return run_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
 }
 
 extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_table,
@@ -393,58 +482,119 @@ extern "C" pa_status pa_decode_attention_padded(const pa_pool* padded_pool, cons
                                                 int32_t kv_cols, float scale, void* workspace,
                                                 size_t workspace_bytes, size_t* workspace_needed,
                                                 float* out, float* lse, hipStream_t stream) {
-  pa_status s = check_pool(padded_pool);
+  pa::DecodeArgs a;
+  size_t need = 0;
+  const pa_status s = padded_decode_prepare(padded_pool, q, num_q_heads, batch, gap_start,
+                                            gap_end, kv_cols, scale, out, lse, &a, &need);
   if (s != PA_OK) return s;
-  const pa_pool_desc& d = padded_pool->desc;
-  if (d.layout != PA_PADDED) return PA_ERR_SHAPE;
-  if (q == nullptr || gap_start == nullptr || gap_end == nullptr || out == nullptr)
-    return PA_ERR_NULL;
-  if (batch < 0 || batch > d.batch_cap || batch > pa::kMaxGridYZ || kv_cols < 0 ||
-      kv_cols > d.seq_cap)
-    return PA_ERR_SHAPE;
-  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0) return PA_ERR_SHAPE;
-  const int G = num_q_heads / d.num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
-  const long long row_stride = (long long)num_q_heads * d.head_dim;
-  if (!q_aligned(q, row_stride, d.dtype)) return PA_ERR_SHAPE;
-  if (!(scale >= 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
+  return run_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
+}
 
-  const int s_max = pa::num_splits(kv_cols, pa::chunk_tokens(d.head_dim));
-  if (s_max > pa::kMaxGridYZ) return PA_ERR_SHAPE;
-  const size_t need = pa::decode_workspace_bytes(batch, 1, num_q_heads, d.head_dim, s_max);
+namespace {
+
+// The append half of the fused calls: checks, and the fields of the decode's argument pack.
+pa_status fused_prepare(const pa_pool* pool, const int32_t* positions, const int32_t* dest,
+                        const void* k_new, const void* v_new, const void* q, void* q_out,
+                        pa::DecodeArgs* a) {
+  const pa_pool_desc& d = pool->desc;
+  if (positions == nullptr || k_new == nullptr || v_new == nullptr) return PA_ERR_NULL;
+  const bool rope = d.rope_max_pos > 0;
+  if (rope && q_out == nullptr) return PA_ERR_NULL;
+  const long long q_stride = (long long)a->H_q * d.head_dim;
+  const long long kv_stride = (long long)d.num_kv_heads * d.head_dim;
+  if (!q_aligned(k_new, kv_stride, d.dtype) || !q_aligned(v_new, kv_stride, d.dtype))
+    return PA_ERR_SHAPE;
+  if (q_out != nullptr) {
+    if (!q_aligned(q_out, q_stride, d.dtype)) return PA_ERR_SHAPE;
+    // every workgroup reads q while split 0 writes q_out: they must not overlap
+    const uintptr_t bytes = (uintptr_t)a->batch * (uintptr_t)q_stride * elem_size(d.dtype);
+    const uintptr_t x = (uintptr_t)q, y = (uintptr_t)q_out;
+    if (bytes > 0 && (x < y ? y - x : x - y) < bytes) return PA_ERR_SHAPE;
+  }
+  a->positions = positions;
+  a->dest = dest;
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->q_out = q_out;
+  a->cos = rope ? pool->rope_cos : nullptr;
+  a->sin = rope ? pool->rope_sin : nullptr;
+  a->rope_max_pos = d.rope_max_pos;
+  return PA_OK;
+}
+
+// One launch of the split kernel that appends and decodes, then the merge. Where the persistent
+// kernel would run (it has no fused append) the append kernel goes first and the plain decode of
+// the rotated queries follows: the same results either way.
+pa_status run_append_decode(const pa_pool* pool, pa::DecodeArgs& a, size_t need, void* workspace,
+                            size_t workspace_bytes, size_t* workspace_needed,
+                            hipStream_t stream) {
   if (workspace_needed != nullptr) {
     *workspace_needed = need;
     return PA_OK;
   }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_CAPACITY;
-  if (batch == 0) return PA_OK;
-
-  pa::DecodeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.layout = PA_PADDED;
-  a.dtype = d.dtype;
-  a.H_kv = d.num_kv_heads;
-  a.H_q = num_q_heads;
-  a.D = d.head_dim;
-  a.n_q = 1;
-  a.seq_cap = d.seq_cap;
-  a.k = padded_pool->k;
-  a.v = padded_pool->v;
-  a.q = q;
-  a.q_row_stride = row_stride;
-  a.gap_start = gap_start;
-  a.gap_end = gap_end;
-  a.kv_cols = kv_cols;
-  a.batch = batch;
-  a.max_kv_len = kv_cols;
-  a.s_max = s_max;
-  a.scale = scale;
-  a.out = out;
-  a.lse = lse;
+  if (a.batch == 0) return PA_OK;
   if (need > 0)
-    pa::carve_workspace(workspace, batch, 1, num_q_heads, d.head_dim, s_max, &a.counter,
-                        &a.part_o, &a.part_lse);
-  hipError_t e = pa::launch_decode_vector(a, stream);
-  if (e == hipSuccess && s_max > 1) e = pa::launch_lse_reduce(a, stream);
+    pa::carve_workspace(workspace, a.batch, 1, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
+                        &a.part_lse);
+  pa::DecodeArgs plain = a;
+  plain.positions = nullptr;
+  plain.dest = nullptr;
+  plain.k_new = nullptr;
+  plain.v_new = nullptr;
+  plain.q_out = nullptr;
+  plain.cos = plain.sin = nullptr;
+  hipError_t e;
+  if (pa::decode_vector_is_persistent(plain)) {
+    pa::AppendArgs ap;
+    const pa_status s = append_prepare(pool, a.block_tables, a.bt_stride, a.positions, a.dest,
+                                       a.k_new, a.v_new, a.q_out != nullptr ? a.q : nullptr,
+                                       a.q_out, a.H_q, a.batch, nullptr, nullptr, 0.f, &ap);
+    if (s != PA_OK) return s;
+    e = pa::launch_append(ap, stream);
+    if (a.cos != nullptr) plain.q = a.q_out;  // the rotated queries, same row stride
+    if (e == hipSuccess) e = pa::launch_decode_vector(plain, stream);
+  } else {
+    e = pa::launch_decode_vector(a, stream);
+  }
+  if (e == hipSuccess && a.s_max > 1) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_append_decode_attention(
+    const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride,
+    const int32_t* positions, const int32_t* dest, const void* k_new, const void* v_new,
+    const void* q, void* q_out, int32_t num_q_heads, const int32_t* kv_lens, int32_t batch,
+    int32_t max_kv_len, float scale, void* workspace, size_t workspace_bytes,
+    size_t* workspace_needed, float* out, float* lse, hipStream_t stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  pa::DecodeArgs a;
+  size_t need = 0;
+  s = paged_decode_prepare(pool, q, (int64_t)num_q_heads * pool->desc.head_dim, 1, num_q_heads,
+                           block_tables, bt_stride, kv_lens, batch, max_kv_len, scale, out, lse,
+                           &a, &need);
+  if (s != PA_OK) return s;
+  s = fused_prepare(pool, positions, dest, k_new, v_new, q, q_out, &a);
+  if (s != PA_OK) return s;
+  return run_append_decode(pool, a, need, workspace, workspace_bytes, workspace_needed, stream);
+}
+
+extern "C" pa_status pa_append_decode_attention_padded(
+    const pa_pool* padded_pool, const int32_t* positions, const int32_t* dest, const void* k_new,
+    const void* v_new, const void* q, void* q_out, int32_t num_q_heads,
+    const int32_t* gap_start, const int32_t* gap_end, int32_t kv_cols, int32_t batch,
+    float scale, void* workspace, size_t workspace_bytes, size_t* workspace_needed, float* out,
+    float* lse, hipStream_t stream) {
+  pa::DecodeArgs a;
+  size_t need = 0;
+  pa_status s = padded_decode_prepare(padded_pool, q, num_q_heads, batch, gap_start, gap_end,
+                                      kv_cols, scale, out, lse, &a, &need);
+  if (s != PA_OK) return s;
+  s = fused_prepare(padded_pool, positions, dest, k_new, v_new, q, q_out, &a);
+  if (s != PA_OK) return s;
+  return run_append_decode(padded_pool, a, need, workspace, workspace_bytes, workspace_needed,
+                           stream);
 }

@@ -132,6 +132,15 @@ struct Vec8<__bf16> {
     o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
     o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z); o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
   }
+  // round each to bf16 (to nearest even), as the append kernel stores
+  __device__ __forceinline__ void from_f32(const float* o) {
+    auto pk = [](float lo, float hi) {
+      return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo)) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi)) << 16);
+    };
+    w = make_uint4(pk(o[0], o[1]), pk(o[2], o[3]), pk(o[4], o[5]), pk(o[6], o[7]));
+  }
+  __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<uint4*>(p) = w; }
   // <a, b> over the 8 elements: one chain of packed dot products, fp32 accumulation of the
   // exact bf16 products
   __device__ __forceinline__ float dot(const Vec8& b) const {
@@ -164,6 +173,14 @@ struct Vec8<float> {
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void to_f32(float* o) const {
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+  __device__ __forceinline__ void from_f32(const float* o) {
+    a = make_float4(o[0], o[1], o[2], o[3]);
+    b = make_float4(o[4], o[5], o[6], o[7]);
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<float4*>(p)[0] = a;
+    reinterpret_cast<float4*>(p)[1] = b;
   }
   __device__ __forceinline__ float dot(const Vec8& o) const {
     float s0 = a.x * o.a.x;
@@ -268,6 +285,120 @@ struct Worker {
   }
   __device__ __forceinline__ int clamp_id(int v) const {
     return (unsigned)v < (unsigned)a.num_blocks ? v : 0;
+  }
+
+  // ---- append fused into the split kernel ----
+  // This lane's 8 cos/sin entries at table row pos: lane c holds dims 8c .. 8c+7, whose
+  // rotate-half pair index is (8c + e) mod D/2.
+  __device__ __forceinline__ void load_trig(int pos, float* cs, float* sn) const {
+    const size_t i0 = (size_t)pos * (D / 2) + (size_t)((c & (LPT / 2 - 1)) * 8);
+    const float4* cp = reinterpret_cast<const float4*>(a.cos + i0);
+    const float4* sp = reinterpret_cast<const float4*>(a.sin + i0);
+    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+    cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w;
+    cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
+    sn[0] = s0.x; sn[1] = s0.y; sn[2] = s0.z; sn[3] = s0.w;
+    sn[4] = s1.x; sn[5] = s1.y; sn[6] = s1.z; sn[7] = s1.w;
+  }
+  // The lane holding dims 8c + D/2 (or 8c - D/2): c ^ (LPT / 2).
+  __device__ __forceinline__ int partner() const { return c ^ (LPT / 2); }
+
+  // Rotate-half RoPE of this lane's 8 dims `own`, paired with the partner lane's 8 dims: the low
+  // half gives own*cos - partner*sin, the high half own*cos + partner*sin, every product and sum
+  // a separate fp32 operation, rounded to T -- the append kernel's arithmetic, bit for bit.
+  __device__ __forceinline__ void rope8(const Vec8<T>& own, const Vec8<T>& other, const float* cs,
+                                        const float* sn, Vec8<T>& out) const {
+#pragma clang fp contract(off)
+    float x[8], y[8], r[8];
+    own.to_f32(x);
+    other.to_f32(y);
+    const bool low = c < LPT / 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p0 = x[e] * cs[e];
+      const float p1 = y[e] * sn[e];
+      r[e] = low ? p0 - p1 : p0 + p1;
+    }
+    out.from_f32(r);
+  }
+
+  // This lane's piece of row `row`'s new key (and its partner half, for the rotation) and
+  // value for KV head g: dims 8c .. 8c+7 (read by every wave, since any may store them).
+  __device__ __forceinline__ void fused_load(int row, int g, Vec8<T>& kx, Vec8<T>& kp,
+                                             Vec8<T>& vx) const {
+    const size_t src = ((size_t)row * a.H_kv + g) * D;
+    const T* kn = reinterpret_cast<const T*>(a.k_new) + src;
+    kx.load_cached(kn + c * 8);
+    vx.load_cached(reinterpret_cast<const T*>(a.v_new) + src + c * 8);
+    if (a.cos != nullptr) kp.load_cached(kn + partner() * 8);
+  }
+
+  // The new token's index t (dest, or positions when dest is NULL) clamped as the append kernel
+  // clamps it: into the row's block table (paged) or the row's columns (padded).
+  __device__ __forceinline__ int fused_index(int row) const {
+    const int t = a.dest != nullptr ? a.dest[row] : a.positions[row];
+    return PADDED ? clampi(t, 0, a.seq_cap - 1) : clampi(t, 0, a.bt_stride * kBlock - 1);
+  }
+
+  // Whether this wave stores row ch.row's new token t: only the workgroup whose chunk holds it
+  // (the last chunk when it lies outside the row's n valid tokens) and, in it, only the wave
+  // whose blocks include it. *first: the token's block is this wave's first block.
+  __device__ __forceinline__ bool fused_target(const Chunk& ch, int n, int t, bool* first) const {
+    int v = t;  // the token's index among the row's valid tokens, or -1 (a padding column)
+    if constexpr (PADDED)
+      v = t < ch.gap_s ? t : (t >= ch.gap_s + ch.gap_shift ? t - ch.gap_shift : -1);
+    const bool inside = v >= 0 && v < n;
+    const int owner = inside ? v / chunk_tokens(D) : ch.ns - 1;
+    const int b = inside ? (v - ch.tok0) / kBlock : 0;  // the token's block within the chunk
+    *first = inside && b == wave;
+    return ch.split == owner && b % kWaves == wave;
+  }
+
+  // Store the new key (rotated at pos when the pool has RoPE tables) and value of token t, KV
+  // head ch.g, at the slot the append kernel stores it to. Later loads of this wave see the
+  // stores (a wave's memory operations stay in order); no other workgroup of the launch reads
+  // the slot.
+  __device__ __forceinline__ void fused_store(Vec8<T> kx, const Vec8<T>& kp, const Vec8<T>& vx,
+                                              const Chunk& ch, int t, int pos) const {
+    size_t slot;  // element offset of [.., ch.g, t's slot or column, 0]
+    if constexpr (PADDED) {
+      slot = (((size_t)ch.row * a.H_kv + ch.g) * a.seq_cap + t) * D;
+    } else {
+      int blk = a.block_tables[(size_t)ch.row * a.bt_stride + t / kBlock];
+      blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+      slot = (((size_t)blk * a.H_kv + ch.g) * kBlock + (t % kBlock)) * D;
+    }
+    if (lane >= LPT) return;
+    if (a.cos != nullptr) {
+      float cs[8], sn[8];
+      load_trig(pos, cs, sn);
+      rope8(kx, kp, cs, sn, kx);
+    }
+    kx.store(reinterpret_cast<T*>(const_cast<void*>(a.k)) + slot + c * 8);
+    vx.store(reinterpret_cast<T*>(const_cast<void*>(a.v)) + slot + c * 8);
+  }
+
+  // Rotate the queries at pos (pools with RoPE tables; each head's partner half is read here)
+  // and, in split 0, store them to q_out.
+  __device__ __forceinline__ void fused_queries(const Chunk& ch, int pos) {
+    if (a.cos != nullptr) {
+      float cs[8], sn[8];
+      load_trig(pos, cs, sn);
+      const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)ch.row * a.q_row_stride +
+                    (size_t)ch.g * G * D + partner() * 8;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        Vec8<T> other;
+        other.load_cached(qp + (size_t)h * D);
+        rope8(q[h], other, cs, sn, q[h]);
+      }
+    }
+    if (a.q_out != nullptr && ch.split == 0 && wave == 0 && lane < LPT) {
+      T* qo = reinterpret_cast<T*>(a.q_out) + ((size_t)ch.row * a.H_q + (size_t)ch.g * G) * D +
+              c * 8;
+#pragma unroll
+      for (int h = 0; h < G; ++h) q[h].store(qo + (size_t)h * D);
+    }
   }
 
   __device__ __forceinline__ void reset() {
@@ -488,14 +619,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   // issued before the row length is known, so their latency overlaps the length load
   int ids = w.load_ids(row, split * chunk);
   w.load_q(w.q, row, g);
+  // fused append: the row's position (a table row, clamped) for the rotations, and this lane's
+  // piece of the new key and value
+  const bool fused = a.k_new != nullptr;
+  const int pos = fused && a.cos != nullptr ? clampi(a.positions[row], 0, a.rope_max_pos - 1) : 0;
+  const int t_new = fused ? w.fused_index(row) : 0;
+  Vec8<T> kx, kp, vx;
+  if (fused && w.lane < W::LPT) w.fused_load(row, g, kx, kp, vx);
   int gap_s, gap_shift;
   const int n = row_valid<PADDED>(a, row, &gap_s, &gap_shift);
   const Chunk ch = make_chunk(row, g, split, n, gap_s, gap_shift, chunk);
   if (split >= ch.ns) return;
+  bool first = false;
+  const bool stores = fused && w.fused_target(ch, n, t_new, &first);
+  if (stores && first) {
+    // the token's block is the next load of this wave: its stores complete first
+    w.fused_store(kx, kp, vx, ch, t_new, pos);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   w.reset();
   typename W::Frag f0, f1;
   const int my = w.my_blocks(ch);
   if (my > 0) w.load_block(f0, ch, ids, w.blk_of(0));
+  if (stores && !first) w.fused_store(kx, kp, vx, ch, t_new, pos);
+  if (fused) w.fused_queries(ch, pos);  // while the first block is in flight
   w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
@@ -885,6 +1032,17 @@ int resident_workgroups(const void* kernel, size_t lds) {
   return per_cu * cus;
 }
 
+}  // namespace
+
+bool decode_vector_is_persistent(const DecodeArgs& a) {
+  if (a.k_new != nullptr) return false;
+  if (!(PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows))
+    return false;
+  return PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits;
+}
+
+namespace {
+
 template <typename T, int D, int G, bool PADDED>
 hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   const long long items = (long long)a.batch * a.H_kv * a.s_max;
@@ -893,7 +1051,7 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   // kernel takes over. With few splits per row the split grid starts faster (a workgroup needs
   // no row scan before its first loads) and runs more waves per SIMD. Both cut rows into the
   // same chunks: their results are identical.
-  if (PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows) {
+  if (decode_vector_is_persistent(a)) {  // never with a fused append
     auto kern = decode_persistent_kernel<T, D, G, PADDED>;
     const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
     if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits)) {

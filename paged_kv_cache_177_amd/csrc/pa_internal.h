@@ -81,6 +81,18 @@ struct DecodeArgs {
   // block-sparse multi-query path: keep flags [batch][ceil(n_q / 16)][mask_kv_blocks], or NULL
   const uint8_t* block_mask;
   int mask_kv_blocks;
+  // append fused into the split kernel (k_new NULL: none). Row b's new key and value go to token
+  // index dest[b] (dest NULL: positions[b]) exactly as append_kernel stores them; q holds the
+  // un-rotated queries, rotated at positions[b] in registers when cos is set, and the workgroups
+  // of split 0 store them to q_out (NULL: not stored).
+  const int32_t* positions;
+  const int32_t* dest;
+  const void* k_new;
+  const void* v_new;
+  void* q_out;
+  const float* cos;  // [rope_max_pos][D/2], or NULL
+  const float* sin;
+  int rope_max_pos;
 };
 
 // Workspace of a decode call (0 bytes when no row can split):
@@ -135,6 +147,9 @@ hipError_t launch_pack_projection(const void* w, void* packed, int out_features,
 hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
                           hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1
+// Whether launch_decode_vector takes the persistent kernel for these arguments (that kernel has
+// no fused append: the caller appends first).
+bool decode_vector_is_persistent(const DecodeArgs& a);
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream);      // n_q > 1
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
 

@@ -92,6 +92,15 @@ class PagedStep:
         self.append()
         self.decode()
 
+    def fused_step(self, with_lse: bool = True):
+        """append + decode in one call (pa_append_decode_attention): the same results as step()."""
+        B.pa_append_decode_attention(self.kv.pool, self.block_tables, self.bt_stride,
+                                     self.positions, self.dest, self.k_new, self.v_new, self.q,
+                                     self.q_rot, self.H_q, self.kv_lens, self.batch,
+                                     self.max_kv_len, self.case.scale, workspace=self.workspace,
+                                     out=self.out, lse=self.lse if with_lse else None,
+                                     stream=self.stream)
+
 
 class MultiQueryStep:
     """Multi-query paged attention: n_q shared queries per row over ragged per-row keys.
@@ -161,6 +170,24 @@ class PaddedLockstep:
         B.pa_decode_attention_padded(self.kv.pool, q, self.H_q, batch, gap_start, gap_end, kv_cols,
                                      scale, workspace=self._ws if need > 0 else None, out=out,
                                      lse=lse, stream=self.stream)
+        return out, lse
+
+    def append_decode(self, positions, dest, k_new, v_new, q, q_out, gap_start, gap_end,
+                      kv_cols: int, scale: float):
+        """append + decode in one call (pa_append_decode_attention_padded): the same results as
+        append() followed by decode() on the rotated queries."""
+        batch = q.shape[0]
+        out = torch.empty((batch, self.H_q, self.D), dtype=torch.float32, device=self.device)
+        lse = torch.empty((batch, self.H_q), dtype=torch.float32, device=self.device)
+        need = B.pa_append_decode_attention_padded(self.kv.pool, positions, dest, k_new, v_new, q,
+                                                   q_out, self.H_q, gap_start, gap_end, kv_cols,
+                                                   batch, scale, out=out, query_workspace=True)
+        if need > 0 and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        B.pa_append_decode_attention_padded(self.kv.pool, positions, dest, k_new, v_new, q, q_out,
+                                            self.H_q, gap_start, gap_end, kv_cols, batch, scale,
+                                            workspace=self._ws if need > 0 else None, out=out,
+                                            lse=lse, stream=self.stream)
         return out, lse
 
 

@@ -1,0 +1,169 @@
+"""GPU parity of the fused append + decode calls (pa_append_decode_attention and its padded form):
+the same bits as pa_append_kv followed by the decode (pool, rotated queries, out, lse), and the
+oracle's values."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from paged_kv_cache_177_amd import binding as B
+from paged_kv_cache_177_amd.runner import PaddedLockstep, PagedStep, to_numpy, to_torch
+
+from _parity import assert_attention_close, bits, log, oracle_append
+
+pytestmark = pytest.mark.gpu
+
+
+def fused_vs_separate(case, rows=None):
+    """Run the case through both paths on two fresh pools; assert identical bits everywhere and
+    check the fused result against the oracle (on ``rows``, default all)."""
+    log(f"[fused] case={case.name} B={case.batch} D={case.head_dim} "
+        f"G={case.num_q_heads // case.num_kv_heads} dtype={case.dtype} max_kv={case.max_kv_len} "
+        f"rope={case.rope_max_pos > 0}")
+    sep = PagedStep(case)
+    sep.step()
+    fus = PagedStep(case)
+    fus.fused_step()
+    torch.cuda.synchronize()
+    dt = case.dtype
+    for name in ("k", "v"):
+        np.testing.assert_array_equal(bits(to_numpy(getattr(fus.kv, name), dt), dt),
+                                      bits(to_numpy(getattr(sep.kv, name), dt), dt))
+    if fus.rope:
+        np.testing.assert_array_equal(bits(to_numpy(fus.q_rot, dt), dt),
+                                      bits(to_numpy(sep.q_rot, dt), dt))
+    np.testing.assert_array_equal(fus.out.cpu().numpy(), sep.out.cpu().numpy())
+    np.testing.assert_array_equal(fus.lse.cpu().numpy(), sep.lse.cpu().numpy())
+    # and the oracle
+    k2, v2, q_used, _, _ = oracle_append(case)
+    np.testing.assert_array_equal(bits(to_numpy(fus.kv.k, dt), dt), bits(k2, dt))
+    rows = np.arange(case.batch) if rows is None else np.asarray(rows)
+    o_ref, l_ref = O.decode_paged(k2, v2, dt, case.block_tables[rows], case.kv_lens[rows],
+                                  q_used[rows], case.scale)
+    mx, mean = assert_attention_close(fus.out.cpu().numpy()[rows], o_ref[:, 0], dt, "out")
+    assert_attention_close(fus.lse.cpu().numpy()[rows], l_ref[:, 0], dt, "lse")
+    log(f"[fused] ok case={case.name} max_err={mx:.2e} mean_err={mean:.2e}")
+    return fus
+
+
+@pytest.mark.parametrize("reading", ["A", "B"])
+def test_fused_tiny(reading):
+    fused_vs_separate(W.tiny(reading))
+
+
+@pytest.mark.parametrize("D,G,dtype,theta", [(64, 4, "bf16", 0.0), (64, 4, "bf16", 1e6),
+                                             (64, 1, "bf16", 1e4), (64, 8, "bf16", 0.0),
+                                             (128, 4, "bf16", 1e4), (128, 2, "f32", 1e4),
+                                             (32, 2, "bf16", 1e4), (32, 4, "f32", 0.0)])
+def test_fused_ragged(D, G, dtype, theta):
+    """Rows from empty to several chunks; the new token lands in every kind of chunk and block."""
+    rng = np.random.default_rng(400 + D + G)
+    n = np.concatenate([[0, 1, 15, 16, 17, 1023, 1024, 1025, 2047, 3000],
+                        rng.integers(1, 2600, 6)])
+    case = W.make_paged_case(f"fused-D{D}-G{G}-{dtype}-t{theta:g}", 41, n, 2 * G, 2, D, dtype,
+                             rope_theta=theta)
+    fused_vs_separate(case)
+
+
+def test_fused_b128_full_size():
+    """The B=128 step at full size (no RoPE table): 12 rows against the oracle, all bits against
+    the separate calls."""
+    c = W.b128()
+    order = np.argsort(c.kv_lens)
+    rows = np.unique(np.concatenate([order[:3], order[-3:], order[::29]]))
+    fused_vs_separate(c, rows=rows)
+
+
+def test_fused_long_rows_take_the_two_launch_form():
+    """Rows of 70 chunks: the decode runs its persistent kernel, which has no fused append, so the
+    call appends first; the results are still those of the separate calls."""
+    case = W.make_paged_case("fused-long", 43, [99, 20 * 1024 + 7, 70 * 1024 - 9], 8, 2, 64,
+                             "bf16", rope_theta=1e4)
+    fused_vs_separate(case)
+
+
+def test_fused_destination_outside_the_row():
+    """A destination at or past kv_len is still written (as pa_append_kv writes it) but not
+    attended to; a row with kv_len 0 attends to nothing."""
+    case = W.make_paged_case("fused-dest", 44, [40, 300, 1500, 0], 8, 2, 64, "bf16",
+                             rope_theta=1e4)
+    case.kv_lens = case.kv_lens.copy()
+    case.kv_lens[0] = 20        # the new token (index 40) lies past the attended tokens
+    case.dest = case.dest.copy()
+    case.dest[1] = 200          # overwrites a token inside the row, away from its end
+    case.kv_lens[1] = 300       # (the slot at index 300 keeps its poison: not attended to)
+    case.kv_lens[3] = 0
+    fus = fused_vs_separate(case)
+    assert torch.all(fus.out[3] == 0) and torch.all(torch.isneginf(fus.lse[3]))
+
+
+def _padded_inputs(pc, dev="cuda"):
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    return (d(pc.positions), d(pc.dest), to_torch(pc.k_new, pc.dtype).to(dev),
+            to_torch(pc.v_new, pc.dtype).to(dev), to_torch(pc.q, pc.dtype).to(dev),
+            d(pc.prefix_lens.astype(np.int32)), d(np.full(pc.batch, pc.padded_len, np.int32)))
+
+
+def _padded_pool(pc):
+    L = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
+                       pc.seq_cap, rope_theta=pc.rope_theta, rope_max_pos=pc.rope_max_pos)
+    L.kv.k.copy_(to_torch(pc.k_pad, pc.dtype))
+    L.kv.v.copy_(to_torch(pc.v_pad, pc.dtype))
+    return L
+
+
+@pytest.mark.parametrize("D,dtype,theta", [(64, "bf16", 1e6), (128, "bf16", 0.0),
+                                           (64, "f32", 1e4)])
+def test_fused_padded(D, dtype, theta):
+    """The lockstep form: gaps of every width; fused and separate give the same bits, and the
+    oracle agrees."""
+    c = W.make_paged_case(f"fused-padded-D{D}-{dtype}", 45, [0, 5, 16, 700, 1023, 1500, 2100],
+                          8, 2, D, dtype, rope_theta=theta)
+    pc = W.padded_from_paged(c, seq_cap=2200)
+    log(f"[fused-padded] case={pc.name} B={pc.batch} D={D} dtype={dtype} theta={theta}")
+    pos, dest, k_new, v_new, q, gs, ge = _padded_inputs(pc)
+    rope = pc.rope_max_pos > 0
+    Ls = _padded_pool(pc)
+    q_rot_s = torch.empty_like(q) if rope else None
+    Ls.append(pos, dest, k_new, v_new, q if rope else None, q_rot_s)
+    out_s, lse_s = Ls.decode(q_rot_s if rope else q, gs, ge, pc.kv_cols, pc.scale)
+    Lf = _padded_pool(pc)
+    q_rot_f = torch.empty_like(q) if rope else None
+    out_f, lse_f = Lf.append_decode(pos, dest, k_new, v_new, q, q_rot_f, gs, ge, pc.kv_cols,
+                                    pc.scale)
+    torch.cuda.synchronize()
+    for name in ("k", "v"):
+        np.testing.assert_array_equal(bits(to_numpy(getattr(Lf.kv, name), dtype), dtype),
+                                      bits(to_numpy(getattr(Ls.kv, name), dtype), dtype))
+    if rope:
+        np.testing.assert_array_equal(bits(to_numpy(q_rot_f, dtype), dtype),
+                                      bits(to_numpy(q_rot_s, dtype), dtype))
+    np.testing.assert_array_equal(out_f.cpu().numpy(), out_s.cpu().numpy())
+    np.testing.assert_array_equal(lse_f.cpu().numpy(), lse_s.cpu().numpy())
+    cos = sin = None
+    if rope:
+        cos, sin = O.rope_tables(pc.rope_theta, pc.head_dim, pc.rope_max_pos)
+    k2, v2, q2 = O.append_kv(pc.k_pad, pc.v_pad, dtype, "padded", None, pc.positions, pc.dest,
+                             pc.k_new, pc.v_new, cos, sin, q_in=pc.q if rope else None)
+    o_ref, l_ref = O.decode_padded(k2, v2, dtype, pc.prefix_lens.astype(np.int32),
+                                   np.full(pc.batch, pc.padded_len, np.int32), pc.kv_cols,
+                                   q2 if rope else pc.q, pc.scale)
+    mx, mean = assert_attention_close(out_f.cpu().numpy(), o_ref[:, 0], dtype, "out")
+    assert_attention_close(lse_f.cpu().numpy(), l_ref[:, 0], dtype, "lse")
+    log(f"[fused-padded] ok max_err={mx:.2e} mean_err={mean:.2e}")
+
+
+def test_fused_copies_queries_without_rope_table():
+    """No RoPE table: q is used as given and copied to q_out when one is passed."""
+    case = W.make_paged_case("fused-copy", 46, [3, 70, 900], 8, 2, 64, "bf16")
+    r = PagedStep(case)
+    q_out = torch.full_like(r.q, float("nan"))
+    B.pa_append_decode_attention(r.kv.pool, r.block_tables, r.bt_stride, r.positions, r.dest,
+                                 r.k_new, r.v_new, r.q, q_out, r.H_q, r.kv_lens, r.batch,
+                                 r.max_kv_len, case.scale, workspace=r.workspace, out=r.out,
+                                 lse=r.lse)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(to_numpy(q_out, "bf16"), "bf16"),
+                                  bits(to_numpy(r.q, "bf16"), "bf16"))
