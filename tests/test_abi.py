@@ -334,3 +334,81 @@ def test_read_probe_library_loads_and_rejects_bad_arguments():
     assert lib.pa_probe_read(FAKE + 8, 1024, sink, 4, None) != 0     # misaligned
     assert lib.pa_probe_read(FAKE, 1024, None, 4, None) != 0         # null sink
     assert lib.pa_probe_read(FAKE, 1024, sink, 0, None) != 0         # empty grid
+
+
+# ---- append + decode in one call ---------------------------------------------------------------
+Q_BYTES = 4 * 32 * 64 * 2  # q of the default arguments below: batch 4, 32 heads, D 64, bf16
+
+
+def _fused(p, **kw):
+    a = dict(block_tables=FAKE, bt_stride=64, positions=FAKE, dest=None, k_new=FAKE, v_new=FAKE,
+             q=FAKE, q_out=FAKE + Q_BYTES, num_q_heads=32, kv_lens=FAKE, batch=4,
+             max_kv_len=1000, scale=0.125, out=FAKE)
+    a.update(kw)
+    return B.pa_append_decode_attention(p, a["block_tables"], a["bt_stride"], a["positions"],
+                                        a["dest"], a["k_new"], a["v_new"], a["q"], a["q_out"],
+                                        a["num_q_heads"], a["kv_lens"], a["batch"],
+                                        a["max_kv_len"], a["scale"], out=a["out"],
+                                        query_workspace=True)
+
+
+def test_fused_workspace_is_the_decodes():
+    p = _fake_pool()
+    for max_kv in (1000, 8193):
+        need = _fused(p, bt_stride=513, batch=128, max_kv_len=max_kv, q_out=None)
+        ref = B.pa_decode_attention(p, FAKE, 32 * 64, 1, 32, FAKE, 513, FAKE, 128, max_kv, 0.125,
+                                    out=FAKE, query_workspace=True)
+        assert need == ref
+    # without RoPE tables q_out may be left out; with them it is required
+    assert _fused(_fake_pool(), q_out=None) == 0
+    assert _fused(_fake_pool(rope_max_pos=2000, rope_theta=1e4)) == 0
+
+
+@pytest.mark.parametrize("kw,rope,status", [
+    (dict(positions=None), False, B.PA_ERR_NULL),
+    (dict(k_new=None), False, B.PA_ERR_NULL),
+    (dict(v_new=None), False, B.PA_ERR_NULL),
+    (dict(q_out=None), True, B.PA_ERR_NULL),              # rotated queries need a home
+    (dict(q=None), False, B.PA_ERR_NULL),                 # the decode's own checks come first
+    (dict(num_q_heads=24), False, B.PA_ERR_UNSUPPORTED),
+    (dict(k_new=FAKE + 2), False, B.PA_ERR_SHAPE),        # 16-byte pieces are read
+    (dict(v_new=FAKE + 8), False, B.PA_ERR_SHAPE),
+    (dict(q_out=FAKE + Q_BYTES + 2), False, B.PA_ERR_SHAPE),
+    (dict(q_out=FAKE), False, B.PA_ERR_SHAPE),            # q_out overlapping q
+    (dict(q_out=FAKE + Q_BYTES - 16), False, B.PA_ERR_SHAPE),
+    (dict(q_out=FAKE - Q_BYTES + 16), False, B.PA_ERR_SHAPE),
+])
+def test_fused_argument_errors(kw, rope, status):
+    p = _fake_pool(rope_max_pos=2000, rope_theta=1e4) if rope else _fake_pool()
+    with pytest.raises(B.PaError) as e:
+        _fused(p, **kw)
+    assert e.value.status == status
+
+
+def test_fused_padded_checks():
+    p = _fake_pool(layout="padded", batch_cap=8, seq_cap=3000, rope_max_pos=3000,
+                   rope_theta=1e6)
+
+    def call(**kw):
+        a = dict(positions=FAKE, dest=None, k_new=FAKE, v_new=FAKE, q=FAKE,
+                 q_out=FAKE + Q_BYTES, gap_start=FAKE, gap_end=FAKE, kv_cols=2500, batch=4)
+        a.update(kw)
+        return B.pa_append_decode_attention_padded(p, a["positions"], a["dest"], a["k_new"],
+                                                   a["v_new"], a["q"], a["q_out"], 32,
+                                                   a["gap_start"], a["gap_end"], a["kv_cols"],
+                                                   a["batch"], 0.125, out=FAKE,
+                                                   query_workspace=True)
+
+    ref = B.pa_decode_attention_padded(p, FAKE, 32, 4, FAKE, FAKE, 2500, 0.125, out=FAKE,
+                                       query_workspace=True)
+    assert call() == ref > 0
+    for kw, status in [(dict(positions=None), B.PA_ERR_NULL), (dict(q_out=None), B.PA_ERR_NULL),
+                       (dict(gap_end=None), B.PA_ERR_NULL), (dict(batch=9), B.PA_ERR_SHAPE),
+                       (dict(q_out=FAKE), B.PA_ERR_SHAPE), (dict(k_new=FAKE + 4), B.PA_ERR_SHAPE)]:
+        with pytest.raises(B.PaError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    # a paged pool is refused by the padded call and the other way round
+    with pytest.raises(B.PaError) as e:
+        _fused(p)
+    assert e.value.status == B.PA_ERR_SHAPE
