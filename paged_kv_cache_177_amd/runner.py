@@ -192,8 +192,9 @@ class PaddedLockstep:
 
 
 class PagedLockstepGraph:
-    """One paged lockstep decode step -- append at the rows' positions, decode over kv_lens (+ the
-    log-sum-exp merge), then pa_advance_lockstep (position += 1, kv_len = position + 1) --
+    """One paged lockstep decode step -- append at the rows' positions and decode over kv_lens in
+    one pa_append_decode_attention call (+ the log-sum-exp merge), then pa_advance_lockstep
+    (position += 1, kv_len = position + 1) --
     recorded once as a HIP graph and replayed per token ("NeuroGrid releases", v0.8.0: the decode
     step replayed as a graph, lengths and positions in device buffers).
 
@@ -232,16 +233,15 @@ class PagedLockstepGraph:
         self.graph = None
 
     def step(self):
+        # append + decode in one call (the append folded into the decode launch), the merge, then
+        # the add-one kernel
         rope = self.pool.pool.desc.rope_max_pos > 0
-        B.pa_append_kv(self.pool.pool, self.block_tables, self.bt_stride, self.positions, None,
-                       self.k_new, self.v_new, self.q_in if rope else None,
-                       self.q_out if rope else None, self.H_q if rope else 0, self.batch)
-        q = self.q_out if rope else self.q_in
-        B.pa_decode_attention(self.pool.pool, q, self.H_q * self.D, 1, self.H_q,
-                              self.block_tables, self.bt_stride, self.kv_lens, self.batch,
-                              self.max_kv_len, self.scale,
-                              workspace=self.workspace if self._need else None, out=self.out,
-                              lse=self.lse)
+        B.pa_append_decode_attention(self.pool.pool, self.block_tables, self.bt_stride,
+                                     self.positions, None, self.k_new, self.v_new, self.q_in,
+                                     self.q_out if rope else None, self.H_q, self.kv_lens,
+                                     self.batch, self.max_kv_len, self.scale,
+                                     workspace=self.workspace if self._need else None,
+                                     out=self.out, lse=self.lse)
         B.pa_advance_lockstep(self.positions, self.kv_lens, None, self.batch)
 
     def capture(self):
