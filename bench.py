@@ -763,7 +763,7 @@ def main():
                                 f"shuffled pool of {case.num_blocks} blocks, seed {case.seed}"),
                    "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
                    "step": ("append_kv + decode + lse merge: pa_append_decode_attention (the "
-                            "append folded into the decode launch where the split grid runs) + "
+                            "append folded into the decode launch) + "
                             "the merge kernel")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -277,7 +277,7 @@ pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
                                      hipStream_t stream);
 
 /* Append and decode in one call: pa_append_kv followed by pa_decode_attention on the rotated
- * queries, with the append folded into the decode's split kernel (helexa PR #121, commit
+ * queries, with the append folded into the decode kernel (helexa PR #121, commit
  * "slice 1": per-row positions, keys stored post-RoPE; "NeuroGrid releases", v0.7.0: block-table
  * slots; v0.6.0: the decode). One launch instead of two.
  *
@@ -289,8 +289,6 @@ pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
  * them and the result is stored to q_out (same shape, required), otherwise q is used as given and
  * copied to q_out when q_out is not NULL. q_out must not overlap q. Results (pool bits, q_out,
  * out, lse) equal those of the two separate calls bit for bit.
- * Where the decode would run its persistent kernel (rows long enough for many splits), the call
- * runs the append kernel and then the decode: same results, two launches.
  * Workspace, out, lse, kv_lens, max_kv_len and block tables as for pa_decode_attention (n_q = 1).
  * Preconditions (clamped, not checked): as for both calls; in addition no row reads another row's
  * destination slot (destination slots are private to their rows).

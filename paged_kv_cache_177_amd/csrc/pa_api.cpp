@@ -522,10 +522,8 @@ pa_status fused_prepare(const pa_pool* pool, const int32_t* positions, const int
   return PA_OK;
 }
 
-// One launch of the split kernel that appends and decodes, then the merge. Where the persistent
-// kernel would run (it has no fused append) the append kernel goes first and the plain decode of
-// the rotated queries follows: the same results either way.
-pa_status run_append_decode(const pa_pool* pool, pa::DecodeArgs& a, size_t need, void* workspace,
+// One launch of the decode kernel that also appends, then the merge.
+pa_status run_append_decode(pa::DecodeArgs& a, size_t need, void* workspace,
                             size_t workspace_bytes, size_t* workspace_needed,
                             hipStream_t stream) {
   if (workspace_needed != nullptr) {
@@ -537,26 +535,7 @@ pa_status run_append_decode(const pa_pool* pool, pa::DecodeArgs& a, size_t need,
   if (need > 0)
     pa::carve_workspace(workspace, a.batch, 1, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
                         &a.part_lse);
-  pa::DecodeArgs plain = a;
-  plain.positions = nullptr;
-  plain.dest = nullptr;
-  plain.k_new = nullptr;
-  plain.v_new = nullptr;
-  plain.q_out = nullptr;
-  plain.cos = plain.sin = nullptr;
-  hipError_t e;
-  if (pa::decode_vector_is_persistent(plain)) {
-    pa::AppendArgs ap;
-    const pa_status s = append_prepare(pool, a.block_tables, a.bt_stride, a.positions, a.dest,
-                                       a.k_new, a.v_new, a.q_out != nullptr ? a.q : nullptr,
-                                       a.q_out, a.H_q, a.batch, nullptr, nullptr, 0.f, &ap);
-    if (s != PA_OK) return s;
-    e = pa::launch_append(ap, stream);
-    if (a.cos != nullptr) plain.q = a.q_out;  // the rotated queries, same row stride
-    if (e == hipSuccess) e = pa::launch_decode_vector(plain, stream);
-  } else {
-    e = pa::launch_decode_vector(a, stream);
-  }
+  hipError_t e = pa::launch_decode_vector(a, stream);
   if (e == hipSuccess && a.s_max > 1) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);
 }
@@ -579,7 +558,7 @@ extern "C" pa_status pa_append_decode_attention(
   if (s != PA_OK) return s;
   s = fused_prepare(pool, positions, dest, k_new, v_new, q, q_out, &a);
   if (s != PA_OK) return s;
-  return run_append_decode(pool, a, need, workspace, workspace_bytes, workspace_needed, stream);
+  return run_append_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
 }
 
 extern "C" pa_status pa_append_decode_attention_padded(
@@ -595,6 +574,5 @@ extern "C" pa_status pa_append_decode_attention_padded(
   if (s != PA_OK) return s;
   s = fused_prepare(padded_pool, positions, dest, k_new, v_new, q, q_out, &a);
   if (s != PA_OK) return s;
-  return run_append_decode(padded_pool, a, need, workspace, workspace_bytes, workspace_needed,
-                           stream);
+  return run_append_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
 }

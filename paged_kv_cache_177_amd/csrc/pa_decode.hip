@@ -378,14 +378,13 @@ struct Worker {
     vx.store(reinterpret_cast<T*>(const_cast<void*>(a.v)) + slot + c * 8);
   }
 
-  // Rotate the queries at pos (pools with RoPE tables; each head's partner half is read here)
-  // and, in split 0, store them to q_out.
-  __device__ __forceinline__ void fused_queries(const Chunk& ch, int pos) {
+  // Rotate the queries at pos (pools with RoPE tables; each head's partner half is read from
+  // qset, the chunk's G x D queries in memory or in LDS) and, in split 0, store them to q_out.
+  __device__ __forceinline__ void fused_queries(const Chunk& ch, int pos, const T* qset) {
     if (a.cos != nullptr) {
       float cs[8], sn[8];
       load_trig(pos, cs, sn);
-      const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)ch.row * a.q_row_stride +
-                    (size_t)ch.g * G * D + partner() * 8;
+      const T* qp = qset + partner() * 8;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         Vec8<T> other;
@@ -642,7 +641,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   const int my = w.my_blocks(ch);
   if (my > 0) w.load_block(f0, ch, ids, w.blk_of(0));
   if (stores && !first) w.fused_store(kx, kp, vx, ch, t_new, pos);
-  if (fused) w.fused_queries(ch, pos);  // while the first block is in flight
+  if (fused)  // while the first block is in flight
+    w.fused_queries(ch, pos, reinterpret_cast<const T*>(a.q) + (size_t)row * a.q_row_stride +
+                                 (size_t)g * G * D);
   w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
@@ -836,6 +837,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
     if (tid < kQVec) s_q[slot][tid] = pq;
   };
 
+  // fused append: store a chunk's new token and wait for the stores (its block is this wave's
+  // next load)
+  const bool fused = a.k_new != nullptr;
+  auto store_now = [&](const Chunk& ch, int t, int p) {
+    Vec8<T> kx, kp, vx;
+    if (w.lane < W::LPT) w.fused_load(ch.row, ch.g, kx, kp, vx);
+    w.fused_store(kx, kp, vx, ch, t, p);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
   Chunk cur = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_cur, chunk);
   {
     int pid = 0;
@@ -852,11 +863,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
     // the chunk after next: its ticket is read after this chunk's merge barrier
     if (tid == 0 && has_nx) rs.ticket[(k + 2) % 3] = n_static + atomicAdd(counter, 1);
     const int ids = s_ids[slot][w.lane];
-    {
-      const T* qs = reinterpret_cast<const T*>(s_q[slot]);
+    const T* qs = reinterpret_cast<const T*>(s_q[slot]);
 #pragma unroll
-      for (int h = 0; h < G; ++h) w.q[h].load_cached(qs + h * D + w.c * 8);
-    }
+    for (int h = 0; h < G; ++h) w.q[h].load_cached(qs + h * D + w.c * 8);
     Chunk nx = cur;
     int pid = 0;
     uint4 pq = make_uint4(0, 0, 0, 0);
@@ -864,9 +873,27 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
       nx = decode_ticket<PADDED>(rs, B, a.H_kv, n_full, t_nxt, chunk);
       fetch(nx, pid, pq);
     }
+    // fused append: this chunk's part. A token in this wave's first block (never prefetched, see
+    // below) is stored before that block's load, any other one right after the first load.
+    int pos = 0, t_new = 0;
+    bool stores = false, first = false;
+    if (fused) {
+      pos = a.cos != nullptr ? clampi(a.positions[cur.row], 0, a.rope_max_pos - 1) : 0;
+      t_new = w.fused_index(cur.row);
+      stores = w.fused_target(cur, uni(rs.n[cur.row]), t_new, &first);
+      if (stores && first) store_now(cur, t_new, pos);
+    }
     w.reset();
     const int my = w.my_blocks(cur);
     if (!pre && my > 0) w.load_block(f0, cur, ids, w.blk_of(0));
+    if (fused) {
+      if (stores && !first) {
+        Vec8<T> kx, kp, vx;
+        if (w.lane < W::LPT) w.fused_load(cur.row, cur.g, kx, kp, vx);
+        w.fused_store(kx, kp, vx, cur, t_new, pos);
+      }
+      w.fused_queries(cur, pos, qs);
+    }
     w.run_blocks(f0, f1, cur, ids, my);
     if (has_nx) park(slot ^ 1, pid, pq);
     w.merge_to_smem(sm);
@@ -875,7 +902,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
     pre = false;
     if (has_nx) {
       const Chunk nu = uni_chunk(nx);
-      if (w.my_blocks(nu) > 0) {
+      // a wave that stores the next chunk's new token into its own first block skips this
+      // prefetch: it stores that token at the chunk's start, then loads the block
+      bool hold = false;
+      if (fused) {
+        bool first_nu = false;
+        hold = w.fused_target(nu, uni(rs.n[nu.row]), w.fused_index(nu.row), &first_nu) &&
+               first_nu;
+      }
+      if (w.my_blocks(nu) > 0 && !hold) {
         w.load_block(f0, nu, s_ids[slot ^ 1][w.lane], w.blk_of(0));
         pre = true;
       }
@@ -1032,16 +1067,12 @@ int resident_workgroups(const void* kernel, size_t lds) {
   return per_cu * cus;
 }
 
-}  // namespace
-
+// Whether launch_decode_vector takes the persistent kernel for these arguments.
 bool decode_vector_is_persistent(const DecodeArgs& a) {
-  if (a.k_new != nullptr) return false;
   if (!(PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows))
     return false;
   return PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits;
 }
-
-namespace {
 
 template <typename T, int D, int G, bool PADDED>
 hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
@@ -1051,7 +1082,7 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   // kernel takes over. With few splits per row the split grid starts faster (a workgroup needs
   // no row scan before its first loads) and runs more waves per SIMD. Both cut rows into the
   // same chunks: their results are identical.
-  if (decode_vector_is_persistent(a)) {  // never with a fused append
+  if (decode_vector_is_persistent(a)) {
     auto kern = decode_persistent_kernel<T, D, G, PADDED>;
     const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
     if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits)) {

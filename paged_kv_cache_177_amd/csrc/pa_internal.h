@@ -147,9 +147,6 @@ hipError_t launch_pack_projection(const void* w, void* packed, int out_features,
 hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
                           hipStream_t stream);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1
-// Whether launch_decode_vector takes the persistent kernel for these arguments (that kernel has
-// no fused append: the caller appends first).
-bool decode_vector_is_persistent(const DecodeArgs& a);
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream);      // n_q > 1
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
 

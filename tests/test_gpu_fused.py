@@ -76,11 +76,15 @@ def test_fused_b128_full_size():
     fused_vs_separate(c, rows=rows)
 
 
-def test_fused_long_rows_take_the_two_launch_form():
-    """Rows of 70 chunks: the decode runs its persistent kernel, which has no fused append, so the
-    call appends first; the results are still those of the separate calls."""
-    case = W.make_paged_case("fused-long", 43, [99, 20 * 1024 + 7, 70 * 1024 - 9], 8, 2, 64,
-                             "bf16", rope_theta=1e4)
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32")])
+def test_fused_long_rows_persistent_kernel(D, dtype):
+    """Rows of up to 70 chunks: the decode runs its persistent kernel, whose chunk loop stores each
+    row's new token (rotated) where its chunk is taken up; short rows in the same batch put the
+    token in a wave's first block, which that wave then does not prefetch."""
+    chunk = 1024 if D <= 64 else 512
+    n = [5, 70, 20 * chunk + 7, 70 * chunk - 9, 3 * chunk + 40]
+    case = W.make_paged_case(f"fused-long-D{D}-{dtype}", 43 + D, n, 8, 2, D, dtype,
+                             rope_theta=1e4)
     fused_vs_separate(case)
 
 
