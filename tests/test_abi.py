@@ -20,7 +20,7 @@ def declared_functions():
     return re.findall(r"^pa_status\s+(\w+)\s*\(", text, flags=re.M)
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_exactly_the_binding_exports():
     assert sorted(declared_functions()) == sorted(B.EXPORTS)
 
 
