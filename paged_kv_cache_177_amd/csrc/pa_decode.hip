@@ -613,7 +613,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   W w(a);
   const int g = blockIdx.x;
   const int row = blockIdx.y;
-  const int split = blockIdx.z;
+  // the highest splits go first: they exist only for the longest rows, so the launch ends with
+  // the splits every row has (a shorter drain than ending on long rows' late full chunks)
+  const int split = (int)gridDim.z - 1 - (int)blockIdx.z;
   const int chunk = chunk_tokens(D);
   // issued before the row length is known, so their latency overlaps the length load
   int ids = w.load_ids(row, split * chunk);
