@@ -31,6 +31,10 @@
 //   * Two launch shapes run the same chunks: a grid of one workgroup per (g, b, s) whose
 //     workgroups past a row's last split exit at once, and a persistent grid that pulls chunks
 //     from a counter (see decode_persistent_kernel), used when rows are long enough for many splits.
+//   * Either can also do the append (the fused call): the wave whose blocks include a row's new
+//     token stores its key (rotated) and value before it loads that block, and every workgroup
+//     rotates its queries in registers, with the append kernel's arithmetic, so the results are
+//     those of the separate append and decode bit for bit.
 #include "pa_internal.h"
 
 #include <map>
