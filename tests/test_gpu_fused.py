@@ -171,3 +171,43 @@ def test_fused_copies_queries_without_rope_table():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(to_numpy(q_out, "bf16"), "bf16"),
                                   bits(to_numpy(r.q, "bf16"), "bf16"))
+
+
+def test_fused_padded_destination_in_the_gap_or_past_the_columns():
+    """Padded rows whose new token goes into the row's own gap, or past kv_cols: written exactly as
+    pa_append_kv writes it, never attended to; the other rows as usual."""
+    c = W.make_paged_case("fused-padded-dest", 47, [3, 40, 700, 1500], 8, 2, 64, "bf16",
+                          rope_theta=1e4)
+    pc = W.padded_from_paged(c, seq_cap=1600)
+    dest_np = pc.dest.copy()
+    dest_np[0] = pc.prefix_lens[0] + 5       # inside row 0's gap [3, 1500)
+    dest_np[1] = pc.kv_cols + 20             # past the attended columns
+    pos, _, k_new, v_new, q, gs, _ = _padded_inputs(pc)
+    dest = torch.from_numpy(dest_np).cuda()
+    # rows 0 and 1 have no token at the lockstep column (it keeps its NaN filler): their gaps run
+    # to kv_cols, so they attend to their prefixes only
+    ge_np = np.full(pc.batch, pc.padded_len, np.int32)
+    ge_np[:2] = pc.kv_cols
+    ge = torch.from_numpy(ge_np).cuda()
+    Ls = _padded_pool(pc)
+    q_rot_s = torch.empty_like(q)
+    Ls.append(pos, dest, k_new, v_new, q, q_rot_s)
+    out_s, lse_s = Ls.decode(q_rot_s, gs, ge, pc.kv_cols, pc.scale)
+    Lf = _padded_pool(pc)
+    q_rot_f = torch.empty_like(q)
+    out_f, lse_f = Lf.append_decode(pos, dest, k_new, v_new, q, q_rot_f, gs, ge, pc.kv_cols,
+                                    pc.scale)
+    torch.cuda.synchronize()
+    for name in ("k", "v"):
+        np.testing.assert_array_equal(bits(to_numpy(getattr(Lf.kv, name), "bf16"), "bf16"),
+                                      bits(to_numpy(getattr(Ls.kv, name), "bf16"), "bf16"))
+    np.testing.assert_array_equal(out_f.cpu().numpy(), out_s.cpu().numpy())
+    np.testing.assert_array_equal(lse_f.cpu().numpy(), lse_s.cpu().numpy())
+    cos, sin = O.rope_tables(pc.rope_theta, pc.head_dim, pc.rope_max_pos)
+    k2, v2, q2 = O.append_kv(pc.k_pad, pc.v_pad, "bf16", "padded", None, pc.positions, dest_np,
+                             pc.k_new, pc.v_new, cos, sin, q_in=pc.q)
+    np.testing.assert_array_equal(bits(to_numpy(Lf.kv.k, "bf16"), "bf16"), bits(k2, "bf16"))
+    o_ref, l_ref = O.decode_padded(k2, v2, "bf16", pc.prefix_lens.astype(np.int32), ge_np,
+                                   pc.kv_cols, q2, pc.scale)
+    assert_attention_close(out_f.cpu().numpy(), o_ref[:, 0], "bf16", "out")
+    assert_attention_close(lse_f.cpu().numpy(), l_ref[:, 0], "bf16", "lse")
