@@ -28,6 +28,13 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=128 ragged bf16"
 METRIC_LONG = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=4 long-context bf16"
+# one GPU's share of a sharded step (the lengths of the whole workload, cut as the sharding cuts)
+METRIC_SHARE = {
+    "b128-tp2": "paged decode-attn K/V GB/s (% HBM peak), B=128 bf16, one GPU of 2 (KV heads split)",
+    "b128-dp2": "paged decode-attn K/V GB/s (% HBM peak), B=128 bf16, one GPU of 2 (rows split)",
+    "long-sp4": "paged decode-attn K/V GB/s (% HBM peak), B=4 long-context bf16, one GPU of 4 "
+                "(each row's tokens split)",
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b128_traffic.txt")
 
 
@@ -37,12 +44,14 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="b128",
-                   choices=["b128", "long", "mq", "mq-sparse", "b16", "mq-tokenize"],
+                   choices=["b128", "long", "mq", "mq-sparse", "b16", "mq-tokenize",
+                            "b128-tp2", "b128-dp2", "long-sp4"],
                    help="b128 is the reported workload; long (B=4 long-context split-K), mq "
                         "(latent cross-attention on the matrix cores; mq-sparse under the "
                         "temporal block mask), b16 (the B=16 lockstep step, paged and "
                         "right-padded) and mq-tokenize (the fused spike tokenizer + K/V "
-                        "projection) measure the other paths")
+                        "projection) measure the other paths; b128-tp2, b128-dp2 and long-sp4 "
+                        "measure one GPU's share of a sharded step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="cache-flush write between the extra flushed decode timings")
@@ -657,7 +666,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    case = W.b128() if args.workload == "b128" else W.long_context()
+    if args.workload == "b128":
+        case = W.b128()
+    elif args.workload == "long":
+        case = W.long_context()
+    else:
+        case = W.shard_share(args.workload)
     kv_bytes = case.kv_bytes()
     r = PagedStep(case, device="cuda:0")
     stream = torch.cuda.current_stream()
@@ -744,7 +758,8 @@ def main():
     src_hash = kernel_source_hash(*DECODE_SOURCES)
     traffic = read_traffic(src_hash) if args.workload == "b128" else None
     out = {
-        "metric": METRIC if args.workload == "b128" else METRIC_LONG,
+        "metric": (METRIC if args.workload == "b128" else
+                   METRIC_LONG if args.workload == "long" else METRIC_SHARE[args.workload]),
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -770,7 +785,7 @@ def main():
                      "traffic": (round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
                                  if traffic is not None else None),
                      "kernel": ("pa_decode_attention call (decode_vector_kernel + "
-                                "lse_reduce_kernel)") if args.workload == "b128" else
+                                "lse_reduce_kernel)") if not args.workload.startswith("long") else
                                ("pa_decode_attention call (decode_persistent_kernel + "
                                 "lse_reduce_kernel)"),
                      "bytes_per_launch": kv_bytes,

@@ -165,6 +165,16 @@ def test_b128_full_size_sampled_rows(b128_case):
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+@pytest.mark.parametrize("kind", ["b128-tp2", "b128-dp2", "long-sp4"])
+def test_one_gpu_shares_sampled_rows(kind):
+    """One GPU's share of a sharded step at its real shape (the lengths of the whole workload, cut
+    by KV head, by rows, or each row's tokens over four GPUs): sampled rows against the oracle."""
+    c = W.shard_share(kind)
+    order = np.argsort(c.kv_lens)
+    rows = np.unique(np.concatenate([order[:2], order[-2:], order[::17]]))
+    run_and_check_paged(c, rows=rows)
+
+
 @pytest.fixture(scope="module")
 def long_case():
     log("[gen] long seed 3")

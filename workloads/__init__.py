@@ -22,6 +22,7 @@ from .generators import (  # noqa: F401
     b16_plan,
     b128,
     long_context,
+    shard_share,
     mq,
     mq_tokenizer,
     TokenizerCase,

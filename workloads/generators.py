@@ -164,6 +164,24 @@ def b128(seed: int = 2) -> PagedCase:
     return make_paged_case("b128", seed, n, 32, 8, 64, "bf16", rng=rng)
 
 
+def shard_share(kind: str) -> PagedCase:
+    """One GPU's share of a sharded step, drawn with the same lengths as the whole workload:
+    "b128-tp2" (B128 split by KV head over two GPUs: 16 query / 4 KV heads), "b128-dp2" (B128
+    split by rows over two GPUs: its first 64 rows), "long-sp4" (each Long row split over four
+    GPUs: a quarter of its tokens)."""
+    if kind in ("b128-tp2", "b128-dp2"):
+        rng = np.random.default_rng(2)
+        n = rng.integers(512, 8192, 128, endpoint=True)
+        if kind == "b128-tp2":
+            return make_paged_case(kind, 2, n, 16, 4, 64, "bf16", rng=rng)
+        return make_paged_case(kind, 2, n[:64], 32, 8, 64, "bf16", rng=rng)
+    if kind == "long-sp4":
+        rng = np.random.default_rng(3)
+        n = rng.integers(32768, 131072, 4, endpoint=True)
+        return make_paged_case(kind, 3, n // 4, 32, 8, 128, "bf16", rng=rng)
+    raise ValueError(kind)
+
+
 def long_context(seed: int = 3) -> PagedCase:
     """B=4 long rows: contexts uniform in [32768, 131072], 32 query / 8 KV heads, D=128, bf16."""
     rng = np.random.default_rng(seed)
