@@ -738,6 +738,30 @@ def main():
     # back-to-back calls between one pair of events each
     append_us, append_norm_us = append_timings(r, case, stream)
 
+    # one GPU of four holding a quarter of each row: after the all-gather of the four shares'
+    # (out, lse), pa_lse_merge combines them; here the share's own results stand in for the four.
+    # Back-to-back calls of so short a kernel are paced by the host's call rate: its own duration
+    # comes from the profiler.
+    merge_us = None
+    if args.workload == "long-sp4":
+        from paged_kv_cache_177_amd import binding as B
+
+        n_pairs = case.batch * case.num_q_heads
+        parts_o = r.out.reshape(1, n_pairs, case.head_dim).repeat(4, 1, 1).contiguous()
+        parts_l = r.lse.reshape(1, n_pairs).repeat(4, 1).contiguous()
+        m_out = torch.empty((n_pairs, case.head_dim), dtype=torch.float32, device="cuda:0")
+        m_lse = torch.empty((n_pairs,), dtype=torch.float32, device="cuda:0")
+        for _ in range(10):
+            B.pa_lse_merge(parts_o, parts_l, 4, n_pairs, case.head_dim, m_out, m_lse)
+        ma, mb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ma.record(stream)
+        for _ in range(args.steps):
+            B.pa_lse_merge(parts_o, parts_l, 4, n_pairs, case.head_dim, m_out, m_lse)
+        mb.record(stream)
+        torch.cuda.synchronize()
+        merge_us = ma.elapsed_time(mb) * 1e3 / args.steps
+
     # extra: decode calls with the last-level cache flushed before each one (outside the events)
     flush = torch.empty(args.flush_mb * (1 << 20), dtype=torch.uint8, device="cuda:0")
     fl = []
@@ -807,6 +831,8 @@ def main():
                    "decode_pct_of_read_ceiling": round(100 * achieved / ceiling, 1),
                    "append_us": round(append_us, 2),
                    "append_qk_norm_us": round(append_norm_us, 2),
+                   "lse_merge_4_parts_us_per_call_events":
+                       None if merge_us is None else round(merge_us, 2),
                    "source_hash": src_hash},
     }
     if not args.no_cpu_baseline:

@@ -320,6 +320,23 @@ pa_status pa_append_decode_attention_padded(const pa_pool* padded_pool, const in
                                             size_t* workspace_needed /* host */, float* out,
                                             float* lse, hipStream_t stream);
 
+/* Merge partial attention results computed over disjoint key sets (the step after an all-gather
+ * when one row's keys are split across GPUs; "NeuroGrid releases", v0.6.0 "Flash Decode Attention
+ * Kernel": partial softmax statistics combined through their maxima).
+ *
+ * out_parts: fp32 [num_parts][n][head_dim], each part's normalised output for n (row, query head)
+ * pairs; lse_parts: fp32 [num_parts][n], each part's log-sum-exp (natural log, -inf for a part
+ * with no keys) -- what pa_decode_attention writes for each part's keys. For every pair:
+ *   M = max_p lse_p,  w_p = exp(lse_p - M),  out = sum_p w_p out_p / sum_p w_p,
+ *   lse = M + log(sum_p w_p)   (fp32, parts summed in index order)
+ * out: fp32 [n][head_dim]; lse: fp32 [n] or NULL. Every part empty gives out = 0, lse = -inf.
+ * Device pointers; out must not overlap out_parts. Asynchronous on stream; no workspace.
+ * Errors: PA_ERR_NULL (out_parts, lse_parts, out); PA_ERR_UNSUPPORTED (head_dim not in
+ * {32, 64, 128}); PA_ERR_SHAPE (num_parts < 1 or > 65535, n < 0 or > 2^34, out overlapping
+ * out_parts). n == 0 is a no-op. */
+pa_status pa_lse_merge(const float* out_parts, const float* lse_parts, int32_t num_parts,
+                       int64_t n, int32_t head_dim, float* out, float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ PA_PAGED, PA_PADDED = 0, 1
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
            "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm",
            "pa_tokenize_kv", "pa_pack_projection", "pa_append_decode_attention",
-           "pa_append_decode_attention_padded")
+           "pa_append_decode_attention_padded", "pa_lse_merge")
 
 
 class PaError(RuntimeError):
@@ -89,6 +89,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                       _P, _I32, _P, _P, _I32, _I32,
                                                       ctypes.c_float, _P, ctypes.c_size_t,
                                                       _SIZE_P, _P, _P, _P]
+    lib.pa_lse_merge.argtypes = [_P, _P, _I32, ctypes.c_int64, _I32, _P, _P, _P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -283,6 +284,14 @@ def pa_append_decode_attention_padded(pool: Pool, positions, dest, k_new, v_new,
                                                _ptr(out), _ptr(lse), _stream(stream))
     _check("pa_append_decode_attention_padded", st)
     return need.value
+
+
+def pa_lse_merge(out_parts, lse_parts, num_parts: int, n: int, head_dim: int, out, lse=None,
+                 stream=None) -> None:
+    """Merge per-part (out, lse) results over disjoint key sets into one (out, lse)."""
+    lib = load_library()
+    _check("pa_lse_merge", lib.pa_lse_merge(_ptr(out_parts), _ptr(lse_parts), num_parts, n,
+                                            head_dim, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------------

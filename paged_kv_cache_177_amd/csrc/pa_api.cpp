@@ -6,6 +6,7 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_merge.h"
 
 namespace {
 
@@ -575,4 +576,26 @@ extern "C" pa_status pa_append_decode_attention_padded(
   s = fused_prepare(padded_pool, positions, dest, k_new, v_new, q, q_out, &a);
   if (s != PA_OK) return s;
   return run_append_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
+}
+
+extern "C" pa_status pa_lse_merge(const float* out_parts, const float* lse_parts, int32_t num_parts,
+                                  int64_t n, int32_t head_dim, float* out, float* lse,
+                                  hipStream_t stream) {
+  if (out_parts == nullptr || lse_parts == nullptr || out == nullptr) return PA_ERR_NULL;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_parts < 1 || num_parts > 65535 || n < 0 || n > ((int64_t)1 << 34)) return PA_ERR_SHAPE;
+  // the outputs must not overlap the parts (every wave reads all parts of its pair)
+  const uintptr_t pb = (uintptr_t)out_parts, pe = pb + (uintptr_t)num_parts * n * head_dim * 4;
+  const uintptr_t ob = (uintptr_t)out, oe = ob + (uintptr_t)n * head_dim * 4;
+  if (n > 0 && ob < pe && pb < oe) return PA_ERR_SHAPE;
+  if (n == 0) return PA_OK;
+  pa::LseMergeArgs a;
+  a.out_parts = out_parts;
+  a.lse_parts = lse_parts;
+  a.num_parts = num_parts;
+  a.n = n;
+  a.D = head_dim;
+  a.out = out;
+  a.lse = lse;
+  return map_hip(pa::launch_lse_merge(a, stream));
 }

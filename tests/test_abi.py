@@ -412,3 +412,17 @@ def test_fused_padded_checks():
     with pytest.raises(B.PaError) as e:
         _fused(p)
     assert e.value.status == B.PA_ERR_SHAPE
+
+
+def test_lse_merge_argument_errors():
+    ok = dict(out_parts=FAKE, lse_parts=FAKE + 0x100000, num_parts=4, n=10, head_dim=64,
+              out=FAKE + 0x200000)
+    B.pa_lse_merge(**{**ok, "n": 0})                       # nothing to do: no launch
+    for kw, status in [(dict(out_parts=None), B.PA_ERR_NULL), (dict(lse_parts=None), B.PA_ERR_NULL),
+                       (dict(out=None), B.PA_ERR_NULL), (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+                       (dict(num_parts=0), B.PA_ERR_SHAPE), (dict(num_parts=65536), B.PA_ERR_SHAPE),
+                       (dict(n=-1), B.PA_ERR_SHAPE), (dict(n=(1 << 34) + 1), B.PA_ERR_SHAPE),
+                       (dict(out=FAKE + 16), B.PA_ERR_SHAPE)]:  # out inside out_parts
+        with pytest.raises(B.PaError) as e:
+            B.pa_lse_merge(**{**ok, **kw})
+        assert e.value.status == status, kw
