@@ -28,9 +28,11 @@
 //     swizzle across rows, a swap across half-waves), then the waves through LDS. One split
 //     writes out/lse; several write normalised partials plus their log-sum-exp for
 //     lse_reduce_kernel.
-//   * Two launch shapes run the same chunks: a grid of one workgroup per (g, b, s) whose
-//     workgroups past a row's last split exit at once, and a persistent grid that pulls chunks
-//     from a counter (see decode_persistent_kernel), used when rows are long enough for many splits.
+//   * Three launch shapes run the same chunks: a grid of one workgroup per (g, b, s) whose
+//     workgroups past a row's last split exit at once; for rows long enough for many splits, a
+//     compact grid whose workgroups map to the chunks through the rows' lengths (batches of at
+//     most 64 rows), or a persistent grid that pulls chunks from a counter (see
+//     decode_persistent_kernel).
 //   * Either can also do the append (the fused call): the wave whose blocks include a row's new
 //     token stores its key (rotated) and value before it loads that block, and every workgroup
 //     rotates its queries in registers, with the append kernel's arithmetic, so the results are
@@ -46,6 +48,11 @@
 #endif
 #ifndef PA_DECODE_PERSISTENT
 #define PA_DECODE_PERSISTENT 1
+#endif
+// Rows long enough for the persistent kernel, in a batch of at most 64 rows: 1 = a compact grid
+// instead (see decode_vector_kernel), 0 = the persistent kernel.
+#ifndef PA_DECODE_COMPACT
+#define PA_DECODE_COMPACT 1
 #endif
 
 namespace pa {
@@ -610,17 +617,57 @@ __device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_
 }
 
 // ---- grid kernel: one workgroup per (KV head, row, split); splits past the row's end exit -------
-template <typename T, int D, int G, bool PADDED>
+// COMPACT (batches of at most 64 rows): a 1-D grid whose workgroups map to the chunks through
+// the rows' lengths, every row's full chunks first and each row's partial last chunk after them,
+// so the workgroups past the last chunk (which exit at once) all come at the end of the launch.
+template <typename T, int D, int G, bool PADDED, bool COMPACT>
 __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const DecodeArgs a) {
   using W = Worker<T, D, G, PADDED>;
   __shared__ typename W::Smem sm;
   W w(a);
-  const int g = blockIdx.x;
-  const int row = blockIdx.y;
-  // the highest splits go first: they exist only for the longest rows, so the launch ends with
-  // the splits every row has (a shorter drain than ending on long rows' late full chunks)
-  const int split = (int)gridDim.z - 1 - (int)blockIdx.z;
   const int chunk = chunk_tokens(D);
+  int g, row, split;
+  int n = 0, gap_s = 0, gap_shift = 0;
+  if constexpr (COMPACT) {
+    // one row per lane: its valid tokens, its full chunks and whether it has a partial one
+    int gs_l = 0, gsh_l = 0;
+    const bool has = w.lane < a.batch;
+    const int nb = has ? row_valid<PADDED>(a, w.lane, &gs_l, &gsh_l) : 0;
+    const int f = has ? nb / chunk : 0;
+    const int pc = has && (nb % chunk != 0 || nb == 0) ? 1 : 0;
+    int fi = f, pi = pc;  // inclusive prefix sums over the rows
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int fu = __shfl_up(fi, o), pu = __shfl_up(pi, o);
+      if (w.lane >= o) {
+        fi += fu;
+        pi += pu;
+      }
+    }
+    const int n_full = __builtin_amdgcn_readlane(fi, 63);
+    const int n_part = __builtin_amdgcn_readlane(pi, 63);
+    const int item = (int)(blockIdx.x / (unsigned)a.H_kv);
+    g = (int)(blockIdx.x % (unsigned)a.H_kv);
+    if (item >= n_full + n_part) return;  // past the last chunk: these come last
+    const bool full = item < n_full;
+    const int k = full ? item : item - n_full;
+    // the one row whose range holds k (rows with an empty range never match)
+    const unsigned long long m =
+        full ? __ballot(has && fi - f <= k && k < fi) : __ballot(has && pi - pc <= k && k < pi);
+    if (m == 0) return;  // cannot happen: the rows' ranges cover every item
+    row = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(m));
+    n = __builtin_amdgcn_readlane(nb, row);
+    gap_s = __builtin_amdgcn_readlane(gs_l, row);
+    gap_shift = __builtin_amdgcn_readlane(gsh_l, row);
+    split = full ? k - (__builtin_amdgcn_readlane(fi, row) - __builtin_amdgcn_readlane(f, row))
+                 : n / chunk;
+  } else {
+    g = blockIdx.x;
+    row = blockIdx.y;
+    // the highest splits go first: they exist only for the longest rows, so the launch ends with
+    // the splits every row has (a shorter drain than ending on long rows' late full chunks)
+    split = (int)gridDim.z - 1 - (int)blockIdx.z;
+  }
   // issued before the row length is known, so their latency overlaps the length load
   int ids = w.load_ids(row, split * chunk);
   w.load_q(w.q, row, g);
@@ -631,8 +678,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   const int t_new = fused ? w.fused_index(row) : 0;
   Vec8<T> kx, kp, vx;
   if (fused && w.lane < W::LPT) w.fused_load(row, g, kx, kp, vx);
-  int gap_s, gap_shift;
-  const int n = row_valid<PADDED>(a, row, &gap_s, &gap_shift);
+  if constexpr (!COMPACT) n = row_valid<PADDED>(a, row, &gap_s, &gap_shift);
   const Chunk ch = make_chunk(row, g, split, n, gap_s, gap_shift, chunk);
   if (split >= ch.ns) return;
   bool first = false;
@@ -1088,6 +1134,17 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
   // kernel takes over. With few splits per row the split grid starts faster (a workgroup needs
   // no row scan before its first loads) and runs more waves per SIMD. Both cut rows into the
   // same chunks: their results are identical.
+  if (PA_DECODE_COMPACT && decode_vector_is_persistent(a) && a.batch <= 64 &&
+      items <= (long long)0x7fffffff) {
+    // Rows with many chunks and few enough rows for one wave to map workgroups to chunks: a
+    // compact grid at the split kernel's occupancy (3 waves per SIMD against the persistent
+    // kernel's 2), with no early-exit workgroups ahead of working ones. It takes 176-178 us on
+    // the B=4 long-context step where the persistent kernel takes 184 us. For short rows the
+    // plain grid stays faster: its exits are few and its loads start before the row is known.
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED, true>), dim3((unsigned)items),
+                       dim3(64 * kWaves), 0, stream, a);
+    return hipGetLastError();
+  }
   if (decode_vector_is_persistent(a)) {
     auto kern = decode_persistent_kernel<T, D, G, PADDED>;
     const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
@@ -1098,8 +1155,8 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
     }
   }
   dim3 grid(a.H_kv, a.batch, a.s_max);
-  hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED>), grid, dim3(64 * kWaves), 0, stream,
-                     a);
+  hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED, false>), grid, dim3(64 * kWaves), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

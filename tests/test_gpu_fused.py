@@ -88,6 +88,14 @@ def test_fused_long_rows_persistent_kernel(D, dtype):
     fused_vs_separate(case)
 
 
+def test_fused_wide_batch_persistent_kernel():
+    """70 rows, two of them long: the persistent kernel's chunk loop does the append."""
+    rng = np.random.default_rng(48)
+    n = np.concatenate([[21000, 17000], rng.integers(0, 400, 68)])
+    case = W.make_paged_case("fused-wide", 48, n, 8, 2, 64, "bf16", rope_theta=1e4)
+    fused_vs_separate(case, rows=[0, 1, 2, 50, 69])
+
+
 def test_fused_destination_outside_the_row():
     """A destination at or past kv_len is still written (as pa_append_kv writes it) but not
     attended to; a row with kv_len 0 attends to nothing."""

@@ -165,6 +165,26 @@ def test_b128_full_size_sampled_rows(b128_case):
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_wide_batch_with_long_rows_runs_the_persistent_kernel(D):
+    """More than 64 rows, one of them long enough for many chunks: the persistent kernel (a batch
+    of at most 64 such rows takes the compact grid). The oracle checks sampled rows, and a row
+    decoded on its own (the compact grid, or the split grid for a short row) gives the same bits."""
+    chunk = 1024 if D <= 64 else 512
+    rng = np.random.default_rng(70 + D)
+    n = np.concatenate([[20 * chunk + 3, 17 * chunk], rng.integers(0, 400, 68)])
+    case = W.make_paged_case(f"wide-long-D{D}", 71 + D, n, 8, 2, D, "bf16")
+    r, _, _ = run_and_check_paged(case, rows=[0, 1, 2, 3, 40, 69])
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    for b in [0, 1, 5]:
+        rb = PagedStep(_single_row(case, b))
+        rb.kv = r.kv
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b])
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
+
+
 @pytest.mark.parametrize("kind", ["b128-tp2", "b128-dp2", "long-sp4"])
 def test_one_gpu_shares_sampled_rows(kind):
     """One GPU's share of a sharded step at its real shape (the lengths of the whole workload, cut
