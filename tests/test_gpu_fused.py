@@ -126,14 +126,21 @@ def _padded_pool(pc):
     return L
 
 
-@pytest.mark.parametrize("D,dtype,theta", [(64, "bf16", 1e6), (128, "bf16", 0.0),
-                                           (64, "f32", 1e4)])
-def test_fused_padded(D, dtype, theta):
+SHORT_ROWS = [0, 5, 16, 700, 1023, 1500, 2100]
+LONG_ROWS = [99, 20 * 1024 + 7, 40 * 1024 - 9]  # 40 chunks: the compact grid over a few rows
+
+
+@pytest.mark.parametrize("D,dtype,theta,lens", [(64, "bf16", 1e6, SHORT_ROWS),
+                                                (128, "bf16", 0.0, SHORT_ROWS),
+                                                (64, "f32", 1e4, SHORT_ROWS),
+                                                (64, "bf16", 1e6, LONG_ROWS)],
+                         ids=["D64-bf16", "D128-bf16", "D64-f32", "D64-bf16-long-rows"])
+def test_fused_padded(D, dtype, theta, lens):
     """The lockstep form: gaps of every width; fused and separate give the same bits, and the
     oracle agrees."""
-    c = W.make_paged_case(f"fused-padded-D{D}-{dtype}", 45, [0, 5, 16, 700, 1023, 1500, 2100],
-                          8, 2, D, dtype, rope_theta=theta)
-    pc = W.padded_from_paged(c, seq_cap=2200)
+    c = W.make_paged_case(f"fused-padded-D{D}-{dtype}-{len(lens)}", 45, lens, 8, 2, D, dtype,
+                          rope_theta=theta)
+    pc = W.padded_from_paged(c, seq_cap=max(lens) + 100)
     log(f"[fused-padded] case={pc.name} B={pc.batch} D={D} dtype={dtype} theta={theta}")
     pos, dest, k_new, v_new, q, gs, ge = _padded_inputs(pc)
     rope = pc.rope_max_pos > 0

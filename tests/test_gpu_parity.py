@@ -185,6 +185,29 @@ def test_wide_batch_with_long_rows_runs_the_persistent_kernel(D):
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+def test_compact_grid_at_its_64_row_limit():
+    """Exactly 64 rows with long ones on the first and the last lane of the row scan, lengths on
+    and next to chunk multiples, and empty rows: the compact grid's widest batch. The oracle checks
+    those rows, and each decoded alone (the compact grid over one row, or the split grid) gives the
+    same bits."""
+    chunk = 1024
+    rng = np.random.default_rng(80)
+    n = rng.integers(0, 3 * chunk, 64)
+    n[[0, 63, 31, 32]] = [16 * chunk - 1, 18 * chunk, 16 * chunk, 0]
+    n[[5, 6]] = [chunk - 1, 2 * chunk]
+    case = W.make_paged_case("compact-64", 81, n, 8, 2, 64, "bf16")
+    rows = [0, 5, 6, 31, 32, 62, 63]
+    r, _, _ = run_and_check_paged(case, rows=rows)
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    for b in [0, 6, 32, 63]:
+        rb = PagedStep(_single_row(case, b))
+        rb.kv = r.kv
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b])
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
+
+
 @pytest.mark.parametrize("kind", ["b128-tp2", "b128-dp2", "long-sp4"])
 def test_one_gpu_shares_sampled_rows(kind):
     """One GPU's share of a sharded step at its real shape (the lengths of the whole workload, cut
