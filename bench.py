@@ -617,8 +617,8 @@ def main_b16(args):
                                 f"{plan.seed}"),
                    "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
                    "step": ("append_kv (k, v, q rotation) + decode + lse merge: "
-                            "pa_append_decode_attention (the append folded into the decode "
-                            "launch) + the merge kernel")},
+                            "pa_append_decode_attention (one launch: the append folded into "
+                            "the split grid, which also merges the splits)")},
         "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (ev_paged * 1e-6) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kv_bytes / (ev_paged * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -802,16 +802,19 @@ def main():
                                 f"shuffled pool of {case.num_blocks} blocks, seed {case.seed}"),
                    "global_batch": case.batch, "kv_bytes_per_step": kv_bytes,
                    "step": ("append_kv + decode + lse merge: pa_append_decode_attention (the "
-                            "append folded into the decode launch) + "
-                            "the merge kernel")},
+                            "append folded into the decode launch) + the merge kernel"
+                            if args.workload.startswith("long") else
+                            "append_kv + decode + lse merge: pa_append_decode_attention (one "
+                            "launch: the append folded into the split grid, which also merges "
+                            "the splits)")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
                                  if traffic is not None else None),
-                     "kernel": ("pa_decode_attention call (decode_vector_kernel + "
-                                "lse_reduce_kernel)") if not args.workload.startswith("long") else
-                               ("pa_decode_attention call (decode_persistent_kernel + "
-                                "lse_reduce_kernel)"),
+                     "kernel": ("pa_decode_attention call (decode_vector_kernel, split grid "
+                                "merging its own splits)") if not args.workload.startswith("long")
+                               else ("pa_decode_attention call (decode_vector_kernel, compact "
+                                     "grid, + lse_reduce_kernel)"),
                      "bytes_per_launch": kv_bytes,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "detail": {"us_per_step": round(ms_per_step * 1e3, 2),

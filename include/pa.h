@@ -155,15 +155,20 @@ pa_status pa_append_kv_qk_norm(const pa_pool* pool, const int32_t* block_tables,
  * softmax, computed online.
  * out: [batch][n_q][num_q_heads][D] fp32. lse: [batch][n_q][num_q_heads] fp32 or NULL.
  * n_q == 1 is the decode path (vector units; one workgroup per (row, KV head, split); long rows are
- * split into chunks whose partial results a second kernel merges by log-sum-exp). n_q > 1 is the
+ * split into chunks whose partial results are merged by log-sum-exp: by the split kernel
+ * itself when no row has more than 16 chunks, else by a second kernel). n_q > 1 is the
  * multi-query path (matrix cores). The split of a row depends on its own kv_len only, so a row's
  * result does not depend on the rest of the batch.
  * Workspace: with workspace_needed != NULL the call only writes the bytes it needs for these
  * arguments there and launches nothing; otherwise workspace must hold that many bytes (it may be
- * NULL when none are needed). A workspace must be zero-filled before its first use: its first 256
- * bytes hold the work counter of the split kernels, which every call leaves at zero again. Calls
- * that overlap in time (other streams) need workspaces of their own. max_kv_len is a host upper
- * bound of kv_lens (<= bt_stride * 16).
+ * NULL when none are needed). A workspace must be zero-filled before its first use: it starts with
+ * counters that every call leaves at zero again, the work counter of the split kernels (256 bytes)
+ * and one finished-split count per (row, query head) (4 * batch * num_q_heads bytes, rounded up
+ * to 256), with the partial results after them. Calls may share a workspace while batch *
+ * num_q_heads stays the same (their split counts may differ); after a change, zero-fill it again
+ * (a smaller call's partials overwrite a larger one's counts). Calls that overlap in time (other
+ * streams) need workspaces of their own. max_kv_len is a host upper bound of kv_lens
+ * (<= bt_stride * 16).
  * Preconditions (clamped, not checked): 0 <= kv_lens[b] <= max_kv_len; block ids < num_blocks.
  * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0 or > 65535,
  * n_q < 1, num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, more

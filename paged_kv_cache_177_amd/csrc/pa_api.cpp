@@ -322,9 +322,11 @@ pa_status run_decode(pa::DecodeArgs& a, size_t need, void* workspace, size_t wor
   if (a.batch == 0) return PA_OK;
   if (need > 0)
     pa::carve_workspace(workspace, a.batch, a.n_q, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
-                        &a.part_lse);
-  hipError_t e = a.n_q == 1 ? pa::launch_decode_vector(a, stream) : pa::launch_decode_mq(a, stream);
-  if (e == hipSuccess && a.s_max > 1) e = pa::launch_lse_reduce(a, stream);
+                        &a.part_lse, &a.merge_counts);
+  bool merged = false;
+  hipError_t e = a.n_q == 1 ? pa::launch_decode_vector(a, stream, &merged)
+                            : pa::launch_decode_mq(a, stream);
+  if (e == hipSuccess && a.s_max > 1 && !merged) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);
 }
 
@@ -535,9 +537,10 @@ pa_status run_append_decode(pa::DecodeArgs& a, size_t need, void* workspace,
   if (a.batch == 0) return PA_OK;
   if (need > 0)
     pa::carve_workspace(workspace, a.batch, 1, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
-                        &a.part_lse);
-  hipError_t e = pa::launch_decode_vector(a, stream);
-  if (e == hipSuccess && a.s_max > 1) e = pa::launch_lse_reduce(a, stream);
+                        &a.part_lse, &a.merge_counts);
+  bool merged = false;
+  hipError_t e = pa::launch_decode_vector(a, stream, &merged);
+  if (e == hipSuccess && a.s_max > 1 && !merged) e = pa::launch_lse_reduce(a, stream);
   return map_hip(e);
 }
 

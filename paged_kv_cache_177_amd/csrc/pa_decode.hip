@@ -26,8 +26,10 @@
 //     rounding. Only a chunk's partial last block runs the masked update.
 //   * At the end the lanes' streams are merged to a common max (DPP inside 16-lane rows, a
 //     swizzle across rows, a swap across half-waves), then the waves through LDS. One split
-//     writes out/lse; several write normalised partials plus their log-sum-exp for
-//     lse_reduce_kernel.
+//     writes out/lse; several write normalised partials plus their log-sum-exp. When no row of
+//     the launch has more than 16 splits, the split grid merges them itself: the workgroup that
+//     finishes a (row, KV head)'s last split merges its heads (see merge_if_last); otherwise
+//     lse_reduce_kernel runs after the launch. Both merges give the same bits.
 //   * Three launch shapes run the same chunks: a grid of one workgroup per (g, b, s) whose
 //     workgroups past a row's last split exit at once; for rows long enough for many splits, a
 //     compact grid whose workgroups map to the chunks through the rows' lengths (batches of at
@@ -53,6 +55,11 @@
 // instead (see decode_vector_kernel), 0 = the persistent kernel.
 #ifndef PA_DECODE_COMPACT
 #define PA_DECODE_COMPACT 1
+#endif
+// 1 = the split grid merges the splits of rows with at most 16 splits itself (no second launch);
+// 0 = lse_reduce_kernel always does.
+#ifndef PA_DECODE_GRID_MERGE
+#define PA_DECODE_GRID_MERGE 1
 #endif
 
 namespace pa {
@@ -592,8 +599,16 @@ struct Worker {
         if (a.lse != nullptr && d == 0) a.lse[(size_t)ch.row * H_q + hq] = lse2 * kLn2;
       } else {
         const size_t pr = ((size_t)ch.row * H_q + hq) * a.s_max + ch.split;
-        a.part_o[pr * D + d] = o;
-        if (d == 0) a.part_lse[pr] = lse2;
+        if (a.merge_counts != nullptr) {
+          // merged in this launch, maybe on another XCD: device-coherent stores (through this
+          // XCD's L2), so no cache-wide write-back is needed before the count
+          __hip_atomic_store(&a.part_o[pr * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d == 0)
+            __hip_atomic_store(&a.part_lse[pr], lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          a.part_o[pr * D + d] = o;
+          if (d == 0) a.part_lse[pr] = lse2;
+        }
       }
     }
   }
@@ -614,6 +629,91 @@ __device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_
     *gap_shift = 0;
     return clampi(a.kv_lens[row], 0, a.max_kv_len);
   }
+}
+
+// ---- merge of a row's splits inside the split grid ----------------------------------------------
+// In a launch where no row has more than kGridMergeSplits splits, the workgroup that finishes the
+// last split of a (row, KV head) -- known from a count of finished splits in the workspace --
+// merges the partials of the G query heads, one wave per head. The arithmetic is that of
+// lse_reduce_kernel's single-wave merge (which every row of at most 16 splits takes there): the
+// same maximum, the weights summed by lane and then across the wave, the outputs accumulated in
+// split order. A row therefore gets the same bits whichever of the two merges it.
+constexpr int kGridMergeSplits = 16;
+
+// A load that sees device-coherent stores of other workgroups (it does not hit stale lines of this
+// XCD's L2).
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+__device__ __forceinline__ void merge_splits_one_wave(const DecodeArgs& a, int row, int hq, int ns,
+                                                      int lane) {
+  const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
+  const float* po = a.part_o + base * D;
+  // every split's output in one round of loads (indices clamped to the last split; the extra
+  // slots are never summed)
+  float v0[kGridMergeSplits], v1[kGridMergeSplits];
+#pragma unroll
+  for (int i = 0; i < kGridMergeSplits; ++i) {
+    const int si = i < ns ? i : ns - 1;
+    v0[i] = lane < D ? coherent_load(po + (size_t)si * D + lane) : 0.f;
+    v1[i] = D > 64 ? coherent_load(po + (size_t)si * D + 64 + lane) : 0.f;
+  }
+  const float ls = lane < ns ? coherent_load(a.part_lse + base + lane) : kNegInf;
+  float mx = ls;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
+  float W = 0.f;
+  W += w;
+  const int wb = __builtin_bit_cast(int, w);
+  float A0 = 0.f, A1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < kGridMergeSplits; k += 8) {
+    if (k < ns) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // lanes past the splits hold w = 0, and their slots add 0 * 0
+        const bool ok = k + i < ns;
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, k + i));
+        A0 = fmaf(wk, ok ? v0[k + i] : 0.f, A0);
+        A1 = fmaf(wk, ok ? v1[k + i] : 0.f, A1);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  float* out = a.out + ((size_t)row * a.H_q + hq) * D;
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  if (lane < D) out[lane] = A0 * inv;
+  if (D > 64) out[64 + lane] = A1 * inv;
+  if (a.lse != nullptr && lane == 0)
+    a.lse[(size_t)row * a.H_q + hq] = W > 0.f ? (mx + __log2f(W)) * kLn2 : kNegInf;
+}
+
+// Called by every thread of a workgroup whose chunk wrote its partial result with device-coherent
+// stores. No cache-wide fence is taken (an L2 write-back and invalidate per workgroup would stall
+// the whole launch): each thread waits for its own stores to be acknowledged, the workgroup meets
+// at a barrier, and only then is the count bumped; the merging wave reads with device-coherent
+// loads.
+template <int D, int G>
+__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, const Chunk& ch, int lane,
+                                              int wave, int* s_last) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* cnt = a.merge_counts + (size_t)ch.row * a.H_kv + ch.g;
+  if (threadIdx.x == 0)
+    *s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      ch.ns - 1
+                  ? 1
+                  : 0;
+  __syncthreads();
+  if (*s_last == 0) return;
+  if (threadIdx.x == 0)  // re-armed for the next call
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int h = wave; h < G; h += kWaves)
+    merge_splits_one_wave<D>(a, ch.row, ch.g * G + h, ch.ns, lane);
 }
 
 // ---- grid kernel: one workgroup per (KV head, row, split); splits past the row's end exit -------
@@ -699,6 +799,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
+  if constexpr (!COMPACT) {
+    // merge_counts is set only when no row of the launch has more than kGridMergeSplits splits
+    if (a.merge_counts != nullptr && ch.ns > 1) {
+      __shared__ int s_last;
+      merge_if_last<D, G>(a, ch, w.lane, w.wave, &s_last);
+    }
+  }
 }
 
 // ---- persistent kernel --------------------------------------------------------------------------
@@ -1127,7 +1234,11 @@ bool decode_vector_is_persistent(const DecodeArgs& a) {
 }
 
 template <typename T, int D, int G, bool PADDED>
-hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_layout(const DecodeArgs& args, hipStream_t stream, bool* merged) {
+  // only the split grid merges its own splits (and only for rows of at most kGridMergeSplits)
+  DecodeArgs a = args;
+  a.merge_counts = nullptr;
+  *merged = false;
   const long long items = (long long)a.batch * a.H_kv * a.s_max;
   // Rows long enough for many splits: the split grid would cover s_max splits of every row, and
   // the rows' differing lengths leave many of its workgroups with nothing to do, so the persistent
@@ -1154,6 +1265,11 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
+  if (PA_DECODE_GRID_MERGE && args.merge_counts != nullptr && a.s_max > 1 &&
+      a.s_max <= kGridMergeSplits) {
+    a.merge_counts = args.merge_counts;
+    *merged = true;
+  }
   dim3 grid(a.H_kv, a.batch, a.s_max);
   hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED, false>), grid, dim3(64 * kWaves), 0,
                      stream, a);
@@ -1161,36 +1277,38 @@ hipError_t launch_layout(const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <typename T, int D, int G>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  return a.layout == PA_PADDED ? launch_layout<T, D, G, true>(a, stream)
-                               : launch_layout<T, D, G, false>(a, stream);
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream, bool* merged) {
+  return a.layout == PA_PADDED ? launch_layout<T, D, G, true>(a, stream, merged)
+                               : launch_layout<T, D, G, false>(a, stream, merged);
 }
 
 template <typename T, int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream, bool* merged) {
   switch (a.H_q / a.H_kv) {
-    case 1: return launch_typed<T, D, 1>(a, stream);
-    case 2: return launch_typed<T, D, 2>(a, stream);
-    case 4: return launch_typed<T, D, 4>(a, stream);
-    case 8: return launch_typed<T, D, 8>(a, stream);
+    case 1: return launch_typed<T, D, 1>(a, stream, merged);
+    case 2: return launch_typed<T, D, 2>(a, stream, merged);
+    case 4: return launch_typed<T, D, 4>(a, stream, merged);
+    case 8: return launch_typed<T, D, 8>(a, stream, merged);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream, bool* merged) {
   switch (a.D) {
-    case 32: return launch_d<T, 32>(a, stream);
-    case 64: return launch_d<T, 64>(a, stream);
-    case 128: return launch_d<T, 128>(a, stream);
+    case 32: return launch_d<T, 32>(a, stream, merged);
+    case 64: return launch_d<T, 64>(a, stream, merged);
+    case 128: return launch_d<T, 128>(a, stream, merged);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream) {
-  return a.dtype == PA_F32 ? launch_t<float>(a, stream) : launch_t<__bf16>(a, stream);
+hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream, bool* merged) {
+  *merged = false;
+  return a.dtype == PA_F32 ? launch_t<float>(a, stream, merged)
+                           : launch_t<__bf16>(a, stream, merged);
 }
 
 template <bool PADDED>

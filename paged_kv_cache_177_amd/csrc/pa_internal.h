@@ -77,6 +77,8 @@ struct DecodeArgs {
   float* part_o;    // [batch][n_q*H_q][s_max][D]
   float* part_lse;  // [batch][n_q*H_q][s_max] (log2 domain)
   int* counter;     // work counter of the persistent decode kernel (0 between calls), or NULL
+  int* merge_counts;  // [batch][H_kv] finished splits per (row, KV head) when the split grid
+                     // merges its own partials (0 between calls), else NULL
   int mq_tiles;     // multi-query path: 16-row query tiles per (row, KV head)
   // block-sparse multi-query path: keep flags [batch][ceil(n_q / 16)][mask_kv_blocks], or NULL
   const uint8_t* block_mask;
@@ -99,22 +101,33 @@ struct DecodeArgs {
 //   [256 B: work counter (int) of the persistent kernel; must be 0 before the first call, each call
 //    leaves it 0] [split partial outputs, fp32] [split partial log-sum-exps, fp32]
 constexpr size_t kCounterBytes = 256;
+// Workspace of a decode with splits, in this order: the persistent kernel's work counter (256
+// bytes), one finished-split count per (row, query head) (a bound of the split grid's per (row,
+// KV head) counts, 256-byte rounded; reserved for every call so that partials never land there),
+// the partial outputs and their log-sum-exp. The counters lead, at offsets that depend on batch x
+// H_q only, so calls of other split counts can share a workspace: every call leaves them at zero.
+inline size_t merge_count_bytes(int batch, int H_q) {
+  return ((size_t)batch * (size_t)H_q * sizeof(int) + 255) & ~(size_t)255;
+}
+
 inline size_t decode_workspace_bytes(int batch, int n_q, int H_q, int D, int s_max) {
   if (s_max <= 1) return 0;
   size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
-  size_t bytes = kCounterBytes;
+  size_t bytes = kCounterBytes + merge_count_bytes(batch, H_q);
   bytes += (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
   bytes += (rows * sizeof(float) + 255) & ~(size_t)255;
   return bytes;
 }
 
 inline void carve_workspace(void* ws, int batch, int n_q, int H_q, int D, int s_max,
-                            int** counter, float** part_o, float** part_lse) {
+                            int** counter, float** part_o, float** part_lse, int** merge_counts) {
   size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
+  size_t c_bytes = merge_count_bytes(batch, H_q);
   size_t o_bytes = (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
   *counter = (int*)ws;
-  *part_o = (float*)((char*)ws + kCounterBytes);
-  *part_lse = (float*)((char*)ws + kCounterBytes + o_bytes);
+  *merge_counts = n_q == 1 ? (int*)((char*)ws + kCounterBytes) : nullptr;
+  *part_o = (float*)((char*)ws + kCounterBytes + c_bytes);
+  *part_lse = (float*)((char*)ws + kCounterBytes + c_bytes + o_bytes);
 }
 
 // ---- launchers (each returns the hipGetLastError of its launches) -----------------------------
@@ -146,7 +159,8 @@ hipError_t launch_pack_projection(const void* w, void* packed, int out_features,
                                   hipStream_t stream);
 hipError_t launch_advance(int32_t* positions, int32_t* kv_lens, int32_t* dest, int batch,
                           hipStream_t stream);
-hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream);  // n_q == 1
+// n_q == 1; *merged tells whether the launch also merged the splits (no lse_reduce needed)
+hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t stream, bool* merged);
 hipError_t launch_decode_mq(const DecodeArgs& a, hipStream_t stream);      // n_q > 1
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
 

@@ -153,11 +153,22 @@ class PaddedLockstep:
         self.kv = B.alloc_pool(desc, device=device, stream=stream)
         self.rope = rope_max_pos > 0
         self._ws = None
+        self._ws_batch = None
 
     def append(self, positions, dest, k_new, v_new, q_in=None, q_out=None):
         B.pa_append_kv(self.kv.pool, None, 1, positions, dest, k_new, v_new, q_in, q_out,
                        self.H_q if q_in is not None else 0, positions.shape[0],
                        stream=self.stream)
+
+    def _workspace_for(self, need: int, batch: int):
+        # one workspace for every call: grown when too small, and zero-filled again when the
+        # batch changes (its counters sit at offsets set by batch x heads)
+        if need > 0 and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        elif need > 0 and self._ws_batch != batch:
+            self._ws.zero_()
+        if need > 0:
+            self._ws_batch = batch
 
     def decode(self, q, gap_start, gap_end, kv_cols: int, scale: float):
         batch = q.shape[0]
@@ -165,8 +176,7 @@ class PaddedLockstep:
         lse = torch.empty((batch, self.H_q), dtype=torch.float32, device=self.device)
         need = B.pa_decode_attention_padded(self.kv.pool, q, self.H_q, batch, gap_start, gap_end,
                                             kv_cols, scale, out=out, query_workspace=True)
-        if need > 0 and (self._ws is None or self._ws.numel() < need):
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        self._workspace_for(need, batch)
         B.pa_decode_attention_padded(self.kv.pool, q, self.H_q, batch, gap_start, gap_end, kv_cols,
                                      scale, workspace=self._ws if need > 0 else None, out=out,
                                      lse=lse, stream=self.stream)
@@ -182,8 +192,7 @@ class PaddedLockstep:
         need = B.pa_append_decode_attention_padded(self.kv.pool, positions, dest, k_new, v_new, q,
                                                    q_out, self.H_q, gap_start, gap_end, kv_cols,
                                                    batch, scale, out=out, query_workspace=True)
-        if need > 0 and (self._ws is None or self._ws.numel() < need):
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        self._workspace_for(need, batch)
         B.pa_append_decode_attention_padded(self.kv.pool, positions, dest, k_new, v_new, q, q_out,
                                             self.H_q, gap_start, gap_end, kv_cols, batch, scale,
                                             workspace=self._ws if need > 0 else None, out=out,

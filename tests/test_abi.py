@@ -118,15 +118,19 @@ def test_decode_workspace_query():
     # max_kv_len 8193 -> 9 splits
     need = B.pa_decode_attention(p, FAKE, 32 * 64, 1, 32, FAKE, 513, FAKE, 128, 8193, 0.125,
                                  out=FAKE, query_workspace=True)
+    # the work counter, one finished-split count per (row, head) (sized by the query heads),
+    # partial outputs, partial log-sum-exp
     rows = 128 * 32 * 9
     o = (rows * 64 * 4 + 255) // 256 * 256
-    assert need == 256 + o + (rows * 4 + 255) // 256 * 256
+    counts = (128 * 32 * 4 + 255) // 256 * 256
+    assert need == 256 + o + (rows * 4 + 255) // 256 * 256 + counts
     # head_dim 128 uses 512-token chunks
     p = _fake_pool(head_dim=128)
     need = B.pa_decode_attention(p, FAKE, 32 * 128, 1, 32, FAKE, 64, FAKE, 4, 1024, 0.1,
                                  out=FAKE, query_workspace=True)
     rows = 4 * 32 * 2
-    assert need == 256 + (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert need == (256 + (4 * 32 * 4 + 255) // 256 * 256 + (rows * 128 * 4 + 255) // 256 * 256
+                    + (rows * 4 + 255) // 256 * 256)
 
 
 @pytest.mark.parametrize("kw,status", [

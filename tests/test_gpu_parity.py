@@ -208,6 +208,37 @@ def test_compact_grid_at_its_64_row_limit():
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+def test_grid_merge_repeated_calls_and_shared_workspace():
+    """The split grid merges a (row, KV head)'s splits in its own launch, through finished-split
+    counts in the workspace that every call leaves at zero. 40 calls in a row give the same bits;
+    two batches of other split counts (same rows and heads) that take turns on one workspace give
+    the bits of fresh workspaces; the first call agrees with the oracle."""
+    rng = np.random.default_rng(90)
+    n_a = rng.integers(0, 9000, 128)
+    n_a[:4] = [0, 1023, 1024, 8999]
+    n_b = rng.integers(0, 4000, 128)
+    a = W.make_paged_case("grid-merge-a", 91, n_a, 32, 8, 64, "bf16")
+    b = W.make_paged_case("grid-merge-b", 92, n_b, 32, 8, 64, "bf16")
+    ra, _, _ = run_and_check_paged(a, rows=[0, 1, 2, 3, 50, 127])
+    rb, _, _ = run_and_check_paged(b, rows=[0, 64, 127])
+    ref = {id(ra): (ra.out.clone(), ra.lse.clone()), id(rb): (rb.out.clone(), rb.lse.clone())}
+    outs = []
+    for _ in range(40):
+        ra.decode()
+        outs.append((ra.out.clone(), ra.lse.clone()))
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref[id(ra)][0]) and torch.equal(l, ref[id(ra)][1])
+    assert ra.workspace.numel() >= rb.workspace.numel()
+    rb.workspace = ra.workspace  # 9 and 4 splits at most: the partials move, the counts stay
+    for _ in range(5):
+        for r in (ra, rb, rb, ra):
+            r.out.zero_()
+            r.decode()
+            torch.cuda.synchronize()
+            assert torch.equal(r.out, ref[id(r)][0]) and torch.equal(r.lse, ref[id(r)][1])
+
+
 @pytest.mark.parametrize("kind", ["b128-tp2", "b128-dp2", "long-sp4"])
 def test_one_gpu_shares_sampled_rows(kind):
     """One GPU's share of a sharded step at its real shape (the lengths of the whole workload, cut
