@@ -113,3 +113,34 @@ def test_padded_long_rows_multiwave_merge():
     c = W.make_paged_case("padded-long", 34, [99, 20 * 1024 + 7, 70 * 1024 - 9], 8, 2, 64,
                           "bf16")
     run_and_check_padded(W.padded_from_paged(c))
+
+
+def test_padded_runner_shares_its_workspace_across_batch_sizes():
+    """One PaddedLockstep keeps one workspace. Its finished-split counts sit at offsets set by
+    batch x heads, so a smaller batch's partials land on a larger batch's counts; the runner
+    zero-fills the workspace again when the batch changes. A call over the first 16 rows between
+    two calls over all 64 (rows of up to 3 splits, merged inside the split grid) gives rows 0-15
+    of the 64-row result, and the second 64-row call the bits of the first."""
+    rng = np.random.default_rng(37)
+    n = rng.integers(1, 3000, 64)
+    c = W.make_paged_case("padded-ws", 37, n, 8, 2, 64, "bf16")
+    pc = W.padded_from_paged(c, seq_cap=3100)
+    dev = "cuda"
+    L = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
+                       pc.seq_cap)
+    L.kv.k.copy_(to_torch(pc.k_pad, pc.dtype))
+    L.kv.v.copy_(to_torch(pc.v_pad, pc.dtype))
+    L.append(torch.from_numpy(pc.positions).to(dev), torch.from_numpy(pc.dest).to(dev),
+             to_torch(pc.k_new, pc.dtype).to(dev), to_torch(pc.v_new, pc.dtype).to(dev),
+             None, None)
+    q = to_torch(pc.q, pc.dtype).to(dev)
+    gs = torch.from_numpy(pc.prefix_lens.astype(np.int32)).to(dev)
+    ge = torch.from_numpy(np.full(pc.batch, pc.padded_len, np.int32)).to(dev)
+    o1, l1 = L.decode(q, gs, ge, pc.kv_cols, pc.scale)
+    o2, l2 = L.decode(q[:16].contiguous(), gs[:16].contiguous(), ge[:16].contiguous(),
+                      pc.kv_cols, pc.scale)
+    o3, l3 = L.decode(q, gs, ge, pc.kv_cols, pc.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all()
+    assert torch.equal(o2, o1[:16]) and torch.equal(l2, l1[:16])
+    assert torch.equal(o3, o1) and torch.equal(l3, l1)
