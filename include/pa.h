@@ -16,7 +16,8 @@
  *   - the lockstep form over right-padded per-row KV with one padding gap per row
  *     ("helexa PR #121", commit "slice 1": assemble_batch, batch_decode_mask);
  *   - the append with a per-head RMSNorm of the keys (and queries) before the rotation
- *     (pa_append_kv_qk_norm; "NeuroGrid releases", v0.7.0, LFM2 notes);
+ *     (pa_append_kv_qk_norm; "NeuroGrid releases", v0.5.0 "LFM2 Hybrid Architecture Support",
+ *     Architecture: per-head RMSNorm of Q and K ahead of the rotation);
  *   - advancing a lockstep batch's positions and lengths on the device, so a recorded decode step
  *     can be replayed token after token (pa_advance_lockstep; "NeuroGrid releases", v0.8.0
  *     "CUDA Graphs");
@@ -127,7 +128,8 @@ pa_status pa_append_kv(const pa_pool* pool, const int32_t* block_tables, int32_t
                        int32_t batch, hipStream_t stream);
 
 /* Append one token per row, with per-head RMSNorm of the new key (and query) before RoPE
- * ("NeuroGrid releases", v0.7.0 LFM2 notes: QK LayerNorm, per-head RMSNorm on Q/K before RoPE).
+ * ("NeuroGrid releases", v0.5.0 "LFM2 Hybrid Architecture Support", Architecture: a per-head
+ * RMSNorm of queries and keys, applied before RoPE).
  *
  * As pa_append_kv, except that every key head x (D elements, fp32 from the pool dtype) -- and every
  * query head when q_in is given -- is first replaced by y_i = (x_i * r) * w_i with
@@ -160,22 +162,23 @@ pa_status pa_append_kv_qk_norm(const pa_pool* pool, const int32_t* block_tables,
  * multi-query path (matrix cores). The split of a row depends on its own kv_len only, so a row's
  * result does not depend on the rest of the batch.
  * Workspace: with workspace_needed != NULL the call only writes the bytes it needs for these
- * arguments there and launches nothing; otherwise workspace must hold that many bytes (it may be
- * NULL when none are needed). A workspace must be zero-filled before its first use: it starts with
- * counters that every call leaves at zero again, the work counter of the split kernels (256 bytes)
- * and one finished-split count per (row, query head) (4 * batch * num_q_heads bytes, rounded up
- * to 256), with the partial results after them. Calls may share a workspace while batch *
- * num_q_heads stays the same (their split counts may differ); after a change, zero-fill it again
- * (a smaller call's partials overwrite a larger one's counts). Calls that overlap in time (other
- * streams) need workspaces of their own. max_kv_len is a host upper bound of kv_lens
- * (<= bt_stride * 16).
+ * arguments there and launches nothing; otherwise workspace must hold that many bytes and be
+ * 256-byte aligned (it may be NULL when none are needed). A workspace must be zero-filled before
+ * its first use: it starts with counters that every call leaves at zero again, the work counter of
+ * the split kernels (256 bytes) and one finished-split count per (row, query head) (4 * batch *
+ * num_q_heads bytes, rounded up to 256), with the partial results after them. Calls may share a
+ * workspace while batch * num_q_heads stays the same (their split counts may differ); after a
+ * change, zero-fill it again (a smaller call's partials overwrite a larger one's counts). A call
+ * that returns PA_ERR_HIP may have stopped with its counters raised: zero-fill the workspace
+ * again before the next call uses it. Calls that overlap in time (other streams) need workspaces
+ * of their own. max_kv_len is a host upper bound of kv_lens (<= bt_stride * 16).
  * Preconditions (clamped, not checked): 0 <= kv_lens[b] <= max_kv_len; block ids < num_blocks.
  * Errors: PA_ERR_NULL (pool, q, block_tables, kv_lens, out); PA_ERR_SHAPE (batch < 0 or > 65535,
  * n_q < 1, num_q_heads not a positive multiple of H_kv, max_kv_len < 0 or > bt_stride * 16, more
  * than 65535 splits for max_kv_len, layout not PA_PAGED, scale negative or not finite, q not
  * 16-byte aligned or q_row_stride not a multiple of 16 bytes); PA_ERR_UNSUPPORTED (n_q == 1 with G
- * not in {1, 2, 4, 8}; n_q > 1 with an fp32 pool); PA_ERR_CAPACITY (workspace too small).
- * batch == 0 is a no-op. */
+ * not in {1, 2, 4, 8}; n_q > 1 with an fp32 pool); PA_ERR_CAPACITY (workspace too small or not
+ * 256-byte aligned). batch == 0 is a no-op. */
 pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_stride,
                               int32_t n_q, int32_t num_q_heads, const int32_t* block_tables,
                               int32_t bt_stride, const int32_t* kv_lens, int32_t batch,
@@ -273,7 +276,8 @@ pa_status pa_decode_attention_block_sparse(const pa_pool* pool, const void* q,
  * Errors: PA_ERR_NULL (pool, q, gap_start, gap_end, out); PA_ERR_SHAPE (batch < 0, > batch_cap
  * or > 65535, kv_cols < 0 or > seq_cap, more than 65535 splits for kv_cols, num_q_heads not a positive multiple of H_kv, layout not PA_PADDED,
  * scale negative or not finite, q not 16-byte aligned);
- * PA_ERR_UNSUPPORTED (G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace too small). */
+ * PA_ERR_UNSUPPORTED (G not in {1, 2, 4, 8}); PA_ERR_CAPACITY (workspace too small or not
+ * 256-byte aligned). */
 pa_status pa_decode_attention_padded(const pa_pool* padded_pool, const void* q,
                                      int32_t num_q_heads, int32_t batch, const int32_t* gap_start,
                                      const int32_t* gap_end, int32_t kv_cols, float scale,
@@ -326,8 +330,9 @@ pa_status pa_append_decode_attention_padded(const pa_pool* padded_pool, const in
                                             float* lse, hipStream_t stream);
 
 /* Merge partial attention results computed over disjoint key sets (the step after an all-gather
- * when one row's keys are split across GPUs; "NeuroGrid releases", v0.6.0 "Flash Decode Attention
- * Kernel": partial softmax statistics combined through their maxima).
+ * when one row's keys are split across GPUs). The pages never split a row; this is the log-sum-exp
+ * merge of this library's own split-K design, the algebra pa_decode_attention applies to the
+ * chunks of a long row.
  *
  * out_parts: fp32 [num_parts][n][head_dim], each part's normalised output for n (row, query head)
  * pairs; lse_parts: fp32 [num_parts][n], each part's log-sum-exp (natural log, -inf for a part

@@ -8,6 +8,8 @@ Sources (page title, then section):
             block tables, a paged-attention kernel that reads K/V through the block table, GQA.
   [NG-0.6]  NeuroGrid releases, v0.6.0 "Flash Decode Attention Kernel": online softmax over KV
             tiles without materialising the score matrix.
+  [NG-0.5]  NeuroGrid releases, v0.5.0 "LFM2 Hybrid Architecture Support", Architecture: a
+            per-head RMSNorm of the queries and keys, applied before RoPE.
   [NG-0.8]  NeuroGrid releases, v0.8.0 "Key Changes": lengths read from device buffers,
             kv_len = position + 1.
   [HX-1]    helexa PR #121 "continuous batching -- batched decode + engine", commit "slice 1"
@@ -127,10 +129,10 @@ def rope_rotate_f32(x32: np.ndarray, c32: np.ndarray, s32: np.ndarray) -> np.nda
 
 
 # --------------------------------------------------------------------------------------------
-# Per-head QK RMSNorm [NG-0.7 LFM2]
+# Per-head QK RMSNorm [NG-0.5]
 # --------------------------------------------------------------------------------------------
 def rms_norm_head_f32(x32: np.ndarray, w32: np.ndarray, eps: float) -> np.ndarray:
-    """Per-head RMSNorm on a query or key head before RoPE [NG-0.7 LFM2]: y = x * r * w with
+    """Per-head RMSNorm on a query or key head before RoPE [NG-0.5]: y = x * r * w with
     r = 1 / sqrt(mean(x^2) + eps), in fp32.
 
     The pages fix no arithmetic; the reading taken (the library's contract, chosen so that results
@@ -138,7 +140,15 @@ def rms_norm_head_f32(x32: np.ndarray, w32: np.ndarray, eps: float) -> np.ndarra
     rounded fp32 operation, y_i = (x_i * r) * w_i, mean = ss / D, and the sum of squares ss runs
     over the rotate-half pairs first, s_i = x_i * x_i + x_{i+D/2} * x_{i+D/2} (i < D/2), then a
     pairwise tree over i that adds neighbours at every level: (s_0 + s_1), (s_2 + s_3), ..., then
-    those sums in pairs, and so on. x32 (..., D); w32 (D,); eps a float (rounded to fp32)."""
+    those sums in pairs, and so on. x32 (..., D); w32 (D,); eps a float (rounded to fp32).
+
+    That summation order is not from the pages: it was chosen to be the order in which the GPU
+    kernel's lanes can form the sum (one lane per rotate-half pair, then a butterfly across
+    neighbouring lanes), so that a bit-exact comparison is possible at all. A bit match with the
+    kernel therefore shows that the kernel follows this order, nothing more. What pins the
+    function to the mathematics is its distance from RMSNorm computed in fp64 and by torch
+    (test_rms_norm_close_to_fp64_and_torch: within a few fp32 ulps) and the closed forms in the
+    same test file (constant heads, power-of-two scaling, weights, zero heads)."""
     x = np.asarray(x32, dtype=np.float32)
     w = np.asarray(w32, dtype=np.float32)
     D = x.shape[-1]
@@ -168,7 +178,7 @@ def append_kv(k_pool, v_pool, dtype, layout, block_tables, positions, dest, k_ne
     (block_tables[b][dest // 16], dest % 16) for the paged layout, column ``dest`` for the padded
     one. The value is stored unchanged. ``q_in`` (if given) is rotated at the same positions.
     With ``k_norm_w``/``q_norm_w`` (fp32 (D,)) and ``norm_eps``, every key head (and query head) is
-    RMS-normalised first (``rms_norm_head_f32``), then rotated [NG-0.7 LFM2: per-head RMSNorm on
+    RMS-normalised first (``rms_norm_head_f32``), then rotated [NG-0.5: per-head RMSNorm on
     Q/K before RoPE]. Returns (k_pool', v_pool', q_out or None).
     """
     norm = k_norm_w is not None

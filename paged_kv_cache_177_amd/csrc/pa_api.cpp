@@ -319,6 +319,8 @@ pa_status run_decode(pa::DecodeArgs& a, size_t need, void* workspace, size_t wor
     return PA_OK;
   }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_CAPACITY;
+  // counters are updated by device-scope atomics and partials stored as aligned vectors
+  if (need > 0 && ((uintptr_t)workspace % 256) != 0) return PA_ERR_CAPACITY;
   if (a.batch == 0) return PA_OK;
   if (need > 0)
     pa::carve_workspace(workspace, a.batch, a.n_q, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
@@ -534,6 +536,8 @@ pa_status run_append_decode(pa::DecodeArgs& a, size_t need, void* workspace,
     return PA_OK;
   }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_CAPACITY;
+  // counters are updated by device-scope atomics and partials stored as aligned vectors
+  if (need > 0 && ((uintptr_t)workspace % 256) != 0) return PA_ERR_CAPACITY;
   if (a.batch == 0) return PA_OK;
   if (need > 0)
     pa::carve_workspace(workspace, a.batch, 1, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,

@@ -4,9 +4,9 @@
 // Each part p holds, for every (row, query head) n, the part's normalised output o_p[n][0..D) and
 // its log-sum-exp l_p[n] (natural log; -inf for a part with no keys). The merged result is
 //   M = max_p l_p,  w_p = exp(l_p - M),  out = sum_p w_p o_p / sum_p w_p,  lse = M + log sum_p w_p
-// -- the same algebra as the split-K merge of the decode (NeuroGrid releases, v0.6.0 "Flash Decode
-// Attention Kernel": partial softmax statistics combined by their running maxima), with a part of
-// weight 0 dropping out and out = 0, lse = -inf when every part is empty. Parts are summed in
+// -- the same algebra as the library's own split-K merge of a long row's chunks (the pages never
+// split a row, so this step is the library's design, not theirs), with a part of weight 0 dropping
+// out and out = 0, lse = -inf when every part is empty. Parts are summed in
 // index order, so the result does not depend on the launch geometry.
 //
 // One wave per (row, head) n: lane i owns dims i and i + 64. The parts' lse values are read 64 at a

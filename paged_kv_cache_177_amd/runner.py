@@ -6,10 +6,18 @@ Nothing here computes any part of attention: it copies arrays and calls the C AB
 
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 import torch
 
 from . import binding as B
+
+
+def on_stream(stream):
+    """Context in which torch's allocations and fills are ordered on ``stream`` (None: the current
+    stream), the stream the library calls of a runner are enqueued on."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def to_torch(a: np.ndarray, dtype: str) -> torch.Tensor:
@@ -68,9 +76,11 @@ class PagedStep:
                                      self.block_tables, self.bt_stride, self.kv_lens, self.batch,
                                      self.max_kv_len, case.scale, out=self.out,
                                      query_workspace=True)
-        # zero-filled once: its first bytes are the decode kernel's work counter
-        self.workspace = (torch.zeros(need, dtype=torch.uint8, device=device) if need > 0
-                          else None)
+        # zero-filled once: its first bytes are the decode kernel's work counter; allocated and
+        # filled on the calls' stream, so the fill is ordered before their first launch
+        with on_stream(stream):
+            self.workspace = (torch.zeros(need, dtype=torch.uint8, device=device) if need > 0
+                              else None)
 
     @property
     def q_decode(self) -> torch.Tensor:
@@ -162,18 +172,26 @@ class PaddedLockstep:
 
     def _workspace_for(self, need: int, batch: int):
         # one workspace for every call: grown when too small, and zero-filled again when the
-        # batch changes (its counters sit at offsets set by batch x heads)
-        if need > 0 and (self._ws is None or self._ws.numel() < need):
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
-        elif need > 0 and self._ws_batch != batch:
-            self._ws.zero_()
+        # batch changes (its counters sit at offsets set by batch x heads). Allocation and fill
+        # run on the calls' stream, so they are ordered after the previous call (whose last
+        # workgroups re-arm the counters) and before the next one.
+        with on_stream(self.stream):
+            if need > 0 and (self._ws is None or self._ws.numel() < need):
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            elif need > 0 and self._ws_batch != batch:
+                self._ws.zero_()
         if need > 0:
             self._ws_batch = batch
 
+    def _outputs(self, batch: int):
+        with on_stream(self.stream):
+            out = torch.empty((batch, self.H_q, self.D), dtype=torch.float32, device=self.device)
+            lse = torch.empty((batch, self.H_q), dtype=torch.float32, device=self.device)
+        return out, lse
+
     def decode(self, q, gap_start, gap_end, kv_cols: int, scale: float):
         batch = q.shape[0]
-        out = torch.empty((batch, self.H_q, self.D), dtype=torch.float32, device=self.device)
-        lse = torch.empty((batch, self.H_q), dtype=torch.float32, device=self.device)
+        out, lse = self._outputs(batch)
         need = B.pa_decode_attention_padded(self.kv.pool, q, self.H_q, batch, gap_start, gap_end,
                                             kv_cols, scale, out=out, query_workspace=True)
         self._workspace_for(need, batch)
@@ -187,8 +205,7 @@ class PaddedLockstep:
         """append + decode in one call (pa_append_decode_attention_padded): the same results as
         append() followed by decode() on the rotated queries."""
         batch = q.shape[0]
-        out = torch.empty((batch, self.H_q, self.D), dtype=torch.float32, device=self.device)
-        lse = torch.empty((batch, self.H_q), dtype=torch.float32, device=self.device)
+        out, lse = self._outputs(batch)
         need = B.pa_append_decode_attention_padded(self.kv.pool, positions, dest, k_new, v_new, q,
                                                    q_out, self.H_q, gap_start, gap_end, kv_cols,
                                                    batch, scale, out=out, query_workspace=True)

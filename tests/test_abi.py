@@ -174,6 +174,32 @@ def test_decode_needs_a_big_enough_workspace():
     assert st == B.PA_ERR_CAPACITY
 
 
+@pytest.mark.parametrize("offset", [4, 16, 128])
+def test_workspace_must_be_256_byte_aligned(offset):
+    """Counters in the workspace take device-scope atomics and partials aligned vector stores: a
+    workspace off a 256-byte boundary is refused (large enough or not) before any launch, by the
+    paged, padded and fused calls alike."""
+    lib = B.load_library()
+    p = _fake_pool()
+    big = 1 << 30
+    st = lib.pa_decode_attention(ctypes.byref(p), FAKE, 32 * 64, 1, 32, FAKE, 513, FAKE, 128,
+                                 8193, ctypes.c_float(0.125), FAKE + offset, big, None, FAKE,
+                                 None, None)
+    assert st == B.PA_ERR_CAPACITY
+    st = lib.pa_append_decode_attention(ctypes.byref(p), FAKE, 513, FAKE, None, FAKE, FAKE, FAKE,
+                                        FAKE + 0x100000, 32, FAKE, 128, 8193,
+                                        ctypes.c_float(0.125), FAKE + offset, big, None, FAKE,
+                                        None, None)
+    assert st == B.PA_ERR_CAPACITY
+    padded = B.Pool()
+    padded.desc = B.make_desc("padded", "bf16", 8, 64, batch_cap=4, seq_cap=3000)
+    padded.k, padded.v = 0x10000, 0x20000
+    st = lib.pa_decode_attention_padded(ctypes.byref(padded), FAKE, 32, 4, FAKE, FAKE, 2500,
+                                        ctypes.c_float(0.125), FAKE + offset, big, None, FAKE,
+                                        None, None)
+    assert st == B.PA_ERR_CAPACITY
+
+
 def test_layout_mismatch_and_null_pool():
     lib = B.load_library()
     padded = B.Pool()

@@ -115,19 +115,23 @@ def test_padded_long_rows_multiwave_merge():
     run_and_check_padded(W.padded_from_paged(c))
 
 
-def test_padded_runner_shares_its_workspace_across_batch_sizes():
+@pytest.mark.parametrize("side_stream", [False, True])
+def test_padded_runner_shares_its_workspace_across_batch_sizes(side_stream):
     """One PaddedLockstep keeps one workspace. Its finished-split counts sit at offsets set by
     batch x heads, so a smaller batch's partials land on a larger batch's counts; the runner
     zero-fills the workspace again when the batch changes. A call over the first 16 rows between
     two calls over all 64 (rows of up to 3 splits, merged inside the split grid) gives rows 0-15
-    of the 64-row result, and the second 64-row call the bits of the first."""
+    of the 64-row result, and the second 64-row call the bits of the first. On a side stream the
+    runner's fills and allocations must be ordered with its launches on that stream: the three
+    calls then give the default stream's bits."""
     rng = np.random.default_rng(37)
     n = rng.integers(1, 3000, 64)
     c = W.make_paged_case("padded-ws", 37, n, 8, 2, 64, "bf16")
     pc = W.padded_from_paged(c, seq_cap=3100)
     dev = "cuda"
+    side = torch.cuda.Stream() if side_stream else None  # default priority
     L = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
-                       pc.seq_cap)
+                       pc.seq_cap, stream=side)
     L.kv.k.copy_(to_torch(pc.k_pad, pc.dtype))
     L.kv.v.copy_(to_torch(pc.v_pad, pc.dtype))
     L.append(torch.from_numpy(pc.positions).to(dev), torch.from_numpy(pc.dest).to(dev),
@@ -136,11 +140,24 @@ def test_padded_runner_shares_its_workspace_across_batch_sizes():
     q = to_torch(pc.q, pc.dtype).to(dev)
     gs = torch.from_numpy(pc.prefix_lens.astype(np.int32)).to(dev)
     ge = torch.from_numpy(np.full(pc.batch, pc.padded_len, np.int32)).to(dev)
+    q16, gs16, ge16 = q[:16].contiguous(), gs[:16].contiguous(), ge[:16].contiguous()
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())  # inputs and pool were written here
     o1, l1 = L.decode(q, gs, ge, pc.kv_cols, pc.scale)
-    o2, l2 = L.decode(q[:16].contiguous(), gs[:16].contiguous(), ge[:16].contiguous(),
-                      pc.kv_cols, pc.scale)
+    o2, l2 = L.decode(q16, gs16, ge16, pc.kv_cols, pc.scale)
     o3, l3 = L.decode(q, gs, ge, pc.kv_cols, pc.scale)
+    if side is not None:
+        torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     assert torch.isfinite(o1).all()
     assert torch.equal(o2, o1[:16]) and torch.equal(l2, l1[:16])
     assert torch.equal(o3, o1) and torch.equal(l3, l1)
+    # the same three calls on the default stream with a fresh runner: the same bits
+    if side is not None:
+        R = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
+                           pc.seq_cap)
+        R.kv.k.copy_(L.kv.k)
+        R.kv.v.copy_(L.kv.v)
+        r1, s1 = R.decode(q, gs, ge, pc.kv_cols, pc.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(r1, o1) and torch.equal(s1, l1)
