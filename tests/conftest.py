@@ -28,3 +28,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Every attention comparison against the oracle, with its observed errors (printed whether or
+    not output capture is on)."""
+    parity = sys.modules.get("_parity")
+    records = getattr(parity, "RECORDS", None)
+    if not records:
+        return
+    tr = terminalreporter
+    tr.section("attention errors against the fp64 oracle")
+    tr.write_line(f"{'comparison':<44} {'elements':>9} {'max abs':>9} {'mean abs':>9} "
+                  f"{'err/derived':>11}")
+    for r in records:
+        ratio = "" if r["ratio"] is None else f"{r['ratio']:.3f}"
+        tr.write_line(f"{r['what'][:44]:<44} {r['n']:>9} {r['max']:>9.2e} {r['mean']:>9.2e} "
+                      f"{ratio:>11}")

@@ -11,7 +11,7 @@ import workloads as W
 from paged_kv_cache_177_amd import binding as B
 from paged_kv_cache_177_amd.runner import PaddedLockstep, PagedStep, to_numpy, to_torch
 
-from _parity import assert_attention_close, bits, log, oracle_append
+from _parity import assert_attention_close, bits, check_rows, log, oracle_append
 
 pytestmark = pytest.mark.gpu
 
@@ -39,12 +39,8 @@ def fused_vs_separate(case, rows=None):
     # and the oracle
     k2, v2, q_used, _, _ = oracle_append(case)
     np.testing.assert_array_equal(bits(to_numpy(fus.kv.k, dt), dt), bits(k2, dt))
-    rows = np.arange(case.batch) if rows is None else np.asarray(rows)
-    o_ref, l_ref = O.decode_paged(k2, v2, dt, case.block_tables[rows], case.kv_lens[rows],
-                                  q_used[rows], case.scale)
-    mx, mean = assert_attention_close(fus.out.cpu().numpy()[rows], o_ref[:, 0], dt, "out")
-    assert_attention_close(fus.lse.cpu().numpy()[rows], l_ref[:, 0], dt, "lse")
-    log(f"[fused] ok case={case.name} max_err={mx:.2e} mean_err={mean:.2e}")
+    check_rows(fus.out.cpu().numpy(), fus.lse.cpu().numpy(), k2, v2, dt, case.block_tables,
+               case.kv_lens, q_used, case.scale, "fused " + case.name, rows=rows)
     return fus
 
 
@@ -68,12 +64,9 @@ def test_fused_ragged(D, G, dtype, theta):
 
 
 def test_fused_b128_full_size():
-    """The B=128 step at full size (no RoPE table): 12 rows against the oracle, all bits against
-    the separate calls."""
-    c = W.b128()
-    order = np.argsort(c.kv_lens)
-    rows = np.unique(np.concatenate([order[:3], order[-3:], order[::29]]))
-    fused_vs_separate(c, rows=rows)
+    """The B=128 step at full size (no RoPE table): every row against the oracle, all bits
+    against the separate calls."""
+    fused_vs_separate(W.b128())
 
 
 @pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32")])
@@ -93,7 +86,7 @@ def test_fused_wide_batch_persistent_kernel():
     rng = np.random.default_rng(48)
     n = np.concatenate([[21000, 17000], rng.integers(0, 400, 68)])
     case = W.make_paged_case("fused-wide", 48, n, 8, 2, 64, "bf16", rope_theta=1e4)
-    fused_vs_separate(case, rows=[0, 1, 2, 50, 69])
+    fused_vs_separate(case)
 
 
 def test_fused_destination_outside_the_row():
