@@ -186,6 +186,34 @@ pa_status pa_decode_attention(const pa_pool* pool, const void* q, int64_t q_row_
                               size_t workspace_bytes, size_t* workspace_needed /* host */,
                               float* out, float* lse, hipStream_t stream);
 
+/* Scratch of pa_decode_attention_noalloc: its size per device, and the most (row, query head)
+ * pairs of one call whose finished-split counts it reserves room for. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define PA_NOALLOC_MAX_ROW_HEADS 16384
+
+/* pa_decode_attention for callers that cannot allocate device memory: code under stream or graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same arguments, results and
+ * errors as pa_decode_attention, without the workspace: the split partials go to the library's
+ * own scratch, one PA_NOALLOC_SCRATCH_BYTES array per device, allocated with the library's code on
+ * that device and held until the process ends. The call allocates and frees nothing.
+ * Limits: a call needing more scratch than PA_NOALLOC_SCRATCH_BYTES (for the split rows: 256 +
+ * 4 * PA_NOALLOC_MAX_ROW_HEADS bytes of counters, then batch * n_q * num_q_heads * splits * (D + 1)
+ * fp32 partials, each part 256-byte rounded), or with batch * num_q_heads > PA_NOALLOC_MAX_ROW_HEADS
+ * when rows can split, returns PA_ERR_CAPACITY before any HIP call. B=128 rows of up to 8192
+ * tokens with 32 query heads at D = 64 use 8.5 MB; 4 rows of up to 131072 tokens at D = 128,
+ * 14.5 MB.
+ * Every call on a device shares that device's scratch, and each call leaves in it only zeroed
+ * counters and its own partials: calls that overlap in time on one device (other streams, other
+ * threads) race and must not be issued. The first call on a device clears the counters with a
+ * small kernel on `stream` (and so does the first call after a failed launch); under stream
+ * capture that clear is recorded too. Calls without split rows (every kv_len within one chunk)
+ * and multi-query calls use no scratch. */
+pa_status pa_decode_attention_noalloc(const pa_pool* pool, const void* q, int64_t q_row_stride,
+                                      int32_t n_q, int32_t num_q_heads,
+                                      const int32_t* block_tables, int32_t bt_stride,
+                                      const int32_t* kv_lens, int32_t batch, int32_t max_kv_len,
+                                      float scale, float* out, float* lse, hipStream_t stream);
+
 /* Projection weights in matrix-core fragment order, for pa_tokenize_kv (a layout of this library,
  * not of the pages: one A-operand fragment of the 16x16x32 bf16 matrix-core product is 64 lanes x
  * 16 contiguous bytes, so the tokenizer reads each with one coalesced 1 KB load).

@@ -25,7 +25,9 @@ PA_PAGED, PA_PADDED = 0, 1
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
            "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm",
            "pa_tokenize_kv", "pa_pack_projection", "pa_append_decode_attention",
-           "pa_append_decode_attention_padded", "pa_lse_merge")
+           "pa_append_decode_attention_padded", "pa_lse_merge", "pa_decode_attention_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20
+NOALLOC_MAX_ROW_HEADS = 16384
 
 
 class PaError(RuntimeError):
@@ -90,6 +92,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                       ctypes.c_float, _P, ctypes.c_size_t,
                                                       _SIZE_P, _P, _P, _P]
     lib.pa_lse_merge.argtypes = [_P, _P, _I32, ctypes.c_int64, _I32, _P, _P, _P]
+    lib.pa_decode_attention_noalloc.argtypes = [ctypes.POINTER(Pool), _P, ctypes.c_int64, _I32,
+                                                _I32, _P, _I32, _P, _I32, _I32, ctypes.c_float,
+                                                _P, _P, _P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -165,6 +170,19 @@ def pa_decode_attention(pool: Pool, q, q_row_stride: int, n_q: int, num_q_heads:
                                  _ptr(lse), _stream(stream))
     _check("pa_decode_attention", st)
     return need.value
+
+
+def pa_decode_attention_noalloc(pool: Pool, q, q_row_stride: int, n_q: int, num_q_heads: int,
+                                block_tables, bt_stride: int, kv_lens, batch: int,
+                                max_kv_len: int, scale: float, out=None, lse=None,
+                                stream=None) -> None:
+    """Enqueue the decode on the library's own per-device scratch (no workspace argument)."""
+    lib = load_library()
+    st = lib.pa_decode_attention_noalloc(ctypes.byref(pool), _ptr(q), q_row_stride, n_q,
+                                         num_q_heads, _ptr(block_tables), bt_stride,
+                                         _ptr(kv_lens), batch, max_kv_len, ctypes.c_float(scale),
+                                         _ptr(out), _ptr(lse), _stream(stream))
+    _check("pa_decode_attention_noalloc", st)
 
 
 def pa_decode_attention_block_sparse(pool: Pool, q, q_row_stride: int, n_q: int,

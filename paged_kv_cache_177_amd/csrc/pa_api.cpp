@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call, so the error paths work without a GPU.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "pa.h"
@@ -323,7 +324,8 @@ pa_status run_decode(pa::DecodeArgs& a, size_t need, void* workspace, size_t wor
   if (need > 0 && ((uintptr_t)workspace % 256) != 0) return PA_ERR_CAPACITY;
   if (a.batch == 0) return PA_OK;
   if (need > 0)
-    pa::carve_workspace(workspace, a.batch, a.n_q, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
+    pa::carve_workspace(workspace, a.batch, a.n_q, a.H_q, a.D, a.s_max,
+                        pa::merge_count_bytes(a.batch, a.H_q), &a.counter, &a.part_o,
                         &a.part_lse, &a.merge_counts);
   bool merged = false;
   hipError_t e = a.n_q == 1 ? pa::launch_decode_vector(a, stream, &merged)
@@ -348,6 +350,112 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
                                            &a, &need);
   if (s != PA_OK) return s;
   return run_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
+}
+
+// ---- the allocation-free decode -----------------------------------------------------------------
+// pa_decode_attention_noalloc runs the split paths on the library's own scratch instead of a
+// caller's workspace. `scratch` is a file-scope device array: the runtime gives every device the
+// library runs on its own copy, which lives until the process ends. In host code its name is only a
+// stand-in for the symbol, never a device address: the address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept in g_scratch[device]. Layout: the
+// persistent kernel's work counter (256 bytes), a fixed reservation for the finished-split counts
+// (the same offsets for every batch, so calls of any size follow one another with no clearing),
+// then the partials. The counters must be zero before a call, and every completed call leaves them
+// at zero; they are cleared by a fill kernel on a device's first call and after a failed launch.
+namespace {
+
+constexpr size_t kNoallocCountBytes = (size_t)PA_NOALLOC_MAX_ROW_HEADS * sizeof(int);
+static_assert(kNoallocCountBytes % 256 == 0, "count reservation keeps the partials aligned");
+static_assert(PA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+// zero n 16-byte words (the counter region of the scratch)
+__global__ void clear_words_kernel(uint4* p, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchSlot {
+  void* ptr = nullptr;  // device address of this device's `scratch`
+  bool dirty = true;    // the counters may be nonzero: clear them before the next launch
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+// This device's scratch, set up on first use; clears the counters (on `stream`, ahead of the
+// caller's launch) when they may be nonzero. Under stream capture the clear is recorded into the
+// graph and the slot stays marked, so the next eager call clears again.
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr, int* dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& slot = g_scratch[dev];
+  if (slot.ptr == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p % 256) != 0) return hipErrorInvalidSymbol;
+    slot.ptr = p;
+    slot.dirty = true;
+  }
+  if (slot.dirty) {
+    const int words = (int)((pa::kCounterBytes + kNoallocCountBytes) / 16);
+    hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint4*>(slot.ptr), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+      slot.dirty = false;
+  }
+  *ptr = slot.ptr;
+  *dev_out = dev;
+  return hipSuccess;
+}
+
+void noalloc_mark_dirty(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch[dev].dirty = true;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_attention_noalloc(const pa_pool* pool, const void* q,
+                                                 int64_t q_row_stride, int32_t n_q,
+                                                 int32_t num_q_heads, const int32_t* block_tables,
+                                                 int32_t bt_stride, const int32_t* kv_lens,
+                                                 int32_t batch, int32_t max_kv_len, float scale,
+                                                 float* out, float* lse, hipStream_t stream) {
+  pa::DecodeArgs a;
+  size_t need = 0;
+  const pa_status s = paged_decode_prepare(pool, q, q_row_stride, n_q, num_q_heads, block_tables,
+                                           bt_stride, kv_lens, batch, max_kv_len, scale, out, lse,
+                                           &a, &need);
+  if (s != PA_OK) return s;
+  size_t need_s = 0;
+  if (need > 0) {
+    if (pa::merge_count_bytes(a.batch, a.H_q) > kNoallocCountBytes) return PA_ERR_CAPACITY;
+    need_s = pa::decode_workspace_bytes(a.batch, a.n_q, a.H_q, a.D, a.s_max, kNoallocCountBytes);
+    if (need_s > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_CAPACITY;
+  }
+  if (a.batch == 0) return PA_OK;
+  int dev = -1;
+  if (need_s > 0) {
+    void* ws = nullptr;
+    if (noalloc_scratch(stream, &ws, &dev) != hipSuccess) return PA_ERR_HIP;
+    pa::carve_workspace(ws, a.batch, a.n_q, a.H_q, a.D, a.s_max, kNoallocCountBytes, &a.counter,
+                        &a.part_o, &a.part_lse, &a.merge_counts);
+  }
+  bool merged = false;
+  hipError_t e = a.n_q == 1 ? pa::launch_decode_vector(a, stream, &merged)
+                            : pa::launch_decode_mq(a, stream);
+  if (e == hipSuccess && a.s_max > 1 && !merged) e = pa::launch_lse_reduce(a, stream);
+  if (e != hipSuccess && dev >= 0) noalloc_mark_dirty(dev);
+  return map_hip(e);
 }
 
 extern "C" pa_status pa_tokenize_kv(const pa_pool* pool, const float* neuron_table,
@@ -540,7 +648,8 @@ pa_status run_append_decode(pa::DecodeArgs& a, size_t need, void* workspace,
   if (need > 0 && ((uintptr_t)workspace % 256) != 0) return PA_ERR_CAPACITY;
   if (a.batch == 0) return PA_OK;
   if (need > 0)
-    pa::carve_workspace(workspace, a.batch, 1, a.H_q, a.D, a.s_max, &a.counter, &a.part_o,
+    pa::carve_workspace(workspace, a.batch, 1, a.H_q, a.D, a.s_max,
+                        pa::merge_count_bytes(a.batch, a.H_q), &a.counter, &a.part_o,
                         &a.part_lse, &a.merge_counts);
   bool merged = false;
   hipError_t e = pa::launch_decode_vector(a, stream, &merged);

@@ -110,19 +110,26 @@ inline size_t merge_count_bytes(int batch, int H_q) {
   return ((size_t)batch * (size_t)H_q * sizeof(int) + 255) & ~(size_t)255;
 }
 
-inline size_t decode_workspace_bytes(int batch, int n_q, int H_q, int D, int s_max) {
+// c_bytes: the bytes reserved for the finished-split counts, merge_count_bytes(batch, H_q) for a
+// caller's workspace, or a fixed reservation that holds the counts of any batch up to a limit (the
+// library's own scratch, whose counts then keep their offsets from one call to the next).
+inline size_t decode_workspace_bytes(int batch, int n_q, int H_q, int D, int s_max,
+                                     size_t c_bytes) {
   if (s_max <= 1) return 0;
   size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
-  size_t bytes = kCounterBytes + merge_count_bytes(batch, H_q);
+  size_t bytes = kCounterBytes + c_bytes;
   bytes += (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
   bytes += (rows * sizeof(float) + 255) & ~(size_t)255;
   return bytes;
 }
+inline size_t decode_workspace_bytes(int batch, int n_q, int H_q, int D, int s_max) {
+  return decode_workspace_bytes(batch, n_q, H_q, D, s_max, merge_count_bytes(batch, H_q));
+}
 
 inline void carve_workspace(void* ws, int batch, int n_q, int H_q, int D, int s_max,
-                            int** counter, float** part_o, float** part_lse, int** merge_counts) {
+                            size_t c_bytes, int** counter, float** part_o, float** part_lse,
+                            int** merge_counts) {
   size_t rows = (size_t)batch * (size_t)n_q * (size_t)H_q * (size_t)s_max;
-  size_t c_bytes = merge_count_bytes(batch, H_q);
   size_t o_bytes = (rows * (size_t)D * sizeof(float) + 255) & ~(size_t)255;
   *counter = (int*)ws;
   *merge_counts = n_q == 1 ? (int*)((char*)ws + kCounterBytes) : nullptr;

@@ -456,3 +456,38 @@ def test_lse_merge_argument_errors():
         with pytest.raises(B.PaError) as e:
             B.pa_lse_merge(**{**ok, **kw})
         assert e.value.status == status, kw
+
+
+def test_noalloc_decode_limits_and_errors():
+    """The allocation-free decode validates like pa_decode_attention and refuses, before any HIP
+    call, what its per-device scratch cannot hold."""
+    p = _fake_pool()
+
+    def call(**kw):
+        a = dict(q=FAKE, q_row_stride=32 * 64, n_q=1, num_q_heads=32, block_tables=FAKE,
+                 bt_stride=513, kv_lens=FAKE, batch=128, max_kv_len=8193, out=FAKE)
+        a.update(kw)
+        B.pa_decode_attention_noalloc(p, a["q"], a["q_row_stride"], a["n_q"], a["num_q_heads"],
+                                      a["block_tables"], a["bt_stride"], a["kv_lens"], a["batch"],
+                                      a["max_kv_len"], 0.125, out=a["out"])
+
+    for kw, status in [(dict(q=None), B.PA_ERR_NULL), (dict(out=None), B.PA_ERR_NULL),
+                       (dict(num_q_heads=24), B.PA_ERR_UNSUPPORTED),
+                       (dict(max_kv_len=513 * 16 + 1), B.PA_ERR_SHAPE),
+                       # 513 rows x 32 heads of finished-split counts > the reservation
+                       (dict(batch=513), B.PA_ERR_CAPACITY)]:
+        with pytest.raises(B.PaError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    big = B.Pool()
+    big.desc = _desc(head_dim=128)
+    big.k, big.v = 0x10000, 0x20000
+    with pytest.raises(B.PaError) as e:  # 16 rows of 131072 tokens, 32 heads, D = 128: 69 MB
+        B.pa_decode_attention_noalloc(big, FAKE, 32 * 128, 1, 32, FAKE, 8192, FAKE, 16, 131072,
+                                      0.1, out=FAKE)
+    assert e.value.status == B.PA_ERR_CAPACITY
+    # the scratch's stated size and count limit, as the header defines them
+    text = open(HEADER).read()
+    assert re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(\(size_t\)16 << 20\)", text)
+    assert "#define PA_NOALLOC_MAX_ROW_HEADS 16384" in text
+    assert B.NOALLOC_SCRATCH_BYTES == 16 << 20 and B.NOALLOC_MAX_ROW_HEADS == 16384
