@@ -415,12 +415,14 @@ def cpu_baseline_tokenize(c, E: int, budget_s: float = 10.0, max_reps: int = 200
                        f"{len(os.sched_getaffinity(0))} cores, BLAS threads {cores}")}
 
 
-def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64):
-    """The paged B=16 step captured as a graph (append + decode + merge + on-device advance) and
-    replayed, and the same four calls issued one by one (the eager counterpart of the graph).
-    Block tables are filled for ``ahead`` positions past each row's start; positions are reset
-    (outside the timed steps) every ``reset_every`` warm-up steps. Returns ((wall, events) of the
-    replays, (wall, events) of the eager steps), in microseconds per step."""
+def graph_step_timing(args, plan, timed, tokens: int = 1, one_launch: bool = True):
+    """The paged B=16 step captured as a graph (per token: append + decode + merge + next positions
+    in one pa_lockstep_decode_step launch, or with ``one_launch=False`` the fused call followed by
+    the add-one kernel), ``tokens`` consecutive tokens per graph, replayed; and the same calls
+    issued one by one (the eager counterpart of the graph). Block tables are filled for every
+    position the warm-up and the timed replays reach between resets (positions are reset outside
+    the timed replays). Returns ((wall, events) of the replays, (wall, events) of the eager runs),
+    in microseconds per token."""
     import numpy as np
     import torch
 
@@ -428,12 +430,15 @@ def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64
     from paged_kv_cache_177_amd import binding as B
     from paged_kv_cache_177_amd.runner import PagedLockstepGraph, to_torch
 
-    assert args.steps <= reset_every <= ahead
+    reset_every = max(1, 256 // tokens)      # replays between position resets
+    ahead = max(args.steps, reset_every) * tokens + tokens
     n0 = plan.n_ctx0.astype(np.int32)
+    extra = 16 * ((ahead + 31) // 16)
     case = W.make_paged_case("b16-graph", plan.seed, n0, plan.num_q_heads, plan.num_kv_heads,
                              plan.head_dim, plan.dtype, rope_theta=plan.rope_theta,
                              rope_max_pos=int(n0.max()) + ahead + 2,
-                             pool_factor=1.5, bt_stride=(int(n0.max()) + ahead + 16) // 16)
+                             num_blocks=int(((n0 + extra) // 16 + 2).sum()) + 8,
+                             bt_stride=(int(n0.max()) + ahead + 16) // 16 + 1)
     # extend every row's table with free blocks for the positions ahead
     bt = case.block_tables.copy()
     used = set(int(x) for x in bt.ravel())
@@ -452,14 +457,13 @@ def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64
     start = torch.from_numpy(n0.copy()).to("cuda:0")
     g = PagedLockstepGraph(pool, torch.from_numpy(bt).to("cuda:0"), start.clone(),
                            case.num_q_heads, int(n0.max()) + ahead + 1, case.scale,
-                           device="cuda:0")
+                           device="cuda:0", tokens=tokens, one_launch=one_launch)
     g.k_new.copy_(to_torch(case.k_new, case.dtype))
     g.v_new.copy_(to_torch(case.v_new, case.dtype))
     g.q_in.copy_(to_torch(case.q, case.dtype))
 
     def reset():
-        g.positions.copy_(start)
-        g.kv_lens.copy_(start + 1)
+        g.set_positions(start)
 
     g.step()
     reset()
@@ -476,11 +480,12 @@ def graph_step_timing(args, plan, timed, ahead: int = 128, reset_every: int = 64
             count[0] += 1
         return run
 
-    # timed() warms up (with resets), then times args.steps steps from a fresh reset
+    # timed() warms up (with resets), then times args.steps replays from a fresh reset
     def timed_from_reset(fn):
         count[0] = 0
         reset()
-        return timed(fn, before_timed=lambda: (reset(), count.__setitem__(0, 0)))
+        wall, ev = timed(fn, before_timed=lambda: (reset(), count.__setitem__(0, 0)))
+        return wall / tokens, ev / tokens
 
     graph = timed_from_reset(every(g.replay))
     eager = timed_from_reset(every(g.step))
@@ -517,6 +522,159 @@ def append_timings(r, case, stream, calls: int = 50):
         torch.cuda.synchronize()
         out.append(a.elapsed_time(b) * 1e3 / calls)
     return out[0], out[1]
+
+
+def b16_protocol_timing(plan, reps: int = 3):
+    """The B=16 lockstep run as the plan specifies it: 32 consecutive steps over 16 ragged rows,
+    two rows leaving and two sequences joining (their histories written into recycled blocks) at
+    the join step, blocks allocated on demand from the shuffled pool's LIFO free list.
+
+    Host and GPU are measured apart. The host's bookkeeping for every step (freeing and
+    allocating blocks, packing the block table) runs first, timed step by step on the host clock.
+    The GPU then runs the 32 steps, each one pa_append_decode_attention call on the step's own
+    inputs and table (already in device memory): once with a pair of events around every step
+    (median, p10, p90; each pair adds the events' own cost), and once as two back-to-back runs,
+    steps before the join and steps from it, each between one pair of events, with the joiners'
+    history upload between them (timed on its own). ``reps`` runs from the initial state.
+    Returns a dict of microsecond figures."""
+    import math
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_177_amd import binding as B
+    from paged_kv_cache_177_amd.blocks import BlockAllocator, SequenceBlocks, block_table_array
+    from paged_kv_cache_177_amd.runner import to_torch
+
+    dev = "cuda:0"
+    H_q, H, D, scale = plan.num_q_heads, plan.num_kv_heads, plan.head_dim, plan.scale
+    sched = plan.schedule()
+    steps, J = len(sched), plan.join_step
+    stride = math.ceil(plan.rope_max_pos / 16)
+    desc = B.make_desc("paged", plan.dtype, H, D, num_blocks=plan.num_blocks,
+                       rope_max_pos=plan.rope_max_pos, rope_theta=plan.rope_theta)
+    pool = B.alloc_pool(desc, device=dev)
+    hist = {sid: tuple(to_torch(a, plan.dtype).to(dev) for a in plan.history(sid))
+            for sid in range(18)}
+
+    def stack(i):  # every step's inputs, resident before the run: [steps][16][heads][D]
+        return torch.stack([torch.stack([to_torch(plan.step_inputs(sid, s)[i], plan.dtype)
+                                         for _, sid, _ in rows])
+                            for s, rows in enumerate(sched)]).to(dev)
+
+    q_all, k_all, v_all = stack(0), stack(1), stack(2)
+    q_rot = torch.empty((16, H_q, D), dtype=q_all.dtype, device=dev)
+    out = torch.empty((16, H_q, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((16, H_q), dtype=torch.float32, device=dev)
+    pos_np = np.array([[pos for _, _, pos in rows] for rows in sched], np.int32)
+    pos_d = torch.from_numpy(pos_np).to(dev)
+    len_d = pos_d + 1
+    max_len = int(pos_np.max()) + 1
+    stream = torch.cuda.current_stream()
+
+    def write_history(sid, blocks):
+        k, v = hist[sid]
+        t = torch.arange(k.shape[0], device=dev)
+        blk = torch.tensor(blocks, dtype=torch.int64, device=dev)[t // 16]
+        pool.k[blk, :, t % 16, :] = k
+        pool.v[blk, :, t % 16, :] = v
+
+    def bookkeeping():
+        """The host side of one run: per step, the table and the host time it took; the blocks
+        of the initial and the joining sequences."""
+        perm = plan.perm
+        seqs, off = {}, 0
+        for sid in range(16):
+            n = math.ceil(plan.seq_ctx(sid) / 16)
+            seqs[sid] = SequenceBlocks(perm[off:off + n])
+            off += n
+        alloc = BlockAllocator(perm[off:-1])
+        alloc.adopt(perm[:off])
+        poison = int(perm[-1])
+        first = {sid: list(seqs[sid].blocks) for sid in range(16)}
+        tables, host, joined = [], [], {}
+        for s, rows in enumerate(sched):
+            t0 = time.perf_counter()
+            if s == J:
+                for slot in plan.leave_slots.tolist():
+                    alloc.free(seqs.pop(sched[s - 1][slot][1]).blocks)
+                for _, sid, _ in rows:
+                    if sid >= 16:
+                        sb = SequenceBlocks()
+                        sb.ensure_token(plan.seq_ctx(sid) - 1, alloc)
+                        seqs[sid] = sb
+                        joined[sid] = list(sb.blocks)
+            for _, sid, pos in rows:
+                seqs[sid].ensure_token(int(pos), alloc)
+            tables.append(block_table_array([seqs[sid] for _, sid, _ in rows], stride, poison))
+            host.append((time.perf_counter() - t0) * 1e6)
+        return np.stack(tables), host, first, joined
+
+    tables, _, _, _ = bookkeeping()
+    bt_d = torch.from_numpy(tables).to(dev)
+    need = B.pa_append_decode_attention(pool.pool, bt_d[0], stride, pos_d[0], None, k_all[0],
+                                        v_all[0], q_all[0], q_rot, H_q, len_d[0], 16, max_len,
+                                        scale, out=out, query_workspace=True)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step(s):
+        B.pa_append_decode_attention(pool.pool, bt_d[s], stride, pos_d[s], None, k_all[s],
+                                     v_all[s], q_all[s], q_rot, H_q, len_d[s], 16, max_len, scale,
+                                     workspace=ws, out=out, lse=lse)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    host_us, per_step_us, b2b_us, join_us = [], [], [], []
+    for rep in range(reps + 1):  # the first run warms up
+        tables_r, host, first, joined = bookkeeping()
+        assert np.array_equal(tables_r, tables)  # the same plan gives the same tables
+        for sid in range(16):
+            write_history(sid, first[sid])
+        torch.cuda.synchronize()
+        # per-step events, steps issued back to back
+        pairs = []
+        for s in range(steps):
+            if s == J:
+                for sid, blocks in joined.items():
+                    write_history(sid, blocks)
+            a = ev()
+            step(s)
+            pairs.append((a, ev()))
+        torch.cuda.synchronize()
+        # the same run as two back-to-back segments around the join
+        for sid in range(16):
+            write_history(sid, first[sid])
+        torch.cuda.synchronize()
+        a = ev()
+        for s in range(J):
+            step(s)
+        b = ev()
+        for sid, blocks in joined.items():
+            write_history(sid, blocks)
+        c = ev()
+        for s in range(J, steps):
+            step(s)
+        d = ev()
+        torch.cuda.synchronize()
+        if rep > 0:
+            host_us.extend(host)
+            per_step_us.extend(x.elapsed_time(y) * 1e3 for x, y in pairs)
+            b2b_us.append((a.elapsed_time(b) + c.elapsed_time(d)) * 1e3 / steps)
+            join_us.append(b.elapsed_time(c) * 1e3)
+    pct = lambda x, q: round(float(np.percentile(x, q)), 2)  # noqa: E731
+    return {"protocol_steps": steps, "protocol_runs": reps,
+            "protocol_gpu_us_per_step_back_to_back": round(statistics.median(b2b_us), 2),
+            "protocol_gpu_us_per_step_events_median": pct(per_step_us, 50),
+            "protocol_gpu_us_per_step_events_p10": pct(per_step_us, 10),
+            "protocol_gpu_us_per_step_events_p90": pct(per_step_us, 90),
+            "protocol_host_bookkeeping_us_per_step_median": pct(host_us, 50),
+            "protocol_host_bookkeeping_us_per_step_p90": pct(host_us, 90),
+            "protocol_host_bookkeeping_us_join_step": round(
+                statistics.median(host_us[J::steps]), 1),
+            "protocol_join_history_upload_gpu_us": round(statistics.median(join_us), 1)}
 
 
 def main_b16(args):
@@ -598,6 +756,17 @@ def main_b16(args):
     wall_paged_sep, ev_paged_sep = timed(paged.step)
     wall_padded_sep, ev_padded_sep = timed(padded_step)
     (wall_graph, ev_graph), (wall_g_eager, ev_g_eager) = graph_step_timing(args, plan, timed)
+    graph_k = {}
+    for k in (4, 16):
+        (wg, eg), (we, ee) = graph_step_timing(args, plan, timed, tokens=k)
+        graph_k[f"graph_{k}_tokens_us_per_token_events"] = round(eg, 2)
+        graph_k[f"graph_{k}_tokens_us_per_token_wall"] = round(wg, 2)
+        graph_k[f"graph_{k}_tokens_eager_us_per_token_events"] = round(ee, 2)
+    for k in (1, 16):  # the two-kernel token (fused call + add-one kernel), for comparison
+        (wg, eg), (we, ee) = graph_step_timing(args, plan, timed, tokens=k, one_launch=False)
+        graph_k[f"graph_{k}_tokens_two_kernels_us_per_token_events"] = round(eg, 2)
+        graph_k[f"graph_{k}_tokens_two_kernels_eager_us_per_token_events"] = round(ee, 2)
+    protocol = b16_protocol_timing(plan)
     out_line = {
         "metric": "B=16 lockstep decode step us (append + decode + merge), paged, bf16",
         "value": round(ev_paged, 2),
@@ -636,6 +805,8 @@ def main_b16(args):
                    "graph_us_per_step_wall": round(wall_graph, 2),
                    "graph_eager_us_per_step_events": round(ev_g_eager, 2),
                    "graph_eager_us_per_step_wall": round(wall_g_eager, 2),
+                   **graph_k,
+                   **protocol,
                    "source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:

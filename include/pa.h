@@ -341,6 +341,28 @@ pa_status pa_append_decode_attention(const pa_pool* pool, const int32_t* block_t
                                      size_t* workspace_needed /* host */, float* out, float* lse,
                                      hipStream_t stream);
 
+/* One lockstep decode step in one launch: pa_append_decode_attention with kv_len = position + 1
+ * taken on the device, and the positions of the next step written out ("NeuroGrid releases",
+ * v0.8.0 "CUDA Graphs": position and kv_len read from device buffers, kv_len = position + 1
+ * computed on the GPU, so a recorded step replays token after token with no host work).
+ *
+ * Row b's new key and value are stored at token index positions[b] (rotated there when the pool
+ * has RoPE tables), and the row attends over its first kv_len = positions[b] + 1 tokens (clamped
+ * into [0, max_kv_len]), exactly as pa_append_decode_attention does with dest = NULL and
+ * kv_lens[b] = positions[b] + 1, bit for bit. In the same launch positions_out[b] =
+ * positions[b] + 1 (int32, device, [batch], must not overlap positions): the next step reads
+ * positions_out, so two buffers alternate from step to step and the step needs no second kernel.
+ * Other arguments, the workspace and the errors as for pa_append_decode_attention; in addition
+ * PA_ERR_NULL (positions_out) and PA_ERR_SHAPE (positions_out overlapping positions). Positions
+ * must stay below 2^31 - 2. */
+pa_status pa_lockstep_decode_step(const pa_pool* pool, const int32_t* block_tables,
+                                  int32_t bt_stride, const int32_t* positions,
+                                  int32_t* positions_out, const void* k_new, const void* v_new,
+                                  const void* q, void* q_out, int32_t num_q_heads, int32_t batch,
+                                  int32_t max_kv_len, float scale, void* workspace,
+                                  size_t workspace_bytes, size_t* workspace_needed /* host */,
+                                  float* out, float* lse, hipStream_t stream);
+
 /* The lockstep form of pa_append_decode_attention over a PA_PADDED pool: pa_append_kv (new token
  * at column dest[b], NULL: positions[b]) followed by pa_decode_attention_padded, in one launch.
  * Arguments and results as for those two calls and pa_append_decode_attention; a destination

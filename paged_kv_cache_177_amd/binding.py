@@ -25,7 +25,8 @@ PA_PAGED, PA_PADDED = 0, 1
 EXPORTS = ("pa_alloc_pool", "pa_append_kv", "pa_decode_attention", "pa_decode_attention_padded",
            "pa_decode_attention_block_sparse", "pa_advance_lockstep", "pa_append_kv_qk_norm",
            "pa_tokenize_kv", "pa_pack_projection", "pa_append_decode_attention",
-           "pa_append_decode_attention_padded", "pa_lse_merge", "pa_decode_attention_noalloc")
+           "pa_append_decode_attention_padded", "pa_lse_merge", "pa_decode_attention_noalloc",
+           "pa_lockstep_decode_step")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 NOALLOC_MAX_ROW_HEADS = 16384
 
@@ -92,6 +93,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                       ctypes.c_float, _P, ctypes.c_size_t,
                                                       _SIZE_P, _P, _P, _P]
     lib.pa_lse_merge.argtypes = [_P, _P, _I32, ctypes.c_int64, _I32, _P, _P, _P]
+    lib.pa_lockstep_decode_step.argtypes = [ctypes.POINTER(Pool), _P, _I32, _P, _P, _P, _P, _P,
+                                            _P, _I32, _I32, _I32, ctypes.c_float, _P,
+                                            ctypes.c_size_t, _SIZE_P, _P, _P, _P]
     lib.pa_decode_attention_noalloc.argtypes = [ctypes.POINTER(Pool), _P, ctypes.c_int64, _I32,
                                                 _I32, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                                 _P, _P, _P]
@@ -281,6 +285,25 @@ def pa_append_decode_attention(pool: Pool, block_tables, bt_stride: int, positio
                                         ws_bytes, ctypes.byref(need) if query_workspace else None,
                                         _ptr(out), _ptr(lse), _stream(stream))
     _check("pa_append_decode_attention", st)
+    return need.value
+
+
+def pa_lockstep_decode_step(pool: Pool, block_tables, bt_stride: int, positions, positions_out,
+                            k_new, v_new, q, q_out, num_q_heads: int, batch: int,
+                            max_kv_len: int, scale: float, workspace=None, out=None, lse=None,
+                            stream=None, query_workspace: bool = False) -> int:
+    """Append + decode (kv_len = position + 1) + positions_out = positions + 1, in one launch;
+    with ``query_workspace`` only return the workspace bytes."""
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_lockstep_decode_step(ctypes.byref(pool), _ptr(block_tables), bt_stride,
+                                     _ptr(positions), _ptr(positions_out), _ptr(k_new),
+                                     _ptr(v_new), _ptr(q), _ptr(q_out), num_q_heads, batch,
+                                     max_kv_len, ctypes.c_float(scale), _ptr(workspace), ws_bytes,
+                                     ctypes.byref(need) if query_workspace else None, _ptr(out),
+                                     _ptr(lse), _stream(stream))
+    _check("pa_lockstep_decode_step", st)
     return need.value
 
 

@@ -678,6 +678,34 @@ extern "C" pa_status pa_append_decode_attention(
   return run_append_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
 }
 
+extern "C" pa_status pa_lockstep_decode_step(
+    const pa_pool* pool, const int32_t* block_tables, int32_t bt_stride, const int32_t* positions,
+    int32_t* positions_out, const void* k_new, const void* v_new, const void* q, void* q_out,
+    int32_t num_q_heads, int32_t batch, int32_t max_kv_len, float scale, void* workspace,
+    size_t workspace_bytes, size_t* workspace_needed, float* out, float* lse,
+    hipStream_t stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  if (positions == nullptr || positions_out == nullptr) return PA_ERR_NULL;
+  // the step reads positions while one workgroup per row writes positions_out
+  const uintptr_t pb = (uintptr_t)positions, po = (uintptr_t)positions_out;
+  const uintptr_t pn = (uintptr_t)(batch > 0 ? batch : 0) * sizeof(int32_t);
+  if (pn > 0 && pb < po + pn && po < pb + pn) return PA_ERR_SHAPE;
+  pa::DecodeArgs a;
+  size_t need = 0;
+  // kv_lens are taken from the positions: the pointer stands in for the decode's own null check
+  s = paged_decode_prepare(pool, q, (int64_t)num_q_heads * pool->desc.head_dim, 1, num_q_heads,
+                           block_tables, bt_stride, positions, batch, max_kv_len, scale, out, lse,
+                           &a, &need);
+  if (s != PA_OK) return s;
+  s = fused_prepare(pool, positions, nullptr, k_new, v_new, q, q_out, &a);
+  if (s != PA_OK) return s;
+  a.kv_lens = nullptr;
+  a.kv_from_positions = 1;
+  a.positions_out = positions_out;
+  return run_append_decode(a, need, workspace, workspace_bytes, workspace_needed, stream);
+}
+
 extern "C" pa_status pa_append_decode_attention_padded(
     const pa_pool* padded_pool, const int32_t* positions, const int32_t* dest, const void* k_new,
     const void* v_new, const void* q, void* q_out, int32_t num_q_heads,

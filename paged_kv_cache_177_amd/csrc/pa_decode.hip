@@ -233,15 +233,25 @@ __device__ __forceinline__ Chunk make_chunk(int row, int g, int split, int n, in
   ch.row = row;
   ch.g = g;
   ch.split = split;
+  ch.ns = num_splits(n, chunk);
   ch.tok0 = split * chunk;
   const int rest = n - ch.tok0;
   ch.ntok = rest < chunk ? (rest > 0 ? rest : 0) : chunk;
   ch.nblk = (ch.ntok + kBlock - 1) / kBlock;
   ch.tail_blk = (ch.ntok % kBlock) != 0 ? ch.nblk - 1 : -1;
-  ch.ns = num_splits(n, chunk);
   ch.gap_s = gap_s;
   ch.gap_shift = gap_shift;
   return ch;
+}
+
+
+
+// Ordering groups of a row's chunks for the compact and persistent launches: the full chunks
+// (splits 0 .. n / chunk - 1) go first, the row's short last chunk (split n / chunk, when there is
+// one, or split 0 of an empty row) after every row's full ones.
+__device__ __forceinline__ void chunk_groups(int n, int chunk, int* full, int* part) {
+  *full = n / chunk;
+  *part = (n % chunk != 0 || n == 0) ? 1 : 0;
 }
 
 template <int G, int D, int WAVES>
@@ -627,8 +637,19 @@ __device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_
   } else {
     *gap_s = 0;
     *gap_shift = 0;
+    if (a.kv_from_positions) {  // kv_len = position + 1
+      const int p = a.positions[row];
+      return p < 0 ? 0 : (p >= a.max_kv_len ? a.max_kv_len : p + 1);
+    }
     return clampi(a.kv_lens[row], 0, a.max_kv_len);
   }
+}
+
+// Lockstep step: the row's position for the next step, written once per row (by the workgroup of
+// KV head 0, split 0, which every row has) to a buffer no workgroup of this launch reads.
+__device__ __forceinline__ void advance_position(const DecodeArgs& a, const Chunk& ch) {
+  if (a.positions_out != nullptr && ch.g == 0 && ch.split == 0 && threadIdx.x == 0)
+    a.positions_out[ch.row] = a.positions[ch.row] + 1;
 }
 
 // ---- merge of a row's splits inside the split grid ----------------------------------------------
@@ -720,8 +741,21 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, const Chunk& 
 // COMPACT (batches of at most 64 rows): a 1-D grid whose workgroups map to the chunks through
 // the rows' lengths, every row's full chunks first and each row's partial last chunk after them,
 // so the workgroups past the last chunk (which exit at once) all come at the end of the launch.
+// Workgroups per CU the bf16 grid kernels are compiled for: 3 caps them at 168 VGPRs, 3 waves per
+// SIMD. The D = 128 instances would otherwise take 169 and run 2 waves per SIMD; held to 168 the
+// long-context decode (compact grid) is 0.4 us faster, with no spills. 0 leaves the register
+// budget to the compiler.
+#ifndef PA_DECODE_MIN_WG_PER_CU
+#define PA_DECODE_MIN_WG_PER_CU 3
+#endif
+template <typename T>
+constexpr int grid_min_wg() {
+  return sizeof(T) == 2 && PA_DECODE_MIN_WG_PER_CU > 0 ? PA_DECODE_MIN_WG_PER_CU : 1;
+}
+
 template <typename T, int D, int G, bool PADDED, bool COMPACT>
-__global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, grid_min_wg<T>()) void decode_vector_kernel(
+    const DecodeArgs a) {
   using W = Worker<T, D, G, PADDED>;
   __shared__ typename W::Smem sm;
   W w(a);
@@ -733,8 +767,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
     int gs_l = 0, gsh_l = 0;
     const bool has = w.lane < a.batch;
     const int nb = has ? row_valid<PADDED>(a, w.lane, &gs_l, &gsh_l) : 0;
-    const int f = has ? nb / chunk : 0;
-    const int pc = has && (nb % chunk != 0 || nb == 0) ? 1 : 0;
+    int f = 0, pc = 0;
+    if (has) chunk_groups(nb, chunk, &f, &pc);
     int fi = f, pi = pc;  // inclusive prefix sums over the rows
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -781,6 +815,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(const Decode
   if constexpr (!COMPACT) n = row_valid<PADDED>(a, row, &gap_s, &gap_shift);
   const Chunk ch = make_chunk(row, g, split, n, gap_s, gap_shift, chunk);
   if (split >= ch.ns) return;
+  advance_position(a, ch);
   bool first = false;
   const bool stores = fused && w.fused_target(ch, n, t_new, &first);
   if (stores && first) {
@@ -844,11 +879,7 @@ __device__ void scan_rows(RowSmem<PADDED>& rs, int B, int chunk) {
   for (int i = 0; i < kPer; ++i) {
     const int b = t * kPer + i;
     int f = 0, p = 0;
-    if (b < B) {
-      const int n = rs.n[b];
-      f = n / chunk;
-      p = (n % chunk != 0 || n == 0) ? 1 : 0;
-    }
+    if (b < B) chunk_groups(rs.n[b], chunk, &f, &p);
     fl[i] = fs;
     pl[i] = ps;
     fs += f;
@@ -1042,6 +1073,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
       stores = w.fused_target(cur, uni(rs.n[cur.row]), t_new, &first);
       if (stores && first) store_now(cur, t_new, pos);
     }
+    advance_position(a, cur);
     w.reset();
     const int my = w.my_blocks(cur);
     if (!pre && my > 0) w.load_block(f0, cur, ids, w.blk_of(0));

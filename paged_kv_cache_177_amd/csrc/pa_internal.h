@@ -95,6 +95,11 @@ struct DecodeArgs {
   const float* cos;  // [rope_max_pos][D/2], or NULL
   const float* sin;
   int rope_max_pos;
+  // lockstep step (paged): kv_len of row b is positions[b] + 1 (clamped to max_kv_len) instead of
+  // kv_lens[b], and the workgroup of (row b, KV head 0, split 0) writes positions_out[b] =
+  // positions[b] + 1
+  int kv_from_positions;
+  int32_t* positions_out;
 };
 
 // Workspace of a decode call (0 bytes when no row can split):

@@ -218,57 +218,92 @@ class PaddedLockstep:
 
 
 class PagedLockstepGraph:
-    """One paged lockstep decode step -- append at the rows' positions and decode over kv_lens in
-    one pa_append_decode_attention call (+ the log-sum-exp merge), then pa_advance_lockstep
-    (position += 1, kv_len = position + 1) --
-    recorded once as a HIP graph and replayed per token ("NeuroGrid releases", v0.8.0: the decode
-    step replayed as a graph, lengths and positions in device buffers).
+    """Paged lockstep decode steps recorded as a HIP graph and replayed ("NeuroGrid releases",
+    v0.8.0: the decode step replayed as a graph, lengths and positions in device buffers,
+    kv_len = position + 1 on the GPU).
 
-    The caller writes each token's keys, values and queries into ``k_new``, ``v_new`` and ``q_in``
-    (in place) and keeps ``block_tables`` filled for the positions ahead; ``max_kv_len`` is the
-    host bound for every replay (it sizes the launch and the workspace). Run ``step()`` once
-    before ``capture()`` so that every kernel has been loaded."""
+    A token is one pa_lockstep_decode_step call: the append at the rows' positions, the decode over
+    position + 1 tokens (merging its own splits) and the next positions, in one launch. The
+    positions alternate between two device buffers (token i reads ``pos[i % 2]`` and writes the
+    other); with an odd count of tokens per graph a copy brings them back to ``pos[0]`` at the end.
+    With ``one_launch=False`` a token is pa_append_decode_attention followed by the add-one kernel
+    (pa_advance_lockstep) on one buffer, the two-kernel form.
+
+    One graph holds ``tokens`` consecutive tokens: token i reads its keys, values and queries from
+    ``k_new[i]``, ``v_new[i]`` and ``q_in[i]`` and writes ``out[i]``/``lse[i]`` (its rotated queries
+    to ``q_out[i]``), so a replay advances every row by ``tokens`` tokens with one launch from the
+    host. The caller writes the inputs in place before a replay and keeps ``block_tables`` filled
+    for the positions ahead; ``max_kv_len`` is the host bound for every step (it sizes the launch
+    and the workspace). Run ``step()`` once before ``capture()`` so that every kernel has been
+    loaded."""
 
     def __init__(self, pool, block_tables, positions, num_q_heads: int, max_kv_len: int,
-                 scale: float, device: str = "cuda"):
+                 scale: float, device: str = "cuda", tokens: int = 1, one_launch: bool = True):
         d = pool.pool.desc
         self.pool = pool
         self.H_q, self.H_kv, self.D = num_q_heads, d.num_kv_heads, d.head_dim
         self.dtype = "bf16" if d.dtype == B.PA_BF16 else "f32"
         tdt = torch.bfloat16 if d.dtype == B.PA_BF16 else torch.float32
+        self.tokens = int(tokens)
+        self.one_launch = bool(one_launch)
         self.batch = int(positions.shape[0])
         self.block_tables = block_tables
         self.bt_stride = int(block_tables.shape[1])
-        self.positions = positions
-        self.kv_lens = (positions + 1).to(torch.int32)
+        # pos[0] holds the positions between replays; pos[1] is the other buffer of the pair
+        self.pos = torch.stack([positions.to(torch.int32), positions.to(torch.int32)]).to(device)
+        self.kv_lens = (positions + 1).to(torch.int32).to(device)  # two-kernel form only
         self.max_kv_len = int(max_kv_len)
         self.scale = float(scale)
-        self.k_new = torch.zeros((self.batch, self.H_kv, self.D), dtype=tdt, device=device)
+        T, Bt = self.tokens, self.batch
+        self.k_new = torch.zeros((T, Bt, self.H_kv, self.D), dtype=tdt, device=device)
         self.v_new = torch.zeros_like(self.k_new)
-        self.q_in = torch.zeros((self.batch, self.H_q, self.D), dtype=tdt, device=device)
+        self.q_in = torch.zeros((T, Bt, self.H_q, self.D), dtype=tdt, device=device)
         self.q_out = torch.zeros_like(self.q_in)
-        self.out = torch.zeros((self.batch, self.H_q, self.D), dtype=torch.float32, device=device)
-        self.lse = torch.zeros((self.batch, self.H_q), dtype=torch.float32, device=device)
-        need = B.pa_decode_attention(pool.pool, self.q_out, self.H_q * self.D, 1, self.H_q,
+        self.out = torch.zeros((T, Bt, self.H_q, self.D), dtype=torch.float32, device=device)
+        self.lse = torch.zeros((T, Bt, self.H_q), dtype=torch.float32, device=device)
+        need = B.pa_decode_attention(pool.pool, self.q_out[0], self.H_q * self.D, 1, self.H_q,
                                      block_tables, self.bt_stride, self.kv_lens, self.batch,
-                                     self.max_kv_len, self.scale, out=self.out,
+                                     self.max_kv_len, self.scale, out=self.out[0],
                                      query_workspace=True)
         # zero-filled before first use (the work counter); every step leaves it at zero again
         self.workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
         self._need = need
         self.graph = None
 
-    def step(self):
-        # append + decode in one call (the append folded into the decode launch), the merge, then
-        # the add-one kernel
+    @property
+    def positions(self) -> torch.Tensor:
+        """The rows' positions between replays (the next token's)."""
+        return self.pos[0]
+
+    def set_positions(self, positions: torch.Tensor):
+        self.pos[0].copy_(positions)
+        self.kv_lens.copy_(positions + 1)
+
+    def token(self, i: int):
+        """Token i of a replay."""
         rope = self.pool.pool.desc.rope_max_pos > 0
-        B.pa_append_decode_attention(self.pool.pool, self.block_tables, self.bt_stride,
-                                     self.positions, None, self.k_new, self.v_new, self.q_in,
-                                     self.q_out if rope else None, self.H_q, self.kv_lens,
-                                     self.batch, self.max_kv_len, self.scale,
-                                     workspace=self.workspace if self._need else None,
-                                     out=self.out, lse=self.lse)
-        B.pa_advance_lockstep(self.positions, self.kv_lens, None, self.batch)
+        ws = self.workspace if self._need else None
+        q_out = self.q_out[i] if rope else None
+        if self.one_launch:
+            B.pa_lockstep_decode_step(self.pool.pool, self.block_tables, self.bt_stride,
+                                      self.pos[i % 2], self.pos[(i + 1) % 2], self.k_new[i],
+                                      self.v_new[i], self.q_in[i], q_out, self.H_q, self.batch,
+                                      self.max_kv_len, self.scale, workspace=ws, out=self.out[i],
+                                      lse=self.lse[i])
+        else:
+            B.pa_append_decode_attention(self.pool.pool, self.block_tables, self.bt_stride,
+                                         self.pos[0], None, self.k_new[i], self.v_new[i],
+                                         self.q_in[i], q_out, self.H_q, self.kv_lens,
+                                         self.batch, self.max_kv_len, self.scale, workspace=ws,
+                                         out=self.out[i], lse=self.lse[i])
+            B.pa_advance_lockstep(self.pos[0], self.kv_lens, None, self.batch)
+
+    def step(self):
+        """The graph's work issued eagerly: every token in turn."""
+        for i in range(self.tokens):
+            self.token(i)
+        if self.one_launch and self.tokens % 2 == 1:
+            self.pos[0].copy_(self.pos[1])
 
     def capture(self):
         g = torch.cuda.CUDAGraph()

@@ -491,3 +491,34 @@ def test_noalloc_decode_limits_and_errors():
     assert re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(\(size_t\)16 << 20\)", text)
     assert "#define PA_NOALLOC_MAX_ROW_HEADS 16384" in text
     assert B.NOALLOC_SCRATCH_BYTES == 16 << 20 and B.NOALLOC_MAX_ROW_HEADS == 16384
+
+
+def test_lockstep_step_checks_and_workspace():
+    """pa_lockstep_decode_step: the fused call's workspace, and its own checks before any
+    launch: positions_out required and not overlapping positions."""
+    p = _fake_pool(rope_max_pos=3000, rope_theta=1e6)
+
+    def call(**kw):
+        a = dict(positions=FAKE + 0x300000, positions_out=FAKE + 0x310000, q_out=FAKE + 0x100000,
+                 batch=128, max_kv_len=2100)
+        a.update(kw)
+        return B.pa_lockstep_decode_step(p, FAKE + 0x200000, 200, a["positions"],
+                                         a["positions_out"], FAKE + 0x400000, FAKE + 0x500000,
+                                         FAKE, a["q_out"], 32, a["batch"], a["max_kv_len"], 0.125,
+                                         out=FAKE + 0x600000, query_workspace=True)
+
+    ref = B.pa_decode_attention(p, FAKE, 32 * 64, 1, 32, FAKE, 200, FAKE, 128, 2100, 0.125,
+                                out=FAKE, query_workspace=True)
+    assert call() == ref > 0
+    for kw, status in [(dict(positions_out=None), B.PA_ERR_NULL),
+                       (dict(positions=None), B.PA_ERR_NULL),
+                       (dict(q_out=None), B.PA_ERR_NULL),             # RoPE pool: rotated q out
+                       (dict(positions_out=FAKE + 0x300000), B.PA_ERR_SHAPE),
+                       (dict(positions_out=FAKE + 0x300000 + 4 * 127), B.PA_ERR_SHAPE),
+                       (dict(positions_out=FAKE + 0x300000 - 4 * 127), B.PA_ERR_SHAPE),
+                       (dict(max_kv_len=200 * 16 + 1), B.PA_ERR_SHAPE)]:
+        with pytest.raises(B.PaError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    # adjacent buffers do not overlap
+    assert call(positions_out=FAKE + 0x300000 + 4 * 128) == ref

@@ -209,15 +209,19 @@ def test_b16_lockstep_protocol():
             f"free_blocks={P.alloc.num_free}")
 
 
-def test_b16_graph_replay_matches_eager():
-    """The paged B=16 step captured as a graph (append + decode + merge + on-device advance) and
-    replayed 24 times: each replay gives the eager step's bits, the pools end identical, and the
-    last step matches the oracle. Between replays the inputs are written in place and other eager
-    work runs, as in a serving loop."""
+@pytest.mark.parametrize("tokens,one_launch", [(1, True), (4, True), (16, True), (1, False),
+                                               (16, False)])
+def test_b16_graph_replay_matches_eager(tokens, one_launch):
+    """The paged B=16 step captured as a graph, ``tokens`` tokens per graph, replayed over 32
+    tokens. A token is one pa_lockstep_decode_step launch (append, decode over position + 1
+    tokens, next positions into the other buffer), or with one_launch False the fused call and the
+    add-one kernel. Every token gives the bits of the eager two-kernel step, the pools end
+    identical, and the last token matches the oracle. Between replays the inputs are written in
+    place and other eager work runs, as in a serving loop."""
     from paged_kv_cache_177_amd.runner import PagedLockstepGraph
 
     plan = W.b16_plan()
-    steps = 24
+    steps = 32
     H_q, H, D, scale = plan.num_q_heads, plan.num_kv_heads, plan.head_dim, plan.scale
     P = PagedSide(plan)
     n0 = plan.n_ctx0.astype(np.int32)
@@ -227,23 +231,24 @@ def test_b16_graph_replay_matches_eager():
     max_len = int(n0.max()) + steps
     ins = [[plan.step_inputs(sid, s) for sid in range(16)] for s in range(steps)]
 
-    def make(pool):
+    def make(pool, k, one):
         return PagedLockstepGraph(pool, torch.from_numpy(bt).cuda(),
-                                  torch.from_numpy(n0.copy()).cuda(), H_q, max_len, scale)
+                                  torch.from_numpy(n0.copy()).cuda(), H_q, max_len, scale,
+                                  tokens=k, one_launch=one)
 
-    def load_inputs(r, s):
-        r.q_in.copy_(to_torch(_stack([x[0] for x in ins[s]]), "bf16"))
-        r.k_new.copy_(to_torch(_stack([x[1] for x in ins[s]]), "bf16"))
-        r.v_new.copy_(to_torch(_stack([x[2] for x in ins[s]]), "bf16"))
+    def load_inputs(r, s, i):
+        r.q_in[i].copy_(to_torch(_stack([x[0] for x in ins[s]]), "bf16"))
+        r.k_new[i].copy_(to_torch(_stack([x[1] for x in ins[s]]), "bf16"))
+        r.v_new[i].copy_(to_torch(_stack([x[2] for x in ins[s]]), "bf16"))
 
-    # eager reference on the side's own pool
-    eager = make(P.dev)
+    # eager reference on the side's own pool, one token at a time
+    eager = make(P.dev, 1, False)
     ref = []
     for s in range(steps):
-        load_inputs(eager, s)
+        load_inputs(eager, s, 0)
         eager.step()
         torch.cuda.synchronize()
-        ref.append((eager.out.clone(), eager.lse.clone()))
+        ref.append((eager.out[0].clone(), eager.lse[0].clone()))
 
     # graph run on a fresh copy of the initial pool
     desc = B.make_desc("paged", "bf16", H, D, num_blocks=plan.num_blocks,
@@ -251,24 +256,27 @@ def test_b16_graph_replay_matches_eager():
     pool2 = B.alloc_pool(desc)
     pool2.k.copy_(to_torch(P.k, "bf16"))
     pool2.v.copy_(to_torch(P.v, "bf16"))
-    g = make(pool2)
+    g = make(pool2, tokens, one_launch)
     g.capture()
     scratch = torch.zeros(1 << 20, device="cuda")
-    for s in range(steps):
-        load_inputs(g, s)
+    for r0 in range(0, steps, tokens):
+        for i in range(tokens):
+            load_inputs(g, r0 + i, i)
         g.replay()
         scratch.add_(1.0)  # unrelated eager work between replays
         torch.cuda.synchronize()
-        assert torch.equal(g.out, ref[s][0]), f"replay {s} out"
-        assert torch.equal(g.lse, ref[s][1]), f"replay {s} lse"
-    log(f"[graph] {steps} replays match the eager steps bit for bit")
+        for i in range(tokens):
+            assert torch.equal(g.out[i], ref[r0 + i][0]), f"token {r0 + i} out"
+            assert torch.equal(g.lse[i], ref[r0 + i][1]), f"token {r0 + i} lse"
+    log(f"[graph] {steps // tokens} replays of {tokens} tokens match the eager steps bit for bit")
     # bit patterns (the pools hold NaN poison, which never compares equal as a value)
     assert torch.equal(pool2.k.view(torch.int16), P.dev.k.view(torch.int16))
     assert torch.equal(pool2.v.view(torch.int16), P.dev.v.view(torch.int16))
     np.testing.assert_array_equal(g.positions.cpu().numpy(), n0 + steps)
-    np.testing.assert_array_equal(g.kv_lens.cpu().numpy(), n0 + steps + 1)
+    if not one_launch:
+        np.testing.assert_array_equal(g.kv_lens.cpu().numpy(), n0 + steps + 1)
 
-    # the oracle, replaying the same appends on its own pool, at the last step
+    # the oracle, replaying the same appends on its own pool, at the last token
     cos, sin = O.rope_tables(plan.rope_theta, plan.head_dim, plan.rope_max_pos)
     k_h, v_h = P.k, P.v
     for s in range(steps):
@@ -278,8 +286,10 @@ def test_b16_graph_replay_matches_eager():
                                    _stack([x[1] for x in ins[s]]), _stack([x[2] for x in ins[s]]),
                                    cos, sin, q_in=q)
     o_ref, l_ref = O.decode_paged(k_h, v_h, "bf16", bt, n0 + steps, q2, scale)
-    assert_attention_close(g.out.cpu().numpy(), o_ref[:, 0], "bf16", "graph last step")
-    assert_attention_close(g.lse.cpu().numpy(), l_ref[:, 0], "bf16", "graph last step lse")
+    assert_attention_close(g.out[tokens - 1].cpu().numpy(), o_ref[:, 0], "bf16",
+                           f"graph x{tokens} last token")
+    assert_attention_close(g.lse[tokens - 1].cpu().numpy(), l_ref[:, 0], "bf16",
+                           f"graph x{tokens} last token lse")
     np.testing.assert_array_equal(to_numpy(pool2.k, "bf16"), k_h)
     np.testing.assert_array_equal(to_numpy(pool2.v, "bf16"), v_h)
 
