@@ -67,11 +67,16 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned short* p) {
           (__attribute__((address_space(3))) const unsigned short*)p));
 }
 
+// a query row's D outputs are contiguous in the merge area, padded so that rows start 16 bytes apart
+// on different banks
+template <int D>
+constexpr int kORow = D + 4;
+
 template <int D, int QT>
 struct MqSmem {
   unsigned short v[kWaves][kBlock * D];  // each wave's staged V block
   int kept[kWaves][64];                  // block-sparse: each wave's kept blocks of its window
-  float o[kWaves][QT][D][kTileRows];
+  float o[kWaves][QT][kTileRows][kORow<D>];
   float m[kWaves][QT][kTileRows];
   float l[kWaves][QT][kTileRows];
 };
@@ -82,6 +87,16 @@ struct MqSmem {
 template <int D, bool SPARSE>
 constexpr int mq_qt() { return (D == 32 && !SPARSE) ? 2 : 1; }
 
+// K/V block fragments per wave (RING - 1 blocks in flight while one is computed): the dense D = 32
+// kernel (the latent cross-attention shape, whose 4 waves per SIMD allow up to 128 registers)
+// takes PA_MQ_RING_D32; the block-sparse one is held to 72 registers and the wider ones would lose
+// occupancy, so they keep three
+#ifndef PA_MQ_RING_D32
+#define PA_MQ_RING_D32 3
+#endif
+template <int D, bool SPARSE>
+constexpr int mq_ring() { return (D == 32 && !SPARSE) ? PA_MQ_RING_D32 : 3; }
+
 template <int D, bool SPARSE>
 // D = 32 (the latent cross-attention shape) keeps several waves per SIMD: 7 with one sub-tile (72
 // registers), 4 with two (128); nearly a whole launch of that workload is then resident at once.
@@ -90,6 +105,7 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   constexpr int KC = D / 32;  // k-steps of the score product
   constexpr int NH = D / 16;  // dim tiles of the output product
   constexpr int QT = mq_qt<D, SPARSE>();
+  constexpr int RING = mq_ring<D, SPARSE>();
   constexpr int TR = kTileRows * QT;  // query rows of a workgroup
   __shared__ MqSmem<D, QT> sm;
   int tile, g, row;
@@ -117,6 +133,19 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   const int col = lane & 15;  // query row inside a sub-tile (S^T / O^T column)
   const int grp = lane >> 4;  // key group: keys 4*grp .. 4*grp+3 of a block
   const int G = a.H_q / a.H_kv;
+  // query row r -> (query r / G, head r % G of the group): shifts when G is a power of two (a
+  // uniform branch), else the divisions
+  const bool g_pow2 = (G & (G - 1)) == 0;
+  const int g_shift = __builtin_ctz((unsigned)G);
+  auto split_row = [&](int r, int& qi, int& hg) {
+    if (g_pow2) {
+      qi = r >> g_shift;
+      hg = r & (G - 1);
+    } else {
+      qi = r / G;
+      hg = r - qi * G;
+    }
+  };
   const int R = a.n_q * G;  // query rows of this KV head
 
   // Q^T fragments (B operand) of sub-tile u: query row tile * TR + 16 u + col, dims 32c + 8 grp
@@ -126,8 +155,9 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   for (int u = 0; u < QT; ++u) {
     const int r = tile * TR + kTileRows * u + col;
     const bool row_ok = r < R;
-    const int qi = row_ok ? r / G : 0;
-    const int qh = g * G + (row_ok ? r % G : 0);
+    int qi = 0, hg = 0;
+    if (row_ok) split_row(r, qi, hg);
+    const int qh = g * G + hg;
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (size_t)row * a.q_row_stride +
                        ((size_t)qi * a.H_q + qh) * D + 8 * grp;
 #pragma unroll
@@ -141,6 +171,7 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v);
   const float qk_scale = a.scale * kLog2e;
+  const float inv_qk = 1.0f / qk_scale;  // the raise threshold needs no exact division
 
   // Per sub-tile: running max m (log2 units), its raise threshold in raw score units thr = (m +
   // kRescale) / qk_scale (recomputed only when m moves), the output accumulators, and the row sums
@@ -167,15 +198,22 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     u32x4_t k[KC];
     u32x4_t v[D / 32];
   };
-  // issue the loads of one block (physical id pb, already clamped into the pool)
+  // issue the loads of one block (physical id pb, already clamped into the pool): a wave-uniform
+  // block base plus 32-bit lane byte offsets, the scalar-base form of the global load (no 64-bit
+  // address arithmetic per lane and block)
+  unsigned k_off = (unsigned)((col * D + 8 * grp) * 2);
+  unsigned v_off = (unsigned)(lane * 16);
+  asm volatile("" : "+v"(k_off), "+v"(v_off));
   auto load = [&](Frag& f, int pb) {
     const size_t base = ((size_t)pb * a.H_kv + g) * (size_t)(kBlock * D);
-    const __bf16* kb = kbase + base + (size_t)col * D + 8 * grp;
+    const char* kb = reinterpret_cast<const char*>(kbase + base);
+    const char* vb = reinterpret_cast<const char*>(vbase + base);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) f.k[c] = *reinterpret_cast<const u32x4_t*>(kb + 32 * c);
-    const __bf16* vb = vbase + base + (size_t)lane * 8;
+    for (int c = 0; c < KC; ++c)
+      f.k[c] = *reinterpret_cast<const u32x4_t*>(kb + k_off + 64 * c);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) f.v[c] = *reinterpret_cast<const u32x4_t*>(vb + 512 * c);
+    for (int c = 0; c < D / 32; ++c)
+      f.v[c] = *reinterpret_cast<const u32x4_t*>(vb + v_off + 1024 * c);
   };
   // One block: scores, online-softmax update, output product. MASK (the row's partial last block
   // only) drops the keys at or past n: their slots may hold anything, NaN included.
@@ -233,7 +271,7 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
 #pragma unroll
           for (int t = 0; t < NH; ++t) o[u][t] *= al;
           m[u] = bms;
-          thr[u] = (bms + kRescale) / qk_scale;
+          thr[u] = (bms + kRescale) * inv_qk;
         }
       }
     }
@@ -274,10 +312,11 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
 
   // This wave's blocks are wave, wave + 4, ...; they are taken in windows of up to 64, whose block
   // ids one load brings in (one per lane; the first window's is issued before the row length is
-  // known: the table row always has bt_stride entries). A ring of three fragments keeps two blocks
-  // in flight while one is computed; the ring is unrolled so no fragment is copied, and every load
-  // is issued unconditionally (past the window's end it re-reads the window's last block, which is
-  // already cached, and the compute is skipped), so each wait covers exactly the fragment it needs.
+  // known: the table row always has bt_stride entries). A ring of RING fragments keeps RING - 1
+  // blocks in flight while one is computed; the ring is unrolled so no fragment is copied, and
+  // every load is issued unconditionally (past the window's end it re-reads the window's last
+  // block, which is already cached, and the compute is skipped), so each wait covers exactly the
+  // fragment it needs.
   auto window_ids = [&](int w0, int cnt) {
     const int e = w0 + (lane < cnt ? lane : cnt - 1);
     const int idx = wave + e * kWaves;
@@ -328,16 +367,16 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     };
     auto id_at = [&](int j) { return __builtin_amdgcn_readlane(ids, pos_at(j)); };
     auto blk_at = [&](int j) { return wave + (w0 + pos_at(j)) * kWaves; };
-    Frag f0, f1, f2;
-    load(f0, id_at(0));
-    load(f1, id_at(1));
-    for (int j = 0; j < nv; j += 3) {
-      load(f2, id_at(j + 2));
-      compute(std::false_type{}, f0, blk_at(j), n);
-      load(f0, id_at(j + 3));
-      if (j + 1 < nv) compute(std::false_type{}, f1, blk_at(j + 1), n);
-      load(f1, id_at(j + 4));
-      if (j + 2 < nv) compute(std::false_type{}, f2, blk_at(j + 2), n);
+    Frag f[RING];
+#pragma unroll
+    for (int r = 0; r + 1 < RING; ++r) load(f[r], id_at(r));
+    for (int j = 0; j < nv; j += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        // the slot computed one step ago takes the block RING - 1 ahead
+        load(f[(r + RING - 1) % RING], id_at(j + r + RING - 1));
+        if (r == 0 || j + r < nv) compute(std::false_type{}, f[r], blk_at(j + r), n);
+      }
     }
   }
   if (n % kBlock != 0 && nfull % kWaves == wave) {
@@ -352,42 +391,61 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     }
   }
 
-  // merge the waves through LDS
+  // merge the waves through LDS: each wave parks its rows' outputs (a query row's D values
+  // contiguous), maxima and sums
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
 #pragma unroll
     for (int t = 0; t < NH; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sm.o[wave][u][16 * t + 4 * grp + j][col] = o[u][t][j];
+      *reinterpret_cast<f32x4_t*>(&sm.o[wave][u][col][16 * t + 4 * grp]) = o[u][t];
     if (grp == 0) {
       sm.m[wave][u][col] = m[u];
       sm.l[wave][u][col] = ls[u][0];
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < TR * D; idx += 64 * kWaves) {
-    const int rr = idx / D;
-    const int d = idx % D;
-    const int u = rr / kTileRows;
-    const int c = rr % kTileRows;
-    const int rg = tile * TR + rr;
-    if (rg >= R) continue;
+  // TPR threads per query row, DPT consecutive dims each: a row's weights and normaliser are
+  // formed once per thread, not once per output element
+  constexpr int TPR = 64 * kWaves / TR;
+  constexpr int DPT = D / TPR;
+  static_assert(TPR * TR == 64 * kWaves && DPT * TPR == D && DPT % 2 == 0, "merge layout");
+  const int rr = threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * DPT;
+  const int u = rr / kTileRows;
+  const int c = rr % kTileRows;
+  const int rg = tile * TR + rr;
+  if (rg < R) {
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][u][c]);
-    float A = 0.f, L = 0.f;
+    float fw[kWaves], L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = sm.m[w][u][c];
-      const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - mx);
-      A = fmaf(f, sm.o[w][u][d][c], A);
-      L = fmaf(f, sm.l[w][u][c], L);
+      fw[w] = (mw == kNegInf) ? 0.f : exp2_fast(mw - mx);
+      L = fmaf(fw[w], sm.l[w][u][c], L);
     }
-    const int i = rg / G;
-    const int h = g * G + rg % G;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    float A[DPT];
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) A[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+      for (int k = 0; k < DPT; k += 2) {
+        const f32x2_t x = *reinterpret_cast<const f32x2_t*>(&sm.o[w][u][c][d0 + k]);
+        A[k] = fmaf(fw[w], x[0], A[k]);
+        A[k + 1] = fmaf(fw[w], x[1], A[k + 1]);
+      }
+    }
+    int i, hg;
+    split_row(rg, i, hg);
+    const int h = g * G + hg;
     const size_t oi = ((size_t)row * a.n_q + i) * a.H_q + h;
-    a.out[oi * D + d] = L > 0.f ? A / L : 0.f;
-    if (a.lse != nullptr && d == 0) a.lse[oi] = L > 0.f ? (mx + __log2f(L)) * kLn2 : kNegInf;
+    float* op = a.out + oi * D + d0;
+#pragma unroll
+    for (int k = 0; k < DPT; k += 2) *reinterpret_cast<f32x2_t*>(op + k) = {A[k] * inv, A[k + 1] * inv};
+    if (a.lse != nullptr && d0 == 0) a.lse[oi] = L > 0.f ? (mx + __log2f(L)) * kLn2 : kNegInf;
   }
 }
 
