@@ -713,11 +713,88 @@ __device__ __forceinline__ void merge_splits_one_wave(const DecodeArgs& a, int r
     a.lse[(size_t)row * a.H_q + hq] = W > 0.f ? (mx + __log2f(W)) * kLn2 : kNegInf;
 }
 
+// Waves that merge one row's splits: a function of the row's own split count only, so a row's
+// result never depends on the rest of the batch. lse_reduce_kernel brings reduce_waves(s_max) waves
+// per (row, query head).
+__host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (ns <= 64 ? 4 : 8); }
+// partial outputs per batch of loads of a wave's range
+template <int NW>
+constexpr int merge_batch() { return NW == 1 ? 8 : (NW == 4 ? 16 : 32); }
+
+// One wave's merge of the splits [sb, se) of one (row, query head): the maximum of their lse, each weight 2^(lse_s - max) by lane and the weights'
+// sum across the wave, the outputs accumulated in split order in batches of KSPEC. lse0 holds the
+// lse of split sb + lane (slots past se may hold anything), v0 / v1 the outputs (dims lane and
+// 64 + lane) of splits sb .. sb + KSPEC - 1 with indices clamped to se - 1, loaded by the caller.
+template <int KSPEC>
+__device__ __forceinline__ void range_merge(const float* po, const float* pls, int D, int sb, int se,
+                                            int lane, float lse0, float* v0, float* v1, float& mx,
+                                            float& W, float& A0, float& A1) {
+  auto ld = [&](const float* p) { return *p; };
+  mx = lane < se - sb ? lse0 : kNegInf;
+  for (int s = sb + 64 + lane; s < se; s += 64) mx = fmaxf(mx, ld(pls + s));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  W = 0.f;
+  A0 = 0.f;
+  A1 = 0.f;
+  for (int s0 = sb; s0 < se; s0 += 64) {
+    float ls = s0 == sb ? lse0 : (s0 + lane < se ? ld(pls + s0 + lane) : kNegInf);
+    if (s0 + lane >= se) ls = kNegInf;
+    const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
+    W += w;
+    const int wb = __builtin_bit_cast(int, w);
+    const int cnt = se - s0 < 64 ? se - s0 : 64;
+    for (int k = 0; k < cnt; k += KSPEC) {
+      if (s0 + k > sb) {
+#pragma unroll
+        for (int i = 0; i < KSPEC; ++i) {
+          const int si = s0 + k + i < se - 1 ? s0 + k + i : se - 1;
+          v0[i] = lane < D ? ld(po + (size_t)si * D + lane) : 0.f;
+          v1[i] = D > 64 ? ld(po + (size_t)si * D + 64 + lane) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KSPEC; ++i) {
+        const bool ok = k + i < cnt;
+        // lanes past the range hold w = 0; the select also drops stale slots' values
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
+        A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
+        A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+}
+
+// The combination of nw ranges' (max, weight sum, outputs), in range order.
+__device__ __forceinline__ void combine_ranges(int nw, const float* mxs, const float* Ws,
+                                               const float* A0s, const float* A1s, int lane, int D,
+                                               float& mx, float& W, float& A0, float& A1) {
+  float M = kNegInf;
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, mxs[w]);
+  float Wt = 0.f, B0 = 0.f, B1 = 0.f;
+  for (int w = 0; w < nw; ++w) {
+    const float mw = mxs[w];
+    const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+    Wt = fmaf(f, Ws[w], Wt);
+    if (lane < D) B0 = fmaf(f, A0s[w], B0);
+    if (D > 64) B1 = fmaf(f, A1s[w], B1);
+  }
+  mx = M;
+  W = Wt;
+  A0 = B0;
+  A1 = B1;
+}
+
 // Called by every thread of a workgroup whose chunk wrote its partial result with device-coherent
 // stores. No cache-wide fence is taken (an L2 write-back and invalidate per workgroup would stall
 // the whole launch): each thread waits for its own stores to be acknowledged, the workgroup meets
 // at a barrier, and only then is the count bumped; the merging wave reads with device-coherent
-// loads.
+// loads. (Rows of more than 16 splits are left to lse_reduce_kernel: a two-level merge of their
+// ranges inside the grid, by the last workgroup of each range and then of the row, gave the
+// kernel's bits but lengthened the end of the launch, 185.0 against 184.7 us on the long-context
+// step and 56.3 against 50.3 us on one GPU's quarter of it.)
 template <int D, int G>
 __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, const Chunk& ch, int lane,
                                               int wave, int* s_last) {
@@ -748,13 +825,14 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, const Chunk& 
 #ifndef PA_DECODE_MIN_WG_PER_CU
 #define PA_DECODE_MIN_WG_PER_CU 3
 #endif
-template <typename T>
+template <typename T, int G>
 constexpr int grid_min_wg() {
-  return sizeof(T) == 2 && PA_DECODE_MIN_WG_PER_CU > 0 ? PA_DECODE_MIN_WG_PER_CU : 1;
+  // G = 8 instances need more registers than 3 waves per SIMD allow: they would spill
+  return sizeof(T) == 2 && G <= 4 && PA_DECODE_MIN_WG_PER_CU > 0 ? PA_DECODE_MIN_WG_PER_CU : 1;
 }
 
 template <typename T, int D, int G, bool PADDED, bool COMPACT>
-__global__ __launch_bounds__(64 * kWaves, grid_min_wg<T>()) void decode_vector_kernel(
+__global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vector_kernel(
     const DecodeArgs a) {
   using W = Worker<T, D, G, PADDED>;
   __shared__ typename W::Smem sm;
@@ -834,12 +912,11 @@ __global__ __launch_bounds__(64 * kWaves, grid_min_wg<T>()) void decode_vector_k
   w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
-  if constexpr (!COMPACT) {
-    // merge_counts is set only when no row of the launch has more than kGridMergeSplits splits
-    if (a.merge_counts != nullptr && ch.ns > 1) {
-      __shared__ int s_last;
-      merge_if_last<D, G>(a, ch, w.lane, w.wave, &s_last);
-    }
+  // merge_counts is set only for the split grid, when no row of the launch has more than
+  // kGridMergeSplits splits
+  if (a.merge_counts != nullptr && ch.ns > 1) {
+    __shared__ int s_last;
+    merge_if_last<D, G>(a, ch, w.lane, w.wave, &s_last);
   }
 }
 
@@ -1116,9 +1193,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
   }
 }
 
-// Waves that merge one row's splits: a function of the row's own split count only, so a row's
-// result never depends on the rest of the batch. The launch brings reduce_waves(s_max).
-__host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (ns <= 64 ? 4 : 8); }
 
 // Merge the split partials of one (row, query head): out = sum_s w_s o_s / sum_s w_s with
 // w_s = 2^(lse_s - max lse); lse = max + log2(sum w_s), returned in natural-log units.
@@ -1132,7 +1206,7 @@ __host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (
 template <bool PADDED, int NW>
 __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a) {
   // partial outputs per batch of loads: a long row's wave covers its whole range in one or two
-  constexpr int kSpec = NW == 1 ? 8 : (NW == 4 ? 16 : 32);
+  constexpr int kSpec = merge_batch<NW>();
   __shared__ float s_acc[NW][128];
   __shared__ float s_mw[NW][2];
   const int hq = blockIdx.x;
@@ -1144,6 +1218,7 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
   if (a.counter != nullptr && hq == 0 && row == 0 && threadIdx.x == 0) *a.counter = 0;
   const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
   const float* po = a.part_o + base * D;
+  const float* pls = a.part_lse + base;
   // this lane's dims (lane, and 64 + lane when D = 128) of the partial outputs of splits
   // s0 + [0, kSpec), indices clamped into [0, last]
   auto load_batch = [&](int s0, int last, float* v0, float* v1) {
@@ -1158,7 +1233,7 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
   float v0[kSpec], v1[kSpec];
   float lse0 = kNegInf;
   if (wave == 0) {
-    lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
+    lse0 = lane < a.s_max ? pls[lane] : kNegInf;
     load_batch(0, a.s_max - 1, v0, v1);
   }
   int gs, gsh;
@@ -1170,39 +1245,12 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
   const int sb = wave < nw ? wave * per : ns;
   const int se = sb + per < ns ? sb + per : ns;
   if (wave > 0 && sb < se) {
-    lse0 = lane < se - sb ? a.part_lse[base + sb + lane] : kNegInf;
+    lse0 = lane < se - sb ? pls[sb + lane] : kNegInf;
     load_batch(sb, se - 1, v0, v1);
   }
 
   float mx = kNegInf, W = 0.f, A0 = 0.f, A1 = 0.f;
-  if (sb < se) {
-    // maximum over this wave's splits' lse
-    mx = lane < se - sb ? lse0 : kNegInf;
-    for (int s = sb + 64 + lane; s < se; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    for (int s0 = sb; s0 < se; s0 += 64) {
-      float ls = s0 == sb ? lse0 : (s0 + lane < se ? a.part_lse[base + s0 + lane] : kNegInf);
-      if (s0 + lane >= se) ls = kNegInf;
-      const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
-      W += w;
-      const int wb = __builtin_bit_cast(int, w);
-      const int cnt = se - s0 < 64 ? se - s0 : 64;
-      for (int k = 0; k < cnt; k += kSpec) {
-        if (s0 + k > sb) load_batch(s0 + k, se - 1, v0, v1);
-#pragma unroll
-        for (int i = 0; i < kSpec; ++i) {
-          const bool ok = k + i < cnt;
-          // lanes past the range hold w = 0; the select also drops stale slots' values
-          const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
-          A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
-          A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
-  }
+  if (sb < se) range_merge<kSpec>(po, pls, D, sb, se, lane, lse0, v0, v1, mx, W, A0, A1);
   if constexpr (NW > 1) {
     if (lane < D) s_acc[wave][lane] = A0;
     if (D > 64) s_acc[wave][64 + lane] = A1;
@@ -1213,20 +1261,15 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
     __syncthreads();
     if (wave != 0) return;
     if (nw > 1) {
-      float M = kNegInf;
-      for (int w = 0; w < nw; ++w) M = fmaxf(M, s_mw[w][0]);
-      float Wt = 0.f, B0 = 0.f, B1 = 0.f;
-      for (int w = 0; w < nw; ++w) {
-        const float mw = s_mw[w][0];
-        const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-        Wt = fmaf(f, s_mw[w][1], Wt);
-        if (lane < D) B0 = fmaf(f, s_acc[w][lane], B0);
-        if (D > 64) B1 = fmaf(f, s_acc[w][64 + lane], B1);
+      float mxs[NW], Ws[NW], A0s[NW], A1s[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        mxs[w] = s_mw[w][0];
+        Ws[w] = s_mw[w][1];
+        A0s[w] = lane < D ? s_acc[w][lane] : 0.f;
+        A1s[w] = D > 64 ? s_acc[w][64 + lane] : 0.f;
       }
-      mx = M;
-      W = Wt;
-      A0 = B0;
-      A1 = B1;
+      combine_ranges(nw, mxs, Ws, A0s, A1s, lane, D, mx, W, A0, A1);
     }
   }
   float* out = a.out + ((size_t)row * a.H_q + hq) * D;
