@@ -980,6 +980,11 @@ def main():
                             "the splits)")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "cache": ("warm: decode calls back to back; the flushed figures write "
+                               f"{args.flush_mb} MB between single calls"),
+                     "achieved_flushed": round(kv_bytes / (statistics.median(fl) * 1e-3) / 1e9, 1),
+                     "frac_flushed": round(kv_bytes / (statistics.median(fl) * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
                                  if traffic is not None else None),
                      "kernel": ("pa_decode_attention call (decode_vector_kernel, split grid "
