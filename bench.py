@@ -28,6 +28,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=128 ragged bf16"
 METRIC_LONG = "paged decode-attn K/V GB/s (% HBM peak) + µs/step, B=4 long-context bf16"
+METRIC_PADDED = ("right-padded decode-attn K/V GB/s (% HBM peak) + µs/step, B=128 ragged bf16 "
+                 "(padding gaps skipped)")
 # one GPU's share of a sharded step (the lengths of the whole workload, cut as the sharding cuts)
 METRIC_SHARE = {
     "b128-tp2": "paged decode-attn K/V GB/s (% HBM peak), B=128 bf16, one GPU of 2 (KV heads split)",
@@ -45,12 +47,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="b128",
                    choices=["b128", "long", "mq", "mq-sparse", "b16", "mq-tokenize",
-                            "b128-tp2", "b128-dp2", "long-sp4"],
+                            "b128-padded", "b128-tp2", "b128-dp2", "long-sp4"],
                    help="b128 is the reported workload; long (B=4 long-context split-K), mq "
                         "(latent cross-attention on the matrix cores; mq-sparse under the "
                         "temporal block mask), b16 (the B=16 lockstep step, paged and "
-                        "right-padded) and mq-tokenize (the fused spike tokenizer + K/V "
-                        "projection) measure the other paths; b128-tp2, b128-dp2 and long-sp4 "
+                        "right-padded), b128-padded (the B=128 step laid out right-padded) and "
+                        "mq-tokenize (the fused spike tokenizer + K/V projection) measure the "
+                        "other paths; b128-tp2, b128-dp2 and long-sp4 "
                         "measure one GPU's share of a sharded step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512,
@@ -814,6 +817,142 @@ def main_b16(args):
     print(json.dumps(out_line), flush=True)
 
 
+def main_b128_padded(args):
+    """The B=128 step in the right-padded lockstep layout: each row's history in columns
+    [0, n_b) of a [128][8][8140][64] bf16 pool, the step's token at the common column 8139, the
+    gap [n_b, 8139) never read. One pa_append_decode_attention_padded call per step (append folded
+    into the split grid, which merges its own splits); the same K/V bytes as the paged step. The
+    paged decode of the same rows runs in the same process for comparison."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_177_amd import binding as B
+    from paged_kv_cache_177_amd.runner import PaddedLockstep, PagedStep, to_torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    case = W.b128()
+    pc = W.padded_from_paged(case)
+    kv_bytes = case.kv_bytes()
+    stream = torch.cuda.current_stream()
+    L = PaddedLockstep(pc.dtype, pc.num_q_heads, pc.num_kv_heads, pc.head_dim, pc.batch,
+                       pc.seq_cap, device=dev)
+    L.kv.k.copy_(to_torch(pc.k_pad, pc.dtype))
+    L.kv.v.copy_(to_torch(pc.v_pad, pc.dtype))
+    pc.k_pad = pc.v_pad = None  # host copies no longer needed
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    pos, dest = d(pc.positions), d(pc.dest)
+    k_new, v_new = to_torch(pc.k_new, pc.dtype).to(dev), to_torch(pc.v_new, pc.dtype).to(dev)
+    q = to_torch(pc.q, pc.dtype).to(dev)
+    gs, ge = d(pc.prefix_lens.astype(np.int32)), d(np.full(pc.batch, pc.padded_len, np.int32))
+    out = torch.empty((pc.batch, pc.num_q_heads, pc.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((pc.batch, pc.num_q_heads), dtype=torch.float32, device=dev)
+    need = B.pa_decode_attention_padded(L.kv.pool, q, pc.num_q_heads, pc.batch, gs, ge,
+                                        pc.kv_cols, pc.scale, out=out, query_workspace=True)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    wsa = ws if need else None
+
+    def fused_step():
+        B.pa_append_decode_attention_padded(L.kv.pool, pos, dest, k_new, v_new, q, None,
+                                            pc.num_q_heads, gs, ge, pc.kv_cols, pc.batch,
+                                            pc.scale, workspace=wsa, out=out, lse=lse)
+
+    def decode():
+        B.pa_decode_attention_padded(L.kv.pool, q, pc.num_q_heads, pc.batch, gs, ge, pc.kv_cols,
+                                     pc.scale, workspace=wsa, out=out, lse=lse)
+
+    def separate_step():
+        L.append(pos, dest, k_new, v_new)
+        decode()
+
+    def timed(fn):
+        t_w = time.perf_counter()
+        done = 0
+        while done < args.warmup or time.perf_counter() - t_w < 1.0:
+            for _ in range(10):
+                fn()
+            done += 10
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, a.elapsed_time(b) / args.steps
+
+    ms_per_step, step_ev_ms = timed(fused_step)
+    sep_ms, sep_ev_ms = timed(separate_step)
+    _, dec_avg_ms = timed(decode)
+
+    flush = torch.empty(args.flush_mb * (1 << 20), dtype=torch.uint8, device=dev)
+    fl = []
+    for _ in range(10):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        decode()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl.append(a.elapsed_time(b))
+    del flush
+
+    # the paged decode of the same rows, timed the same way (same process, same clocks)
+    r = PagedStep(case, device=dev)
+    r.append()
+    _, paged_dec_ms = timed(r.decode)
+
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    flushed_gbs = kv_bytes / (statistics.median(fl) * 1e-3) / 1e9
+    out_line = {
+        "metric": METRIC_PADDED,
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"b128 right-padded: B={pc.batch} rows, histories "
+                                f"{int(pc.prefix_lens.min())}..{pc.padded_len} columns, padded "
+                                f"to {pc.padded_len} + the step's column, H_q={pc.num_q_heads}, "
+                                f"H_kv={pc.num_kv_heads}, D={pc.head_dim}, seed {case.seed}"),
+                   "global_batch": pc.batch, "kv_bytes_per_step": kv_bytes,
+                   "step": ("append_kv + padded decode + lse merge: "
+                            "pa_append_decode_attention_padded (one launch)")},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "cache": ("warm: decode calls back to back; the flushed figures write "
+                               f"{args.flush_mb} MB between single calls"),
+                     "achieved_flushed": round(flushed_gbs, 1),
+                     "frac_flushed": round(flushed_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": ("pa_decode_attention_padded call (decode_vector_kernel, padded "
+                                "split grid merging its own splits)"),
+                     "bytes_per_launch": kv_bytes,
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
+        "detail": {"us_per_step": round(ms_per_step * 1e3, 2),
+                   "us_per_step_events": round(step_ev_ms * 1e3, 2),
+                   "us_per_step_separate_calls": round(sep_ms * 1e3, 2),
+                   "us_per_step_separate_calls_events": round(sep_ev_ms * 1e3, 2),
+                   "decode_us_flushed_median": round(statistics.median(fl) * 1e3, 2),
+                   "paged_decode_us_same_run": round(paged_dec_ms * 1e3, 2),
+                   "padded_over_paged_decode_time": round(dec_avg_ms / paged_dec_ms, 4),
+                   "padded_pool_bytes": int(L.kv.k.numel() * L.kv.k.element_size() * 2),
+                   "source_hash": kernel_source_hash(*DECODE_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        out_line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -827,6 +966,9 @@ def main():
         return main_tokenize(args)
     if args.workload == "b16":
         main_b16(args)
+        return
+    if args.workload == "b128-padded":
+        main_b128_padded(args)
         return
 
     import numpy as np

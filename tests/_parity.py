@@ -129,16 +129,21 @@ def assert_attention_close(got, ref, dtype, what="out"):
 
 
 def check_rows(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale, what,
-               rows=None, q_shared=False):
+               rows=None, q_shared=False, gather=None):
     """Every row (or ``rows``) of a paged decode result against the oracle, gathered row by row
     through its block table: the acceptance tolerance over all compared elements, and the derived
     bound element by element. out (B, [n_q,] H_q, D), lse (B, [n_q,] H_q) from the GPU; q the
-    queries the decode read (B, H_q, D) storage, or (n_q, H_q, D) when q_shared. Returns the
-    record (max, mean, and the largest error / derived bound ratio)."""
+    queries the decode read (B, H_q, D) storage, or (n_q, H_q, D) when q_shared. ``gather(b)``,
+    when given, returns row b's keys and values instead (a right-padded row's valid columns); the
+    pools and block tables are then unused and kv_lens[b] is the row's valid-column count.
+    Returns the record (max, mean, and the largest error / derived bound ratio)."""
     rows = range(len(kv_lens)) if rows is None else rows
     d_out, d_lse, ratio = [], [], 0.0
     for b in rows:
-        K, V = O.gather_paged(k_pool, v_pool, dtype, block_tables[b], kv_lens[b])
+        if gather is not None:
+            K, V = gather(b)
+        else:
+            K, V = O.gather_paged(k_pool, v_pool, dtype, block_tables[b], kv_lens[b])
         qb = O.storage_to_f64(q if q_shared else q[b], dtype)
         if qb.ndim == 2:
             qb = qb[None]
