@@ -721,72 +721,6 @@ __host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (
 template <int NW>
 constexpr int merge_batch() { return NW == 1 ? 8 : (NW == 4 ? 16 : 32); }
 
-// One wave's merge of the splits [sb, se) of one (row, query head): the maximum of their lse, each weight 2^(lse_s - max) by lane and the weights'
-// sum across the wave, the outputs accumulated in split order in batches of KSPEC. lse0 holds the
-// lse of split sb + lane (slots past se may hold anything), v0 / v1 the outputs (dims lane and
-// 64 + lane) of splits sb .. sb + KSPEC - 1 with indices clamped to se - 1, loaded by the caller.
-template <int KSPEC>
-__device__ __forceinline__ void range_merge(const float* po, const float* pls, int D, int sb, int se,
-                                            int lane, float lse0, float* v0, float* v1, float& mx,
-                                            float& W, float& A0, float& A1) {
-  auto ld = [&](const float* p) { return *p; };
-  mx = lane < se - sb ? lse0 : kNegInf;
-  for (int s = sb + 64 + lane; s < se; s += 64) mx = fmaxf(mx, ld(pls + s));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  W = 0.f;
-  A0 = 0.f;
-  A1 = 0.f;
-  for (int s0 = sb; s0 < se; s0 += 64) {
-    float ls = s0 == sb ? lse0 : (s0 + lane < se ? ld(pls + s0 + lane) : kNegInf);
-    if (s0 + lane >= se) ls = kNegInf;
-    const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
-    W += w;
-    const int wb = __builtin_bit_cast(int, w);
-    const int cnt = se - s0 < 64 ? se - s0 : 64;
-    for (int k = 0; k < cnt; k += KSPEC) {
-      if (s0 + k > sb) {
-#pragma unroll
-        for (int i = 0; i < KSPEC; ++i) {
-          const int si = s0 + k + i < se - 1 ? s0 + k + i : se - 1;
-          v0[i] = lane < D ? ld(po + (size_t)si * D + lane) : 0.f;
-          v1[i] = D > 64 ? ld(po + (size_t)si * D + 64 + lane) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < KSPEC; ++i) {
-        const bool ok = k + i < cnt;
-        // lanes past the range hold w = 0; the select also drops stale slots' values
-        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
-        A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
-        A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
-}
-
-// The combination of nw ranges' (max, weight sum, outputs), in range order.
-__device__ __forceinline__ void combine_ranges(int nw, const float* mxs, const float* Ws,
-                                               const float* A0s, const float* A1s, int lane, int D,
-                                               float& mx, float& W, float& A0, float& A1) {
-  float M = kNegInf;
-  for (int w = 0; w < nw; ++w) M = fmaxf(M, mxs[w]);
-  float Wt = 0.f, B0 = 0.f, B1 = 0.f;
-  for (int w = 0; w < nw; ++w) {
-    const float mw = mxs[w];
-    const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-    Wt = fmaf(f, Ws[w], Wt);
-    if (lane < D) B0 = fmaf(f, A0s[w], B0);
-    if (D > 64) B1 = fmaf(f, A1s[w], B1);
-  }
-  mx = M;
-  W = Wt;
-  A0 = B0;
-  A1 = B1;
-}
-
 // Called by every thread of a workgroup whose chunk wrote its partial result with device-coherent
 // stores. No cache-wide fence is taken (an L2 write-back and invalidate per workgroup would stall
 // the whole launch): each thread waits for its own stores to be acknowledged, the workgroup meets
@@ -912,11 +846,14 @@ __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vec
   w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
-  // merge_counts is set only for the split grid, when no row of the launch has more than
-  // kGridMergeSplits splits
-  if (a.merge_counts != nullptr && ch.ns > 1) {
-    __shared__ int s_last;
-    merge_if_last<D, G>(a, ch, w.lane, w.wave, &s_last);
+  if constexpr (!COMPACT) {
+    // merge_counts is set only for the split grid, when no row of the launch has more than
+    // kGridMergeSplits splits (the compact grid leaves the merge to lse_reduce_kernel: carrying
+    // the unused merge code made its long-context launch 1.7 us slower)
+    if (a.merge_counts != nullptr && ch.ns > 1) {
+      __shared__ int s_last;
+      merge_if_last<D, G>(a, ch, w.lane, w.wave, &s_last);
+    }
   }
 }
 
@@ -1218,7 +1155,6 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
   if (a.counter != nullptr && hq == 0 && row == 0 && threadIdx.x == 0) *a.counter = 0;
   const size_t base = ((size_t)row * a.H_q + hq) * a.s_max;
   const float* po = a.part_o + base * D;
-  const float* pls = a.part_lse + base;
   // this lane's dims (lane, and 64 + lane when D = 128) of the partial outputs of splits
   // s0 + [0, kSpec), indices clamped into [0, last]
   auto load_batch = [&](int s0, int last, float* v0, float* v1) {
@@ -1233,7 +1169,7 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
   float v0[kSpec], v1[kSpec];
   float lse0 = kNegInf;
   if (wave == 0) {
-    lse0 = lane < a.s_max ? pls[lane] : kNegInf;
+    lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
     load_batch(0, a.s_max - 1, v0, v1);
   }
   int gs, gsh;
@@ -1245,12 +1181,39 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
   const int sb = wave < nw ? wave * per : ns;
   const int se = sb + per < ns ? sb + per : ns;
   if (wave > 0 && sb < se) {
-    lse0 = lane < se - sb ? pls[sb + lane] : kNegInf;
+    lse0 = lane < se - sb ? a.part_lse[base + sb + lane] : kNegInf;
     load_batch(sb, se - 1, v0, v1);
   }
 
   float mx = kNegInf, W = 0.f, A0 = 0.f, A1 = 0.f;
-  if (sb < se) range_merge<kSpec>(po, pls, D, sb, se, lane, lse0, v0, v1, mx, W, A0, A1);
+  if (sb < se) {
+    // maximum over this wave's splits' lse
+    mx = lane < se - sb ? lse0 : kNegInf;
+    for (int s = sb + 64 + lane; s < se; s += 64) mx = fmaxf(mx, a.part_lse[base + s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int s0 = sb; s0 < se; s0 += 64) {
+      float ls = s0 == sb ? lse0 : (s0 + lane < se ? a.part_lse[base + s0 + lane] : kNegInf);
+      if (s0 + lane >= se) ls = kNegInf;
+      const float w = (ls == kNegInf) ? 0.f : exp2_fast(ls - mx);
+      W += w;
+      const int wb = __builtin_bit_cast(int, w);
+      const int cnt = se - s0 < 64 ? se - s0 : 64;
+      for (int k = 0; k < cnt; k += kSpec) {
+        if (s0 + k > sb) load_batch(s0 + k, se - 1, v0, v1);
+#pragma unroll
+        for (int i = 0; i < kSpec; ++i) {
+          const bool ok = k + i < cnt;
+          // lanes past the range hold w = 0; the select also drops stale slots' values
+          const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, (k + i) & 63));
+          A0 = fmaf(wk, ok ? v0[i] : 0.f, A0);
+          A1 = fmaf(wk, ok ? v1[i] : 0.f, A1);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  }
   if constexpr (NW > 1) {
     if (lane < D) s_acc[wave][lane] = A0;
     if (D > 64) s_acc[wave][64 + lane] = A1;
@@ -1261,15 +1224,20 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
     __syncthreads();
     if (wave != 0) return;
     if (nw > 1) {
-      float mxs[NW], Ws[NW], A0s[NW], A1s[NW];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        mxs[w] = s_mw[w][0];
-        Ws[w] = s_mw[w][1];
-        A0s[w] = lane < D ? s_acc[w][lane] : 0.f;
-        A1s[w] = D > 64 ? s_acc[w][64 + lane] : 0.f;
+      float M = kNegInf;
+      for (int w = 0; w < nw; ++w) M = fmaxf(M, s_mw[w][0]);
+      float Wt = 0.f, B0 = 0.f, B1 = 0.f;
+      for (int w = 0; w < nw; ++w) {
+        const float mw = s_mw[w][0];
+        const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+        Wt = fmaf(f, s_mw[w][1], Wt);
+        if (lane < D) B0 = fmaf(f, s_acc[w][lane], B0);
+        if (D > 64) B1 = fmaf(f, s_acc[w][64 + lane], B1);
       }
-      combine_ranges(nw, mxs, Ws, A0s, A1s, lane, D, mx, W, A0, A1);
+      mx = M;
+      W = Wt;
+      A0 = B0;
+      A1 = B1;
     }
   }
   float* out = a.out + ((size_t)row * a.H_q + hq) * D;

@@ -201,13 +201,16 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   // issue the loads of one block (physical id pb, already clamped into the pool): a wave-uniform
   // block base plus 32-bit lane byte offsets, the scalar-base form of the global load (no 64-bit
   // address arithmetic per lane and block)
-  unsigned k_off = (unsigned)((col * D + 8 * grp) * 2);
-  unsigned v_off = (unsigned)(lane * 16);
-  asm volatile("" : "+v"(k_off), "+v"(v_off));
+  const unsigned k_off0 = (unsigned)((col * D + 8 * grp) * 2);
+  const unsigned v_off0 = (unsigned)(lane * 16);
   auto load = [&](Frag& f, int pb) {
     const size_t base = ((size_t)pb * a.H_kv + g) * (size_t)(kBlock * D);
     const char* kb = reinterpret_cast<const char*>(kbase + base);
     const char* vb = reinterpret_cast<const char*>(vbase + base);
+    // the offsets pass through an empty asm at every load, so the compiler cannot hoist a 64-bit
+    // widening out of the loop and add the block base in vector registers for every load
+    unsigned k_off = k_off0, v_off = v_off0;
+    asm volatile("" : "+v"(k_off), "+v"(v_off));
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       f.k[c] = *reinterpret_cast<const u32x4_t*>(kb + k_off + 64 * c);
@@ -246,7 +249,9 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
         s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[c]),
                                                        qf[u][c], s[u], 0, 0, 0);
     }
-    bool any_raise = false;
+    // lanes (of any sub-tile) whose own keys call for a raise; the masks are combined in scalar
+    // registers, so the branch takes no vector instruction
+    unsigned long long raise = 0;
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       if (MASK) {
@@ -257,9 +262,9 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
       // raised, to the block maximum over all 16 keys, only when some lane's own keys beat it by
       // more than kRescale; otherwise the block needs no cross-lane step at all.
       lm[u] = fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3]));
-      any_raise = any_raise || lm[u] > thr[u];
+      raise |= __builtin_amdgcn_ballot_w64(lm[u] > thr[u]);
     }
-    if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {
+    if (raise != 0) {
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
         float bm = fmaxf(lm[u], swap_rows16(lm[u]));
