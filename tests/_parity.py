@@ -7,7 +7,7 @@ Two criteria apply to attention results in fp32 from bf16 or fp32 inputs:
     the acceptance tolerance is coarser than the outputs themselves (a 112k-token row averages its
     values down to ~3e-3), so a lost or doubled 16-token block, which moves the output by 2e-4 to
     1e-3, would pass it; the derived bound is ~20x tighter and catches it
-    (test_host_helpers.test_parity_bound_catches_a_dropped_or_doubled_block).
+    (test_parity_bound.test_a_lost_or_doubled_block_fails).
 Every comparison is logged, and recorded for the end-of-session summary (conftest)."""
 
 import math
