@@ -717,6 +717,13 @@ __device__ __forceinline__ void merge_splits_one_wave(const DecodeArgs& a, int r
 // result never depends on the rest of the batch. lse_reduce_kernel brings reduce_waves(s_max) waves
 // per (row, query head).
 __host__ __device__ constexpr int reduce_waves(int ns) { return ns <= 16 ? 1 : (ns <= 64 ? 4 : 8); }
+// Splits per merging wave: a row of at most 16 splits is merged by one wave; up to 64, by waves of
+// 16 consecutive splits; up to 256, of 32; beyond, ceil(ns / 8) each. A function of the row's own
+// split count, so a row's merge is the same in any batch, and fixed over wide ranges of it, so the
+// waves can load their ranges before the row length arrives.
+__host__ __device__ constexpr int split_range(int ns) {
+  return ns <= 16 ? 16 : (ns <= 64 ? 16 : (ns <= 256 ? 32 : (ns + 7) / 8));
+}
 // partial outputs per batch of loads of a wave's range
 template <int NW>
 constexpr int merge_batch() { return NW == 1 ? 8 : (NW == 4 ? 16 : 32); }
@@ -1133,9 +1140,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
 
 // Merge the split partials of one (row, query head): out = sum_s w_s o_s / sum_s w_s with
 // w_s = 2^(lse_s - max lse); lse = max + log2(sum w_s), returned in natural-log units.
-// reduce_waves(ns) waves share the row's splits in contiguous ranges; each merges its range
+// Waves share the row's splits in contiguous ranges of split_range(ns); each merges its range
 // against its own maximum and wave 0 combines their results in wave order. It is latency-bound,
-// so the chain of dependent loads is kept short: wave 0's first 64 partial lse values and first
+// so the chain of dependent loads is kept short: every wave's first 64 partial lse values and first
 // kSpec partial outputs load together with the row length (speculatively: the workspace always
 // holds s_max of each; slots past the range are dropped by a select, so whatever they hold never
 // reaches the sums), and later partial outputs load in batches of kSpec (8, 16 or 32 with the
@@ -1166,21 +1173,26 @@ __global__ __launch_bounds__(64 * NW) void lse_reduce_kernel(const DecodeArgs a)
       v1[i] = D > 64 ? p[64 + lane] : 0.f;
     }
   };
+  // Every wave loads its range before the row length is known: the range of a row's splits per
+  // wave is split_range(ns), guessed here as that of the launch's own wave count (exact for every
+  // row whose split count takes this many waves, which is the longest ones), and loaded again
+  // after the length only when the guess was wrong.
   float v0[kSpec], v1[kSpec];
+  const int sb_guess = wave * (NW == 1 ? kSpec : split_range(NW == 4 ? 64 : 256));
   float lse0 = kNegInf;
-  if (wave == 0) {
-    lse0 = lane < a.s_max ? a.part_lse[base + lane] : kNegInf;
-    load_batch(0, a.s_max - 1, v0, v1);
+  if (sb_guess < a.s_max) {
+    lse0 = lane < a.s_max - sb_guess ? a.part_lse[base + sb_guess + lane] : kNegInf;
+    load_batch(sb_guess, a.s_max - 1, v0, v1);
   }
   int gs, gsh;
   const int n = row_valid<PADDED>(a, row, &gs, &gsh);
   const int ns = num_splits(n, chunk_tokens(D));
   if (ns <= 1) return;  // the same for every wave of the workgroup
-  const int nw = reduce_waves(ns);
-  const int per = (ns + nw - 1) / nw;
+  const int per = split_range(ns);
+  const int nw = (ns + per - 1) / per;
   const int sb = wave < nw ? wave * per : ns;
   const int se = sb + per < ns ? sb + per : ns;
-  if (wave > 0 && sb < se) {
+  if (sb < se && sb != sb_guess) {
     lse0 = lane < se - sb ? a.part_lse[base + sb + lane] : kNegInf;
     load_batch(sb, se - 1, v0, v1);
   }
