@@ -42,6 +42,7 @@
 #include "pa_internal.h"
 
 #include <map>
+#include <type_traits>
 #include <mutex>
 #include <tuple>
 
@@ -291,6 +292,16 @@ struct Worker {
         qk_scale(args.scale * kLog2e),
         kbase(reinterpret_cast<const T*>(args.k)),
         vbase(reinterpret_cast<const T*>(args.v)) {}
+
+  // LDS that a worker needs besides the epilogue's (none for this one)
+  template <typename S>
+  __device__ __forceinline__ void bind(S&) {}
+  // this chunk's queries, from memory or from the chunk's G x D queries staged in LDS
+  __device__ __forceinline__ void load_queries(int row, int g) { load_q(q, row, g); }
+  __device__ __forceinline__ void load_queries_from(const T* qs) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) q[h].load_cached(qs + h * D + c * 8);
+  }
 
   // queries of the G heads of KV head g in row `row`: this lane's 8 dims of each
   __device__ __forceinline__ void load_q(Vec8<T>* qq, int row, int g) const {
@@ -624,6 +635,313 @@ struct Worker {
   }
 };
 
+// ---- the single-query worker on the matrix cores (bf16) -------------------------------------------
+// The same chunks, the same dealing of a chunk's blocks to the waves and the same end-of-chunk
+// combination as Worker (whose helpers it inherits), with each block's arithmetic on the matrix
+// cores. A wave's G query heads are the columns of one 16-column tile (columns G .. 15 are zero), so
+// per block and wave:
+//   S^T[16 keys][16 q] = K[16 keys][D] . Q^T[D][16 q]      v_mfma_f32_16x16x32_bf16, D/32 steps
+//     K is the A operand loaded straight from the block (lane: key l%16, dims 32c + 8(l/16) .. +7),
+//     Q^T the B operand (lane: head l%16, the same dims); lane l gets head l%16, keys 4(l/16)..+3.
+//   online softmax per head, its running max shared by its four lanes (l%16 + 16k): raised to the
+//     block maximum only when some lane's scores beat it by more than kRescale (a wave ballot
+//     against a threshold kept in raw score units), so most blocks take no cross-lane step;
+//   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   v_mfma_f32_16x16x16_bf16, D/16 tiles
+//     P^T is the first product's result in place; V^T comes from the block staged in the wave's LDS
+//     area and read back transposed (ds_read_b64_tr_b16). P enters as two bf16 parts, hi + lo
+//     (within 2^-18 of each fp32 weight), and the weight sums come from the same products (a
+//     constant A operand whose row 0 is ones): numerator and denominator see the same weights.
+// A lane keeps its head's outputs for dims 16t + 4(l/16) .. +3, so no lane merge is needed.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Two fp32 weights -> their bf16 parts rounded to nearest (one packed conversion) and the bf16 of
+// what those leave over.
+__device__ __forceinline__ void split_bf16x2(float p0, float p1, unsigned& hi, unsigned& lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t));
+  const f32x2_t h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{p0, p1} - h, bf16x2_t));
+}
+
+// ds_read_b64_tr_b16: within each 16-lane quarter-wave, lanes 4j .. 4j + 3 name (8-byte addresses,
+// 4 elements each) row j of a 4 x 16 block of 16-bit elements; lane l receives element l of rows
+// 0 .. 3.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(
+          (__attribute__((address_space(3))) const unsigned short*)p));
+}
+
+template <int D, int G, bool PADDED>
+struct WorkerM : Worker<__bf16, D, G, PADDED> {
+  using Base = Worker<__bf16, D, G, PADDED>;
+  using Base::a;
+  using Base::lane;
+  using Base::wave;
+  using Base::qk_scale;
+  using Base::kbase;
+  using Base::vbase;
+  static constexpr int KC = D / 32;  // 32-dim steps of the score product
+  static constexpr int NH = D / 16;  // 16-dim tiles of the output product
+  static constexpr int VC = D / 32;  // 16-byte pieces per lane of a block's V (32 D bytes)
+  static_assert(G <= 16, "a group's heads fill at most one 16-column tile");
+  // a block's K and V as loaded: lane l holds elements 8l + 512c .. +7 of each [16][D] array
+  // (whole 1 KB runs per load instruction), rearranged through LDS for the products
+  struct Frag {
+    u32x4_t k[KC];
+    u32x4_t v[VC];
+  };
+  // K rows padded by 8 elements (16 bytes): the 16 lanes of a quarter-wave, reading one 16-byte
+  // piece of 16 different rows, then fall on 16 disjoint groups of 4 banks
+  static constexpr int kKRow = D + 8;
+  struct Smem : EpilogueSmem<G, D, kWaves> {
+    unsigned short vst[kWaves][kBlock * D];     // each wave's staged V block
+    unsigned short kst[kWaves][kBlock * kKRow];  // and K block
+  };
+
+  const int col, grp;
+  const float inv_qk;  // 1 / qk_scale: the raise threshold in raw score units
+  Smem* smp = nullptr;
+  Vec8<__bf16> qf[KC];  // Q^T fragments: head col (zero past G), dims 32c + 8 grp .. +7
+  float mq, thr;        // the head's running max (log2 units) and its raise threshold
+  f32x4_t o[NH], ls;    // O^T accumulators; the weight sum in element 0 of the lanes grp == 0
+
+  __device__ __forceinline__ explicit WorkerM(const DecodeArgs& args)
+      : Base(args), col(lane & 15), grp(lane >> 4), inv_qk(1.0f / qk_scale) {}
+
+  __device__ __forceinline__ void bind(Smem& sm) { smp = &sm; }
+
+  __device__ __forceinline__ void load_queries(int row, int g) {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (size_t)row * a.q_row_stride +
+                       ((size_t)g * G + (col < G ? col : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (col < G) qf[c].load_cached(qp + 32 * c);
+      else qf[c].zero();
+    }
+  }
+  __device__ __forceinline__ void load_queries_from(const __bf16* qs) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (col < G) qf[c].load_cached(qs + col * D + 32 * c + 8 * grp);
+      else qf[c].zero();
+    }
+  }
+
+  // Rotate the queries at pos (pools with RoPE tables; each piece's partner half, dims d ^ D/2,
+  // is read from qset, the chunk's G x D queries in memory or in LDS) with the append kernel's
+  // arithmetic, and, in split 0, store them to q_out.
+  __device__ __forceinline__ void fused_queries(const Chunk& ch, int pos, const __bf16* qset) {
+    if (col >= G) return;
+    if (a.cos != nullptr) {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int d0 = 32 * c + 8 * grp;
+        const size_t i0 = (size_t)pos * (D / 2) + (size_t)(d0 & (D / 2 - 1));
+        const float4* cp = reinterpret_cast<const float4*>(a.cos + i0);
+        const float4* sp = reinterpret_cast<const float4*>(a.sin + i0);
+        const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+        const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        Vec8<__bf16> other;
+        other.load_cached(qset + col * D + (d0 ^ (D / 2)));
+        float x[8], y[8], r[8];
+        qf[c].to_f32(x);
+        other.to_f32(y);
+        const bool low = d0 < D / 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p0 = x[e] * cs[e];
+          const float p1 = y[e] * sn[e];
+          r[e] = low ? p0 - p1 : p0 + p1;
+        }
+        qf[c].from_f32(r);
+      }
+    }
+    if (a.q_out != nullptr && ch.split == 0 && wave == 0) {
+      __bf16* qo = reinterpret_cast<__bf16*>(a.q_out) +
+                   ((size_t)ch.row * a.H_q + (size_t)ch.g * G + col) * D + 8 * grp;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qf[c].store(qo + 32 * c);
+    }
+  }
+
+  __device__ __forceinline__ void reset() {
+    mq = kNegInf;
+    thr = kNegInf;
+    ls = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NH; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __device__ __forceinline__ void load_block(Frag& f, const Chunk& ch, int ids, int blk) const {
+    if constexpr (PADDED) {
+      const size_t head_base = ((size_t)ch.row * a.H_kv + ch.g) * (size_t)a.seq_cap * D;
+      auto column = [&](int key) {
+        const int tv = ch.tok0 + blk * kBlock + key;
+        const int cc = tv < ch.gap_s ? tv : tv + ch.gap_shift;
+        return cc < a.kv_cols ? cc : a.kv_cols - 1;
+      };
+#pragma unroll
+      for (int c = 0; c < VC; ++c) {
+        const int e = lane * 8 + 512 * c;  // element of the [16][D] block: key e / D, dim e % D
+        const size_t off = head_base + (size_t)column(e / D) * D + e % D;
+        f.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kbase + off));
+        f.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vbase + off));
+      }
+    } else {
+      const int pb = this->clamp_id(__builtin_amdgcn_readlane(ids, blk));
+      const size_t boff = ((size_t)pb * a.H_kv + ch.g) * (size_t)(kBlock * D);
+      const char* kb = reinterpret_cast<const char*>(kbase + boff);
+      const char* vb = reinterpret_cast<const char*>(vbase + boff);
+      // a 32-bit lane offset on a wave-uniform base: the scalar-base form of the global load
+      unsigned lo = (unsigned)(lane * 16);
+      asm volatile("" : "+v"(lo));
+#pragma unroll
+      for (int c = 0; c < VC; ++c) {
+        f.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + lo + 1024 * c));
+        f.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + lo + 1024 * c));
+      }
+    }
+  }
+
+  // One block. MASK is for the chunk's partial last block: its slots past the chunk end may hold
+  // anything (NaN included) and never reach the sums.
+  template <bool MASK>
+  __device__ __forceinline__ void update(const Frag& f, const Chunk& ch, int blk) {
+    unsigned short* vst = smp->vst[wave];
+    unsigned short* kst = smp->kst[wave];
+    u32x4_t* vs = reinterpret_cast<u32x4_t*>(vst);
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {
+      const int e = lane * 8 + 512 * c;
+      *reinterpret_cast<u32x4_t*>(kst + (e / D) * kKRow + e % D) = f.k[c];
+      vs[lane + 64 * c] = f.v[c];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // K fragments (A operand): key col, dims 32c + 8 grp .. +7
+    u32x4_t kf[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      kf[c] = *reinterpret_cast<const u32x4_t*>(kst + col * kKRow + 32 * c + 8 * grp);
+    const int key0 = blk * kBlock + 4 * grp;
+    bool valid[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) valid[j] = !MASK || key0 + j < ch.ntok;
+    // V^T fragments (dims 16t + col, keys 4 grp .. +3), read now so the LDS latency hides behind
+    // the score product
+    const unsigned short* vtr = vst + (4 * grp + col / 4) * D + 4 * (col % 4);
+    s16x4_t vt[NH];
+#pragma unroll
+    for (int t = 0; t < NH; ++t) vt[t] = lds_read_tr16(vtr + 16 * t);
+    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[c]),
+                                                  __builtin_bit_cast(bf16x8_t, qf[c].w), s, 0, 0,
+                                                  0);
+    if (MASK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] = valid[j] ? s[j] : kNegInf;
+    }
+    const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__builtin_amdgcn_ballot_w64(lm > thr) != 0) {
+      float bm = fmaxf(lm, swap_rows16(lm));
+      bm = fmaxf(bm, swap_halves32(bm));
+      const float bms = bm * qk_scale;
+      if (bms > mq + kRescale) {
+        const float al = exp2_fast(mq - bms);
+        ls[0] *= al;  // the other elements hold zero
+#pragma unroll
+        for (int t = 0; t < NH; ++t) o[t] *= al;
+        mq = bms;
+        thr = (bms + kRescale) * inv_qk;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = exp2_fast(fmaf(s[j], qk_scale, -mq));
+      if (MASK) p[j] = valid[j] ? p[j] : 0.f;  // a head with only masked keys has mq = -inf
+    }
+    unsigned h01, h23, l01, l23;
+    split_bf16x2(p[0], p[1], h01, l01);
+    split_bf16x2(p[2], p[3], h23, l23);
+    const s16x4_t p_hi = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
+    const s16x4_t p_lo = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
+    const short one = col == 0 ? (short)0x3F80 : (short)0;  // bf16 1.0 in row 0 of the A operand
+    const s16x4_t ones = {one, one, one, one};
+    ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_hi, ls, 0, 0, 0);
+    ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_lo, ls, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NH; ++t) {
+      if (MASK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vt[t][j] = valid[j] ? vt[t][j] : (short)0;
+      }
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_hi, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_lo, o[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Worker::run_blocks' schedule (two fragments swapping roles, the partial last block masked)
+  // with this worker's loads and updates.
+  __device__ __forceinline__ void run_blocks(Frag& f0, Frag& f1, const Chunk& ch, int ids, int my) {
+    int i = 0;
+    for (; i + 2 < my; i += 2) {
+      load_block(f1, ch, ids, this->blk_of(i + 1));
+      update<false>(f0, ch, this->blk_of(i));
+      load_block(f0, ch, ids, this->blk_of(i + 2));
+      update<false>(f1, ch, this->blk_of(i + 1));
+    }
+    const bool tail = my > 0 && this->blk_of(my - 1) == ch.tail_blk;
+    if (i + 1 < my) {
+      load_block(f1, ch, ids, this->blk_of(i + 1));
+      update<false>(f0, ch, this->blk_of(i));
+      if (tail) update<true>(f1, ch, this->blk_of(i + 1));
+      else update<false>(f1, ch, this->blk_of(i + 1));
+    } else if (i < my) {
+      if (tail) update<true>(f0, ch, this->blk_of(i));
+      else update<false>(f0, ch, this->blk_of(i));
+    }
+  }
+
+  // Park the wave's per-head state in LDS for the combination across waves (then a barrier).
+  __device__ __forceinline__ void merge_to_smem(Smem& sm) {
+    if (col < G) {
+#pragma unroll
+      for (int t = 0; t < NH; ++t)
+        *reinterpret_cast<f32x4_t*>(&sm.acc[wave][col][16 * t + 4 * grp]) = o[t];
+      if (grp == 0) {
+        sm.m[wave][col] = mq;
+        sm.l[wave][col] = ls[0];
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// The worker of each element type: bf16 on the matrix cores (PA_DECODE_MFMA = 1), fp32 on the
+// vector ALUs.
+#ifndef PA_DECODE_MFMA
+#define PA_DECODE_MFMA 1
+#endif
+template <typename T, int D, int G, bool PADDED>
+struct DecodeWorker {
+  using type = Worker<T, D, G, PADDED>;
+};
+template <int D, int G, bool PADDED>
+struct DecodeWorker<__bf16, D, G, PADDED> {
+  using type = std::conditional_t<PA_DECODE_MFMA != 0, WorkerM<D, G, PADDED>,
+                                  Worker<__bf16, D, G, PADDED>>;
+};
+
 // Valid tokens of a row (and, padded, its gap start and width), lengths clamped to the bounds.
 template <bool PADDED>
 __device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_s, int* gap_shift) {
@@ -775,9 +1093,10 @@ constexpr int grid_min_wg() {
 template <typename T, int D, int G, bool PADDED, bool COMPACT>
 __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vector_kernel(
     const DecodeArgs a) {
-  using W = Worker<T, D, G, PADDED>;
+  using W = typename DecodeWorker<T, D, G, PADDED>::type;
   __shared__ typename W::Smem sm;
   W w(a);
+  w.bind(sm);
   const int chunk = chunk_tokens(D);
   int g, row, split;
   int n = 0, gap_s = 0, gap_shift = 0;
@@ -823,7 +1142,7 @@ __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vec
   }
   // issued before the row length is known, so their latency overlaps the length load
   int ids = w.load_ids(row, split * chunk);
-  w.load_q(w.q, row, g);
+  w.load_queries(row, g);
   // fused append: the row's position (a table row, clamped) for the rotations, and this lane's
   // piece of the new key and value
   const bool fused = a.k_new != nullptr;
@@ -999,7 +1318,7 @@ __device__ __forceinline__ Chunk decode_ticket(const RowSmem<PADDED>& rs, int B,
 template <typename T, int D, int G, bool PADDED>
 __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
     const DecodeArgs a) {
-  using W = Worker<T, D, G, PADDED>;
+  using W = typename DecodeWorker<T, D, G, PADDED>::type;
   constexpr int kQVec = G * D * (int)sizeof(T) / 16;  // 16-byte pieces of one (row, g) query set
   static_assert(kQVec <= 64 * kWaves, "query staging: at most one piece per thread");
   __shared__ typename W::Smem sm;
@@ -1007,6 +1326,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
   __shared__ int s_ids[2][64];
   __shared__ uint4 s_q[2][kQVec];
   W w(a);
+  w.bind(sm);
   const int B = a.batch;
   const int chunk = chunk_tokens(D);
   int* counter = a.counter;
@@ -1075,8 +1395,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_persistent_kernel(
     if (tid == 0 && has_nx) rs.ticket[(k + 2) % 3] = n_static + atomicAdd(counter, 1);
     const int ids = s_ids[slot][w.lane];
     const T* qs = reinterpret_cast<const T*>(s_q[slot]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) w.q[h].load_cached(qs + h * D + w.c * 8);
+    w.load_queries_from(qs);
     Chunk nx = cur;
     int pid = 0;
     uint4 pq = make_uint4(0, 0, 0, 0);
