@@ -649,8 +649,11 @@ struct Worker {
 //   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   v_mfma_f32_16x16x16_bf16, D/16 tiles
 //     P^T is the first product's result in place; V^T comes from the block staged in the wave's LDS
 //     area and read back transposed (ds_read_b64_tr_b16). P enters as two bf16 parts, hi + lo
-//     (within 2^-18 of each fp32 weight), and the weight sums come from the same products (a
+//     (within 2^-16 of each fp32 weight), and the weight sums come from the same products (a
 //     constant A operand whose row 0 is ones): numerator and denominator see the same weights.
+// K is loaded as whole 1 KB runs like V (as the products' operand layout it would be half lines of
+// 64 bytes, each read by two instructions: 8% slower on the B=128 step) and rearranged through the
+// wave's padded K area in LDS.
 // A lane keeps its head's outputs for dims 16t + 4(l/16) .. +3, so no lane merge is needed.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -42,13 +42,24 @@ K_FIXED = 84
 K_ACC_MIN = 128
 # log2 of the largest chunk: a chunk's log-sum-exp exceeds its largest score by at most this
 LOG2_CHUNK = 10.0
+# The bf16 paths run on the matrix cores (the decode worker and the multi-query kernel):
+# - a score adds D exact bf16 products into an fp32 accumulator; at worst every addition is rounded
+#   in sequence, so D roundings take the place of K_DOT;
+# - a weight p enters the products as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi): bf16 keeps
+#   8 significant bits, so |p - hi| <= 2^-8 |p| and |p - (hi + lo)| <= 2^-8 |p - hi| <= 2^-16 |p|
+#   (weights so small that lo underflows are below 2^-118 and change the sums by less than that);
+SPLIT_REL = 2.0 ** -16
+# - each 16-key block adds its 16 weighted terms into a wave's accumulators, at worst one rounding
+#   per term, so a wave's chain is the tokens it reads of one chunk (chunk / 4 waves); then the
+#   cross-wave combination (4), the division (1), the split merge (40) and the normalisation (2).
+K_FIXED_MFMA = 47
 
 
 def _gamma(k):
     return k * U32 / (1.0 - k * U32)
 
 
-def attention_bound(q, K, V, scale):
+def attention_bound(q, K, V, scale, mfma=False, wave_tokens=256):
     """Per-element bounds of |out_gpu - out_exact| and |lse_gpu - lse_exact| for one row.
 
     q (n_q, H_q, D), K, V (n, H_kv, D) fp64 (the stored values exactly); scale the fp32 value.
@@ -57,8 +68,12 @@ def attention_bound(q, K, V, scale):
         eps_w = scale gamma(K_DOT) max_j a_j                (the dot product)
               + u (ln 2 (8 X + 4 LOG2_CHUNK + 12) + 2)     (scale product, fused exponent,
                                                              split lse roundings, the exp2 itself)
+        on the matrix cores (mfma) with D roundings in place of K_DOT and + SPLIT_REL (the
+        weight's hi + lo bf16 parts);
       * every sum of weights and weight * value terms carries a relative error of at most
-        gamma(K_ACC) of the sum of its terms' magnitudes, K_ACC = max(128, 84 + X / 4 + 1);
+        gamma(K_ACC) of the sum of its terms' magnitudes, K_ACC = max(128, 84 + X / 4 + 1), on the
+        matrix cores K_ACC = wave_tokens + 47 + X / 4 + 1 (wave_tokens: the tokens one wave
+        accumulates, a quarter of a split chunk);
     so, with A_d = sum_j w_j |v_jd| / sum_j w_j (exact weights),
       |d out_d| <= 1.001 (2 eps_w + 2 gamma(K_ACC)) A_d + 3 u |out_d|
       |d lse|   <= 1.001 (eps_w + gamma(K_ACC)) + 8 u (|lse| + 1).
@@ -75,9 +90,15 @@ def attention_bound(q, K, V, scale):
         x = scale * (q[:, h, :] @ K[:, g, :].T)              # (n_q, n)
         a = np.abs(q[:, h, :]) @ np.abs(K[:, g, :]).T
         X = np.abs(x).max(axis=1) * LOG2E
-        g_acc = _gamma(np.maximum(K_ACC_MIN, K_FIXED + np.ceil(X / 4.0) + 1.0))
-        eps_w = (scale * _gamma(K_DOT) * a.max(axis=1)
-                 + U32 * (math.log(2.0) * (8.0 * X + 4.0 * LOG2_CHUNK + 12.0) + 2.0))
+        if mfma:
+            g_acc = _gamma(wave_tokens + K_FIXED_MFMA + np.ceil(X / 4.0) + 1.0)
+            eps_w = (scale * _gamma(D) * a.max(axis=1)
+                     + U32 * (math.log(2.0) * (8.0 * X + 4.0 * LOG2_CHUNK + 12.0) + 2.0)
+                     + SPLIT_REL)
+        else:
+            g_acc = _gamma(np.maximum(K_ACC_MIN, K_FIXED + np.ceil(X / 4.0) + 1.0))
+            eps_w = (scale * _gamma(K_DOT) * a.max(axis=1)
+                     + U32 * (math.log(2.0) * (8.0 * X + 4.0 * LOG2_CHUNK + 12.0) + 2.0))
         m = x.max(axis=1, keepdims=True)
         w = np.exp(x - m)
         L = w.sum(axis=1)
@@ -139,6 +160,11 @@ def check_rows(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale,
     Returns the record (max, mean, and the largest error / derived bound ratio)."""
     rows = range(len(kv_lens)) if rows is None else rows
     d_out, d_lse, ratio = [], [], 0.0
+    # bf16 rows are decoded on the matrix cores, fp32 rows on the vector ALUs; a wave accumulates a
+    # quarter of a split chunk (1024 tokens up to D = 64, 512 at D = 128)
+    D = q.shape[-1]
+    mfma = dtype == "bf16"
+    wave_tokens = (1024 if D <= 64 else 512) // 4
     for b in rows:
         if gather is not None:
             K, V = gather(b)
@@ -148,7 +174,7 @@ def check_rows(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale,
         if qb.ndim == 2:
             qb = qb[None]
         o_ref, l_ref = O.attend_two_pass(qb, K, V, scale)
-        bo, bl = attention_bound(qb, K, V, scale)
+        bo, bl = attention_bound(qb, K, V, scale, mfma=mfma, wave_tokens=wave_tokens)
         go = np.asarray(out[b], dtype=np.float64).reshape(o_ref.shape)
         gl = np.asarray(lse[b], dtype=np.float64).reshape(l_ref.shape)
         do, dl = _abs_diff(go, o_ref), _abs_diff(gl, l_ref)
