@@ -1603,6 +1603,42 @@ int resident_workgroups(const void* kernel, size_t lds) {
   return per_cu * cus;
 }
 
+// Workgroups of the bf16 split grid per CU. The matrix-core worker's registers would allow 4, and 4
+// streaming workgroups per CU measured 1.3% slower than 3 on the B=128 step (more concurrent
+// streams for the same bytes): the launch reserves enough unused LDS to hold residency at this.
+#ifndef PA_DECODE_GRID_WG_PER_CU
+#define PA_DECODE_GRID_WG_PER_CU 3
+#endif
+
+// Dynamic LDS that holds `kernel` to at most `per_cu` resident workgroups per CU (0: none needed),
+// cached per (device, kernel).
+size_t lds_reservation(const void* kernel, int per_cu) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> cache;
+  int dev = 0;
+  if (per_cu <= 0 || hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_pair(dev, kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  hipFuncAttributes attr;
+  int lds_cu = 0, lds_block = 0;
+  size_t pad = 0;
+  if (hipFuncGetAttributes(&attr, kernel) == hipSuccess &&
+      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+          hipSuccess &&
+      hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+          hipSuccess &&
+      lds_cu > 0) {
+    const size_t want = (size_t)lds_cu / (size_t)(per_cu + 1) + 1;  // per_cu + 1 no longer fit
+    const size_t own = attr.sharedSizeBytes;
+    if (want > own && want <= (size_t)lds_block) pad = (want - own + 255) & ~(size_t)255;
+    if (own + pad > (size_t)lds_block) pad = 0;
+  }
+  cache[key] = pad;
+  return pad;
+}
+
 // Whether launch_decode_vector takes the persistent kernel for these arguments.
 bool decode_vector_is_persistent(const DecodeArgs& a) {
   if (!(PA_DECODE_PERSISTENT && a.counter != nullptr && a.s_max > 1 && a.batch <= kMaxRows))
@@ -1648,8 +1684,11 @@ hipError_t launch_layout(const DecodeArgs& args, hipStream_t stream, bool* merge
     *merged = true;
   }
   dim3 grid(a.H_kv, a.batch, a.s_max);
-  hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED, false>), grid, dim3(64 * kWaves), 0,
-                     stream, a);
+  auto kern = decode_vector_kernel<T, D, G, PADDED, false>;
+  const size_t pad =
+      sizeof(T) == 2 ? lds_reservation(reinterpret_cast<const void*>(kern), PA_DECODE_GRID_WG_PER_CU)
+                     : 0;
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), pad, stream, a);
   return hipGetLastError();
 }
 
