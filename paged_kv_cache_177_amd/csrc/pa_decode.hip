@@ -893,6 +893,36 @@ struct WorkerM : Worker<__bf16, D, G, PADDED> {
     __builtin_amdgcn_wave_barrier();
   }
 
+  // A ring of three fragments (two blocks in flight while one is computed), for grids that the
+  // device holds at once: a wave then has its SIMD nearly to itself, and with the products on the
+  // matrix cores it waits on its loads. Block b sits in the fragment b mod 3; every load in the loop
+  // is unconditional (past the wave's last block it re-reads that block), and the chunk's partial
+  // last block is updated masked after the loop. The updates run in run_blocks' order: the same
+  // bits.
+  __device__ __forceinline__ void run_blocks3(Frag& f0, Frag& f1, const Chunk& ch, int ids, int my) {
+    Frag f2;
+    if (my <= 0) return;
+    const int last = my - 1;
+    auto clamp = [&](int b) { return this->blk_of(b < last ? b : last); };
+    load_block(f1, ch, ids, clamp(1));
+    const bool tail = this->blk_of(last) == ch.tail_blk;
+    const int steady = tail ? last : my;  // blocks that take the unmasked update
+    for (int i = 0; i < steady; i += 3) {
+      load_block(f2, ch, ids, clamp(i + 2));
+      update<false>(f0, ch, this->blk_of(i));
+      load_block(f0, ch, ids, clamp(i + 3));
+      if (i + 1 < steady) update<false>(f1, ch, this->blk_of(i + 1));
+      load_block(f1, ch, ids, clamp(i + 4));
+      if (i + 2 < steady) update<false>(f2, ch, this->blk_of(i + 2));
+    }
+    if (tail) {
+      const int slot = last % 3;
+      if (slot == 0) update<true>(f0, ch, this->blk_of(last));
+      else if (slot == 1) update<true>(f1, ch, this->blk_of(last));
+      else update<true>(f2, ch, this->blk_of(last));
+    }
+  }
+
   // Worker::run_blocks' schedule (two fragments swapping roles, the partial last block masked)
   // with this worker's loads and updates.
   __device__ __forceinline__ void run_blocks(Frag& f0, Frag& f1, const Chunk& ch, int ids, int my) {
@@ -1093,7 +1123,9 @@ constexpr int grid_min_wg() {
   return sizeof(T) == 2 && G <= 4 && PA_DECODE_MIN_WG_PER_CU > 0 ? PA_DECODE_MIN_WG_PER_CU : 1;
 }
 
-template <typename T, int D, int G, bool PADDED, bool COMPACT>
+// RING = 3: the bf16 worker's three-fragment ring (run_blocks3), for split grids the device holds
+// at once.
+template <typename T, int D, int G, bool PADDED, bool COMPACT, int RING = 2>
 __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vector_kernel(
     const DecodeArgs a) {
   using W = typename DecodeWorker<T, D, G, PADDED>::type;
@@ -1172,7 +1204,8 @@ __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vec
   if (fused)  // while the first block is in flight
     w.fused_queries(ch, pos, reinterpret_cast<const T*>(a.q) + (size_t)row * a.q_row_stride +
                                  (size_t)g * G * D);
-  w.run_blocks(f0, f1, ch, ids, my);
+  if constexpr (RING == 3) w.run_blocks3(f0, f1, ch, ids, my);
+  else w.run_blocks(f0, f1, ch, ids, my);
   w.merge_to_smem(sm);
   w.write_result(sm, ch);
   if constexpr (!COMPACT) {
@@ -1684,12 +1717,26 @@ hipError_t launch_layout(const DecodeArgs& args, hipStream_t stream, bool* merge
     *merged = true;
   }
   dim3 grid(a.H_kv, a.batch, a.s_max);
-  auto kern = decode_vector_kernel<T, D, G, PADDED, false>;
-  const size_t pad =
-      sizeof(T) == 2 ? lds_reservation(reinterpret_cast<const void*>(kern), PA_DECODE_GRID_WG_PER_CU)
-                     : 0;
-  hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), pad, stream, a);
-  return hipGetLastError();
+  if constexpr (sizeof(T) == 2 && PA_DECODE_MFMA != 0) {
+    auto kern = decode_vector_kernel<T, D, G, PADDED, false>;
+    const size_t pad =
+        lds_reservation(reinterpret_cast<const void*>(kern), PA_DECODE_GRID_WG_PER_CU);
+    // a grid the device holds at once (the lockstep batches) keeps two blocks in flight per wave
+    auto ring = decode_vector_kernel<T, D, G, PADDED, false, 3>;
+    const size_t ring_pad =
+        lds_reservation(reinterpret_cast<const void*>(ring), PA_DECODE_GRID_WG_PER_CU);
+    const int resident = resident_workgroups(reinterpret_cast<const void*>(ring), ring_pad);
+    if (resident > 0 && items <= resident) {
+      hipLaunchKernelGGL(ring, grid, dim3(64 * kWaves), ring_pad, stream, a);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), pad, stream, a);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((decode_vector_kernel<T, D, G, PADDED, false>), grid, dim3(64 * kWaves),
+                       0, stream, a);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, int D, int G>
