@@ -15,9 +15,11 @@ constexpr int kMaxGridYZ = 65535;  // largest grid extent in y and z (rows, spli
 // A row of n keys is cut into ceil(n / chunk) chunks of `chunk` tokens (the last one shorter);
 // chunk depends only on head_dim, so a row's split -- and with it the exact order of its fp32
 // reductions -- depends on that row's own length alone. chunk is a multiple of 16 and at most
-// 64 blocks, so one wave holds a chunk's block ids in one register.
+// 64 blocks, so one wave holds a chunk's block ids in one register. Both head sizes take the
+// largest, 1024 tokens (at D = 128 512-token chunks made the long-context call 4.3% slower once
+// the blocks' products moved to the matrix cores).
 #ifndef PA_CHUNK_D128
-#define PA_CHUNK_D128 512
+#define PA_CHUNK_D128 1024
 #endif
 #ifndef PA_CHUNK_D64
 #define PA_CHUNK_D64 1024

@@ -161,10 +161,9 @@ def check_rows(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale,
     rows = range(len(kv_lens)) if rows is None else rows
     d_out, d_lse, ratio = [], [], 0.0
     # bf16 rows are decoded on the matrix cores, fp32 rows on the vector ALUs; a wave accumulates a
-    # quarter of a split chunk (1024 tokens up to D = 64, 512 at D = 128)
-    D = q.shape[-1]
+    # quarter of a split chunk (1024 tokens)
     mfma = dtype == "bf16"
-    wave_tokens = (1024 if D <= 64 else 512) // 4
+    wave_tokens = 1024 // 4
     for b in rows:
         if gather is not None:
             K, V = gather(b)

@@ -124,9 +124,9 @@ def test_decode_workspace_query():
     o = (rows * 64 * 4 + 255) // 256 * 256
     counts = (128 * 32 * 4 + 255) // 256 * 256
     assert need == 256 + o + (rows * 4 + 255) // 256 * 256 + counts
-    # head_dim 128 uses 512-token chunks
+    # head_dim 128 uses the same 1024-token chunks: max_kv_len 2048 -> 2 splits
     p = _fake_pool(head_dim=128)
-    need = B.pa_decode_attention(p, FAKE, 32 * 128, 1, 32, FAKE, 64, FAKE, 4, 1024, 0.1,
+    need = B.pa_decode_attention(p, FAKE, 32 * 128, 1, 32, FAKE, 128, FAKE, 4, 2048, 0.1,
                                  out=FAKE, query_workspace=True)
     rows = 4 * 32 * 2
     assert need == (256 + (4 * 32 * 4 + 255) // 256 * 256 + (rows * 128 * 4 + 255) // 256 * 256

@@ -74,7 +74,7 @@ def test_fused_long_rows_persistent_kernel(D, dtype):
     """Rows of up to 70 chunks: the decode runs its persistent kernel, whose chunk loop stores each
     row's new token (rotated) where its chunk is taken up; short rows in the same batch put the
     token in a wave's first block, which that wave then does not prefetch."""
-    chunk = 1024 if D <= 64 else 512
+    chunk = 1024
     n = [5, 70, 20 * chunk + 7, 70 * chunk - 9, 3 * chunk + 40]
     case = W.make_paged_case(f"fused-long-D{D}-{dtype}", 43 + D, n, 8, 2, D, dtype,
                              rope_theta=1e4)

@@ -152,7 +152,7 @@ def test_split_merge_wave_counts(D):
     1, 4 and 8 waves. Every row matches the oracle, and a row decoded on its own gives the same
     bits as in the batch, although the launches differ: the batch (70 splits) runs the persistent
     kernel with an 8-wave merge, the two short rows alone run the split grid with a 1-wave one."""
-    chunk = 1024 if D <= 64 else 512
+    chunk = 1024
     n = [700, 3 * chunk, 18 * chunk + 5, 70 * chunk - 3]
     case = W.make_paged_case(f"merge-waves-D{D}", 61 + D, [x - 1 for x in n], 8, 2, D, "bf16")
     r, _, _ = run_and_check_paged(case)
@@ -202,7 +202,7 @@ def test_wide_batch_with_long_rows_runs_the_persistent_kernel(D):
     of at most 64 such rows takes the compact grid). The oracle checks sampled rows, and a row
     decoded on its own (the compact grid, or the split grid for a short row) gives the same bits.
     Every row is compared with the oracle."""
-    chunk = 1024 if D <= 64 else 512
+    chunk = 1024
     rng = np.random.default_rng(70 + D)
     n = np.concatenate([[20 * chunk + 3, 17 * chunk], rng.integers(0, 400, 68)])
     case = W.make_paged_case(f"wide-long-D{D}", 71 + D, n, 8, 2, D, "bf16")
@@ -284,7 +284,7 @@ def long_case():
 
 
 def test_long_context_all_heads(long_case):
-    """Four rows of 41k-113k tokens, D=128: every row splits into 81-220 chunks. All 32 query
+    """Four rows of 41k-113k tokens, D=128: every row splits into 41-110 chunks. All 32 query
     heads of every row against the oracle, both under the acceptance tolerance and under the
     bound derived from the kernels' fp32 arithmetic (the tolerance alone would not see a lost or
     doubled block at these lengths); the whole pool bit for bit."""

@@ -28,7 +28,7 @@ def _case(kind):
         n = rng.integers(0, 9000, 96)
         n[:3] = [0, 1023, 8999]
         return W.make_paged_case("noalloc-large", 311, n, 32, 8, 64, "bf16", rope_theta=1e4)
-    if kind == "small":    # 5 rows, D = 128, up to 40 splits: compact grid + lse_reduce_kernel
+    if kind == "small":    # 5 rows, D = 128, up to 20 splits: compact grid + lse_reduce_kernel
         return W.make_paged_case("noalloc-small", 312, [20000, 3, 511, 512, 7000], 16, 4, 128,
                                  "bf16")
     n = rng.integers(0, 5000, 120)  # 120 rows: more rows than the first call
