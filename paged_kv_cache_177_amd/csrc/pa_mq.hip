@@ -13,11 +13,12 @@
 //       K is the A operand straight from the block (lane: key l%16, 8 dims), Q^T the B operand
 //       (lane: query l%16, 8 dims); the result puts query l%16 in lane l, keys 4(l/16)..+3.
 //   online softmax per query: lane-local, plus two cross-lane steps for the block maximum;
-//   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   v_mfma_f32_16x16x16_bf16, D/16 steps
-//       P^T is the B operand exactly as the first product left it (query l%16, keys 4(l/16)..);
-//       V^T (lane: dim l%16, keys 4(l/16)..) comes from the block staged in LDS with one
-//       ds_read_b64_tr_b16 per 16 dims (the gfx950 transposing LDS read).
-//       P is split into bf16 hi + lo parts (two products), so the weights keep ~16 bits.
+//   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   v_mfma_f32_16x16x32_bf16, D/16 steps
+//       P is split into bf16 hi + lo parts, so the weights keep ~16 bits, and both parts go
+//       through one K = 32 product: each lane's B operand is its 4 hi weights then its 4 lo
+//       weights, in the lanes where the first product left them (query l%16, keys 4(l/16)..);
+//       the A operand holds V^T (lane: dim l%16, keys 4(l/16)..) twice over, read from the block
+//       staged in LDS by two ds_read_b64_tr_b16 per 16 dims (the gfx950 transposing LDS read).
 // Query rows therefore sit in the same lanes in S^T and O^T: rescales and the final division are
 // lane-local.
 #include <type_traits>
@@ -51,11 +52,27 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Two fp32 weights -> their bf16 hi parts (RNE, one packed conversion) and the bf16 of what the
-// hi parts leave over: p ~ hi + lo to ~16 bits.
-__device__ __forceinline__ void split_bf16x2(float p0, float p1, unsigned& hi, unsigned& lo) {
+// hi parts leave over: p ~ hi + lo to ~16 bits. The remainders p - hi come exactly (both terms are
+// within one bf16 step of each other, so the difference is an fp32 number) from the bf16 dot
+// product of the hi pair with (-1, 0), resp. (0, -1), accumulated onto p: one instruction each.
+// neg0 and neg1 are those two pairs, passed in scalar registers: written as a constant, the first
+// pair is encoded as the inline constant -1.0, which this instruction reads as the fp32 -1.0, i.e.
+// the pair (0, -1).
+__device__ __forceinline__ void split_bf16x2(float p0, float p1, unsigned neg0, unsigned neg1,
+                                             unsigned& hi, unsigned& lo) {
   hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t));
-  const f32x2_t h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{p0, p1} - h, bf16x2_t));
+  const bf16x2_t h = __builtin_bit_cast(bf16x2_t, hi);
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, neg0), p0, false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, neg1), p1, false);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2_t));
+}
+
+// A raw-buffer resource for one K or V block: the block's base address in scalar registers, so a
+// load adds only the lane's 32-bit offset (the loop-invariant vector offsets need no copies or
+// 64-bit address arithmetic per block). Word 3 is the gfx9-family raw-buffer format word; the
+// range is wider than any offset used (offsets stay inside the block).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
 }
 
 // ds_read_b64_tr_b16: within each 16-lane quarter-wave, lanes 4j .. 4j + 3 name (with 8-byte
@@ -87,20 +104,21 @@ struct MqSmem {
 template <int D, bool SPARSE>
 constexpr int mq_qt() { return (D == 32 && !SPARSE) ? 2 : 1; }
 
-// K/V block fragments per wave (RING - 1 blocks in flight while one is computed): the dense D = 32
-// kernel (the latent cross-attention shape, whose 4 waves per SIMD allow up to 128 registers)
-// takes PA_MQ_RING_D32; the block-sparse one is held to 72 registers and the wider ones would lose
-// occupancy, so they keep three
+// K/V block fragments per wave (RING - 1 blocks in flight while one is computed): three for the
+// dense kernels (the D = 32 one, the latent cross-attention shape, may take PA_MQ_RING_D32; its 4
+// waves per SIMD allow up to 128 registers). The block-sparse D = 32 kernel keeps two: it computes
+// only the kept blocks (about a tenth on the latent workload), and two fragments hold it to 64
+// registers, so its launch of 8 waves per SIMD is resident at once (three need 71: 7 waves).
 #ifndef PA_MQ_RING_D32
 #define PA_MQ_RING_D32 3
 #endif
 template <int D, bool SPARSE>
-constexpr int mq_ring() { return (D == 32 && !SPARSE) ? PA_MQ_RING_D32 : 3; }
+constexpr int mq_ring() { return D != 32 ? 3 : (SPARSE ? 2 : PA_MQ_RING_D32); }
 
 template <int D, bool SPARSE>
-// D = 32 (the latent cross-attention shape) keeps several waves per SIMD: 7 with one sub-tile (72
-// registers), 4 with two (128); nearly a whole launch of that workload is then resident at once.
-__attribute__((amdgpu_waves_per_eu(D == 32 ? (mq_qt<D, SPARSE>() == 2 ? 4 : 7) : 1)))
+// D = 32 (the latent cross-attention shape) keeps several waves per SIMD: 8 with one sub-tile (64
+// registers), 4 with two (128); a whole launch of that workload is then resident at once.
+__attribute__((amdgpu_waves_per_eu(D == 32 ? (mq_qt<D, SPARSE>() == 2 ? 4 : 8) : 1)))
 __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const DecodeArgs a) {
   constexpr int KC = D / 32;  // k-steps of the score product
   constexpr int NH = D / 16;  // dim tiles of the output product
@@ -189,8 +207,18 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
   }
   const short one = col == 0 ? (short)0x3F80 : (short)0;  // bf16 1.0 in row 0 of the A operand
   const s16x4_t ones = {one, one, one, one};
+  const bf16x8_t ones8 =
+      __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ones, ones, 0, 1, 2, 3, 0, 1, 2, 3));
+  // (-1, 0) and (0, -1) as bf16 pairs in scalar registers (see split_bf16x2)
+  unsigned neg0 = 0x0000BF80u, neg1 = 0xBF800000u;
+  asm("" : "+s"(neg0), "+s"(neg1));
   // this lane's address for the transposed V^T reads: key 4 grp + col / 4, dims 4 (col % 4) ..
   const unsigned short* vtr = sm.v[wave] + (4 * grp + col / 4) * D + 4 * (col % 4);
+  // the same address again, which the compiler cannot prove equal: the second transposed read fills
+  // the other half of the A operand (a register copy of the first read would cost 2 VALU per tile)
+  int vtr_zero = 0;
+  asm("" : "+v"(vtr_zero));
+  const unsigned short* vtr2 = vtr + vtr_zero;
 
   // K fragment (A operand): key col of the block, dims 32c + 8 grp; V: 16 contiguous bytes per lane
   // at lane * 8 elements (its transpose is read back from LDS)
@@ -198,25 +226,20 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     u32x4_t k[KC];
     u32x4_t v[D / 32];
   };
-  // issue the loads of one block (physical id pb, already clamped into the pool): a wave-uniform
-  // block base plus 32-bit lane byte offsets, the scalar-base form of the global load (no 64-bit
-  // address arithmetic per lane and block)
-  const unsigned k_off0 = (unsigned)((col * D + 8 * grp) * 2);
-  const unsigned v_off0 = (unsigned)(lane * 16);
+  // issue the loads of one block (physical id pb, already clamped into the pool): buffer loads off a
+  // per-block scalar resource with the lanes' fixed 32-bit byte offsets
+  const int k_off0 = (col * D + 8 * grp) * 2;
+  const int v_off0 = lane * 16;
   auto load = [&](Frag& f, int pb) {
     const size_t base = ((size_t)pb * a.H_kv + g) * (size_t)(kBlock * D);
-    const char* kb = reinterpret_cast<const char*>(kbase + base);
-    const char* vb = reinterpret_cast<const char*>(vbase + base);
-    // the offsets pass through an empty asm at every load, so the compiler cannot hoist a 64-bit
-    // widening out of the loop and add the block base in vector registers for every load
-    unsigned k_off = k_off0, v_off = v_off0;
-    asm volatile("" : "+v"(k_off), "+v"(v_off));
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + base);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + base);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      f.k[c] = *reinterpret_cast<const u32x4_t*>(kb + k_off + 64 * c);
+      f.k[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off0, 64 * c, 0));
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      f.v[c] = *reinterpret_cast<const u32x4_t*>(vb + v_off + 1024 * c);
+      f.v[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off0, 1024 * c, 0));
   };
   // One block: scores, online-softmax update, output product. MASK (the row's partial last block
   // only) drops the keys at or past n: their slots may hold anything, NaN included.
@@ -234,9 +257,12 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
     for (int j = 0; j < 4; ++j) valid[j] = !MASK || key0 + j < n;
     // V^T fragments (dim 16t + col, keys 4 grp .. +3; masked keys read as zero), shared by the
     // sub-tiles; read now so that the LDS latency hides behind the score products
-    s16x4_t vt[NH];
+    s16x4_t vt[NH], vt2[NH];
 #pragma unroll
-    for (int t = 0; t < NH; ++t) vt[t] = lds_read_tr16(vtr + 16 * t);
+    for (int t = 0; t < NH; ++t) {
+      vt[t] = lds_read_tr16(vtr + 16 * t);
+      vt2[t] = lds_read_tr16(vtr2 + 16 * t);
+    }
     // The sub-tiles' chains run side by side (their products, maxima, exponentials and
     // conversions interleave), with one branch for the rare raise of a running max.
     f32x4_t s[QT];
@@ -290,27 +316,33 @@ __global__ __launch_bounds__(64 * kWaves) void mq_paged_mfma_kernel(const Decode
         if (MASK) p[j] = valid[j] ? p[j] : 0.f;  // a zero scale would make -inf * 0 a NaN
       }
       unsigned h01, h23, l01, l23;
-      split_bf16x2(p[0], p[1], h01, l01);
-      split_bf16x2(p[2], p[3], h23, l23);
+      split_bf16x2(p[0], p[1], neg0, neg1, h01, l01);
+      split_bf16x2(p[2], p[3], neg0, neg1, h23, l23);
       p_hi[u] = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
       p_lo[u] = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
     }
+    // k 0..3 of a lane's group carry the hi weights, k 4..7 the lo weights of the same keys
+    bf16x8_t pb[QT];
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_hi[u], ls[u], 0, 0, 0);
-      ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_lo[u], ls[u], 0, 0, 0);
+      pb[u] = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_shufflevector(p_hi[u], p_lo[u], 0, 1, 2, 3, 4, 5, 6, 7));
+      ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pb[u], ls[u], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < NH; ++t) {
       if (MASK) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vt[t][j] = valid[j] ? vt[t][j] : (short)0;
+        for (int j = 0; j < 4; ++j) {
+          vt[t][j] = valid[j] ? vt[t][j] : (short)0;
+          vt2[t][j] = valid[j] ? vt2[t][j] : (short)0;
+        }
       }
+      const bf16x8_t va =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vt[t], vt2[t], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int u = 0; u < QT; ++u) {
-        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_hi[u], o[u][t], 0, 0, 0);
-        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_lo[u], o[u][t], 0, 0, 0);
-      }
+      for (int u = 0; u < QT; ++u)
+        o[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[u], o[u][t], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   };
