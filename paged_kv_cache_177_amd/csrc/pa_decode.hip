@@ -646,11 +646,15 @@ struct Worker {
 //   online softmax per head, its running max shared by its four lanes (l%16 + 16k): raised to the
 //     block maximum only when some lane's scores beat it by more than kRescale (a wave ballot
 //     against a threshold kept in raw score units), so most blocks take no cross-lane step;
-//   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   v_mfma_f32_16x16x16_bf16, D/16 tiles
+//   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]   D/16 tiles
 //     P^T is the first product's result in place; V^T comes from the block staged in the wave's LDS
 //     area and read back transposed (ds_read_b64_tr_b16). P enters as two bf16 parts, hi + lo
 //     (within 2^-16 of each fp32 weight), and the weight sums come from the same products (a
 //     constant A operand whose row 0 is ones): numerator and denominator see the same weights.
+//     D <= 64: one v_mfma_f32_16x16x32_bf16 per tile takes both parts (B operand: a lane's 4 hi
+//     weights, then its 4 lo weights; A operand: its V^T fragment twice over, from a second
+//     transposed read). D = 128: two v_mfma_f32_16x16x16_bf16 per tile (hi, then lo), since the
+//     second copy of the 8 tiles' fragments would not fit in 3 waves' registers per SIMD.
 // K is loaded as whole 1 KB runs like V (as the products' operand layout it would be half lines of
 // 64 bytes, each read by two instructions: 8% slower on the B=128 step) and rearranged through the
 // wave's padded K area in LDS.
@@ -691,6 +695,9 @@ struct WorkerM : Worker<__bf16, D, G, PADDED> {
   static constexpr int KC = D / 32;  // 32-dim steps of the score product
   static constexpr int NH = D / 16;  // 16-dim tiles of the output product
   static constexpr int VC = D / 32;  // 16-byte pieces per lane of a block's V (32 D bytes)
+  // the output product as one K = 32 product per tile taking both weight parts (D <= 64), or as
+  // two K = 16 products (D = 128, where the doubled V^T operand would not fit the register cap)
+  static constexpr bool kK32 = D <= 64;
   static_assert(G <= 16, "a group's heads fill at most one 16-column tile");
   // a block's K and V as loaded: lane l holds elements 8l + 512c .. +7 of each [16][D] array
   // (whole 1 KB runs per load instruction), rearranged through LDS for the products
@@ -842,6 +849,15 @@ struct WorkerM : Worker<__bf16, D, G, PADDED> {
     s16x4_t vt[NH];
 #pragma unroll
     for (int t = 0; t < NH; ++t) vt[t] = lds_read_tr16(vtr + 16 * t);
+    // D <= 64: the same fragments again, for the other half of the K = 32 product's A operand (the
+    // address passes through an empty asm, so the compiler emits a second read, not register copies)
+    s16x4_t vt2[NH];
+    if constexpr (kK32) {
+      int vz = 0;
+      asm("" : "+v"(vz));
+#pragma unroll
+      for (int t = 0; t < NH; ++t) vt2[t] = lds_read_tr16(vtr + vz + 16 * t);
+    }
     f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c)
@@ -879,16 +895,38 @@ struct WorkerM : Worker<__bf16, D, G, PADDED> {
     const s16x4_t p_lo = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
     const short one = col == 0 ? (short)0x3F80 : (short)0;  // bf16 1.0 in row 0 of the A operand
     const s16x4_t ones = {one, one, one, one};
-    ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_hi, ls, 0, 0, 0);
-    ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_lo, ls, 0, 0, 0);
+    if constexpr (kK32) {
+      // k 0..3 of a lane's group carry the hi weights, k 4..7 the lo weights of the same keys
+      const bf16x8_t pb =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(p_hi, p_lo, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8_t ones8 =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ones, ones, 0, 1, 2, 3, 0, 1, 2, 3));
+      ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pb, ls, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < NH; ++t) {
-      if (MASK) {
+      for (int t = 0; t < NH; ++t) {
+        if (MASK) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vt[t][j] = valid[j] ? vt[t][j] : (short)0;
+          for (int j = 0; j < 4; ++j) {
+            vt[t][j] = valid[j] ? vt[t][j] : (short)0;
+            vt2[t][j] = valid[j] ? vt2[t][j] : (short)0;
+          }
+        }
+        const bf16x8_t va = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(vt[t], vt2[t], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[t], 0, 0, 0);
       }
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_hi, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_lo, o[t], 0, 0, 0);
+    } else {
+      ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_hi, ls, 0, 0, 0);
+      ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, p_lo, ls, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NH; ++t) {
+        if (MASK) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vt[t][j] = valid[j] ? vt[t][j] : (short)0;
+        }
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_hi, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], p_lo, o[t], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -1721,8 +1759,10 @@ hipError_t launch_layout(const DecodeArgs& args, hipStream_t stream, bool* merge
     auto kern = decode_vector_kernel<T, D, G, PADDED, false>;
     const size_t pad =
         lds_reservation(reinterpret_cast<const void*>(kern), PA_DECODE_GRID_WG_PER_CU);
-    // a grid the device holds at once (the lockstep batches) keeps two blocks in flight per wave
-    auto ring = decode_vector_kernel<T, D, G, PADDED, false, 3>;
+    // a grid the device holds at once (the lockstep batches) keeps two blocks in flight per wave;
+    // not at D = 128, where the third fragment would spill under the 3-waves-per-SIMD register cap
+    // (a 16-row batch took 40.6 us spilled against 18.9 us with the two-fragment loop)
+    auto ring = decode_vector_kernel<T, D, G, PADDED, false, D <= 64 ? 3 : 2>;
     const size_t ring_pad =
         lds_reservation(reinterpret_cast<const void*>(ring), PA_DECODE_GRID_WG_PER_CU);
     const int resident = resident_workgroups(reinterpret_cast<const void*>(ring), ring_pad);

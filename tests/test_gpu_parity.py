@@ -100,11 +100,12 @@ def test_block_placement_and_batch_composition_are_bit_invisible():
 @pytest.mark.parametrize("D", [64, 128])
 def test_resident_grid_ring_gives_the_two_fragment_bits(D):
     """A bf16 split grid that the device holds at once takes the kernel instance whose waves keep
-    two blocks in flight (a ring of three fragments); a larger one takes the two-fragment loop.
-    Both update a wave's blocks in the same order, so a row gives the same bits in a 96-row batch
-    (two-fragment loop: 96 x 8 x 2..5 workgroups) and alone (ring): rows of one or more chunks with
-    partial tail blocks, rows of fewer blocks than the ring holds, a row of exactly one chunk and
-    an empty row; plain decode and the fused append + decode."""
+    two blocks in flight (a ring of three fragments; D <= 64 only: at D = 128 the third fragment
+    would spill, and small grids take the two-fragment loop too); a larger one takes the
+    two-fragment loop. Both update a wave's blocks in the same order, so a row gives the same bits
+    in a 96-row batch (two-fragment loop: 96 x 8 x 2..5 workgroups) and alone (ring at D = 64):
+    rows of one or more chunks with partial tail blocks, rows of fewer blocks than the ring holds,
+    a row of exactly one chunk and an empty row; plain decode and the fused append + decode."""
     rng = np.random.default_rng(61 + D)
     edge = [0, 1, 15, 16, 17, 40, 63, 65, 511, 512, 1023, 1024, 1025, 2047]
     n = np.concatenate([edge, rng.integers(1, 2048, 96 - len(edge))])
