@@ -149,21 +149,31 @@ def assert_attention_close(got, ref, dtype, what="out"):
     return float(d.max()), float(d.mean())
 
 
+def mq_wave_tokens(kv_lens):
+    """The most tokens one wave of the multi-query kernel accumulates: its 4 waves deal a row's
+    16-token blocks round-robin, so a wave takes at most ceil(blocks / 4) of the longest row's."""
+    n = int(np.max(kv_lens)) if len(kv_lens) else 0
+    return 16 * (-(-(-(-n // 16)) // 4))
+
+
 def check_rows(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale, what,
-               rows=None, q_shared=False, gather=None):
+               rows=None, q_shared=False, gather=None, wave_tokens=None):
     """Every row (or ``rows``) of a paged decode result against the oracle, gathered row by row
     through its block table: the acceptance tolerance over all compared elements, and the derived
     bound element by element. out (B, [n_q,] H_q, D), lse (B, [n_q,] H_q) from the GPU; q the
     queries the decode read (B, H_q, D) storage, or (n_q, H_q, D) when q_shared. ``gather(b)``,
     when given, returns row b's keys and values instead (a right-padded row's valid columns); the
     pools and block tables are then unused and kv_lens[b] is the row's valid-column count.
+    ``wave_tokens``: the most tokens one wave accumulates (default: a quarter of a 1024-token
+    split chunk; the multi-query kernel's 4 waves take a quarter of the whole row's blocks).
     Returns the record (max, mean, and the largest error / derived bound ratio)."""
     rows = range(len(kv_lens)) if rows is None else rows
     d_out, d_lse, ratio = [], [], 0.0
     # bf16 rows are decoded on the matrix cores, fp32 rows on the vector ALUs; a wave accumulates a
-    # quarter of a split chunk (1024 tokens)
+    # quarter of a split chunk (1024 tokens) unless the caller says otherwise
     mfma = dtype == "bf16"
-    wave_tokens = 1024 // 4
+    if wave_tokens is None:
+        wave_tokens = 1024 // 4
     for b in rows:
         if gather is not None:
             K, V = gather(b)
