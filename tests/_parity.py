@@ -211,6 +211,54 @@ def check_rows(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale,
     return rec
 
 
+def check_rows_block_sparse(out, lse, k_pool, v_pool, dtype, block_tables, kv_lens, q, scale,
+                            keep, what, q_shared=True, wave_tokens=None):
+    """A block-sparse multi-query result against the oracle under the derived bound: query block i
+    (queries 16 i .. 16 i + 15) of row b attends to the keys of the 16-token blocks j with
+    keep[b, i, j]; each block's result is the two-pass attention over exactly those keys, and its
+    bound is attention_bound over the same keys (the kernel visits only kept blocks, so a wave's
+    chain is at most that of the dense call). A query block with no kept key must give 0 and -inf
+    exactly. Also asserts the acceptance tolerance over all elements; returns the record."""
+    if wave_tokens is None:
+        wave_tokens = mq_wave_tokens(kv_lens)
+    mfma = dtype == "bf16"
+    d_out, d_lse, ratio, blocks = [], [], 0.0, 0
+    for b in range(len(kv_lens)):
+        n = int(kv_lens[b])
+        K, V = O.gather_paged(k_pool, v_pool, dtype, block_tables[b], n)
+        qb = O.storage_to_f64(q if q_shared else q[b], dtype)
+        go = np.asarray(out[b], dtype=np.float64)
+        gl = np.asarray(lse[b], dtype=np.float64)
+        for i in range(-(-qb.shape[0] // 16)):
+            rows = slice(16 * i, min(16 * i + 16, qb.shape[0]))
+            cols = [t for t in range(n) if keep[b, i, t // 16]]
+            if not cols:
+                assert np.all(go[rows] == 0) and np.all(np.isneginf(gl[rows])), \
+                    f"{what}: row {b} query block {i} keeps nothing"
+                continue
+            blocks += 1
+            o_ref, l_ref = O.attend_two_pass(qb[rows], K[cols], V[cols], scale)
+            bo, bl = attention_bound(qb[rows], K[cols], V[cols], scale, mfma=mfma,
+                                     wave_tokens=wave_tokens)
+            do, dl = _abs_diff(go[rows], o_ref), _abs_diff(gl[rows], l_ref)
+            d_out.append(do.ravel())
+            d_lse.append(dl.ravel())
+            ratio = max(ratio, float((do / bo).max()), float((dl / bl).max()))
+            assert np.all(do <= bo), (f"{what}: row {b} block {i} out error {do.max():.3e} beyond "
+                                      f"the derived fp32 bound")
+            assert np.all(dl <= bl), (f"{what}: row {b} block {i} lse error {dl.max():.3e} beyond "
+                                      f"the derived fp32 bound")
+    d_out, d_lse = np.concatenate(d_out), np.concatenate(d_lse)
+    max_tol, mean_tol = TOL[dtype]
+    rec = _record(what, d_out, ratio)
+    _record(what + " lse", d_lse)
+    log(f"[parity] {what}: {blocks} kept query blocks, max_err={rec['max']:.2e} "
+        f"mean_err={rec['mean']:.2e} max err/derived bound={ratio:.3f}")
+    assert d_out.max() <= max_tol and d_out.mean() <= mean_tol, f"{what}: beyond the tolerance"
+    assert d_lse.max() <= max_tol and d_lse.mean() <= mean_tol, f"{what} lse: beyond the tolerance"
+    return rec
+
+
 def oracle_append(case):
     cos = sin = None
     if case.rope_max_pos > 0:

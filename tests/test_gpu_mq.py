@@ -9,7 +9,8 @@ import workloads as W
 from paged_kv_cache_177_amd import binding as B
 from paged_kv_cache_177_amd.runner import MultiQueryStep, to_torch
 
-from _parity import assert_attention_close, check_rows, log, mq_wave_tokens
+from _parity import (assert_attention_close, check_rows, check_rows_block_sparse, log,
+                     mq_wave_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +135,8 @@ def test_mq_block_sparse_temporal_mask():
                                                shared_q=True)
     assert_attention_close(out, o_ref, "bf16", "sparse out")
     assert_attention_close(lse, l_ref, "bf16", "sparse lse")
+    check_rows_block_sparse(out, lse, c.k_pool, c.v_pool, "bf16", c.block_tables, c.kv_lens, c.q,
+                            c.scale, keep.astype(bool), "mq sparse temporal")
 
 
 @pytest.mark.parametrize("D,H_q,H_kv,n_q", [(32, 4, 4, 37), (64, 8, 2, 21), (128, 4, 4, 16)])
@@ -162,6 +165,8 @@ def test_mq_block_sparse_random_masks(D, H_q, H_kv, n_q):
                                                c.kv_lens, c.q, c.scale, keep, shared_q=True)
     assert_attention_close(out, o_ref, "bf16", "sparse out")
     assert_attention_close(lse, l_ref, "bf16", "sparse lse")
+    check_rows_block_sparse(out, lse, c.k_pool, c.v_pool, "bf16", c.block_tables, c.kv_lens, c.q,
+                            c.scale, keep, f"mq sparse random D={D}")
     assert np.all(out[3, :16] == 0) and np.all(np.isneginf(lse[3, :16]))
     # every tile kept: the dense multi-query call, bit for bit
     full = np.ones_like(keep)

@@ -10,7 +10,7 @@ import pytest
 import oracle as O
 import workloads as W
 
-from _parity import TOL, attention_bound, check_rows
+from _parity import TOL, attention_bound, check_rows, check_rows_block_sparse, mq_wave_tokens
 
 H_KV, G, D = 2, 4, 128
 
@@ -83,3 +83,50 @@ def test_bound_scales_with_the_arithmetic():
     V = rng.standard_normal((1, 1, D))
     bo, bl = attention_bound(q, K, V, 0.088)
     assert np.all(bo > 0) and np.all(bo <= 3e-4 * np.abs(V[0, 0]) + 1e-12)
+
+
+def test_block_sparse_check_accepts_the_oracle_and_rejects_a_dropped_block():
+    """The block-sparse helper (check_rows_block_sparse) on the CPU: the oracle's own fp32-rounded
+    result passes; a result in which one query block lost one of its kept key blocks fails; a
+    query block that keeps nothing must be exactly 0 / -inf."""
+    rng = np.random.default_rng(77)
+    kv, n_q, H_q, H_kv, Dh = [0, 100, 900], 40, 4, 2, 32
+    c = W.make_paged_case("sparse-pin", 77, [max(x - 1, 0) for x in kv], H_q, H_kv, Dh, "bf16")
+    # the step's token appended, so row b holds exactly kv[b] keys
+    kp, vp, _ = O.append_kv(c.k_pool, c.v_pool, "bf16", "paged", c.block_tables, c.positions,
+                            c.dest, c.k_new, c.v_new)
+    c.k_pool, c.v_pool, c.kv_lens = kp, vp, np.asarray(kv, np.int32)
+    q = W.to_storage(rng.standard_normal((n_q, H_q, Dh), dtype=np.float32), "bf16")
+    keep = rng.random((len(kv), 3, (max(kv) + 15) // 16 + 1)) < 0.5
+    keep[2, 1, :] = False  # a query block of the long row keeps nothing
+    o, l = O.decode_paged_block_sparse(c.k_pool, c.v_pool, "bf16", c.block_tables, c.kv_lens, q,
+                                       c.scale, keep, shared_q=True)
+    out, lse = o.astype(np.float32), l.astype(np.float32)
+    rec = check_rows_block_sparse(out, lse, c.k_pool, c.v_pool, "bf16", c.block_tables, c.kv_lens,
+                                  q, c.scale, keep, "sparse true")
+    assert rec["ratio"] < 0.05
+    # one kept key block of query block 0 of the long row dropped
+    j = int(np.flatnonzero(keep[2, 0, :(kv[2] + 15) // 16])[3])
+    keep_m = keep.copy()
+    keep_m[2, 0, j] = False
+    o_m, l_m = O.decode_paged_block_sparse(c.k_pool, c.v_pool, "bf16", c.block_tables, c.kv_lens,
+                                           q, c.scale, keep_m, shared_q=True)
+    with pytest.raises(AssertionError):
+        check_rows_block_sparse(o_m.astype(np.float32), l_m.astype(np.float32), c.k_pool,
+                                c.v_pool, "bf16", c.block_tables, c.kv_lens, q, c.scale, keep,
+                                "sparse dropped block")
+    # an empty query block that is not exactly 0 fails
+    out_z = out.copy()
+    out_z[2, 16, 0, 0] = 1e-30
+    with pytest.raises(AssertionError, match="keeps nothing"):
+        check_rows_block_sparse(out_z, lse, c.k_pool, c.v_pool, "bf16", c.block_tables, c.kv_lens,
+                                q, c.scale, keep, "sparse empty block")
+
+
+def test_mq_wave_tokens_counts_a_waves_blocks():
+    """4 waves deal a row's 16-token blocks round-robin: a wave takes ceil(blocks / 4) blocks."""
+    assert mq_wave_tokens(np.array([0])) == 0
+    assert mq_wave_tokens(np.array([1])) == 16
+    assert mq_wave_tokens(np.array([64])) == 16       # 4 blocks, one each
+    assert mq_wave_tokens(np.array([65])) == 32       # 5 blocks: one wave takes two
+    assert mq_wave_tokens(np.array([821, 17])) == 208  # 52 blocks of the longer row: 13 per wave
