@@ -185,9 +185,14 @@ struct Vec8<float> {
     a = make_float4(x.x, x.y, x.z, x.w);
     b = make_float4(y.x, y.y, y.z, y.w);
   }
+  // element-wise through native 4-float vectors: whole-struct float4 copies become memory copies
+  // that kept the fused append's pieces in scratch memory
   __device__ __forceinline__ void load_cached(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 x = reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 y = reinterpret_cast<const f32x4*>(p)[1];
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void to_f32(float* o) const {
@@ -198,8 +203,9 @@ struct Vec8<float> {
     b = make_float4(o[4], o[5], o[6], o[7]);
   }
   __device__ __forceinline__ void store(float* p) const {
-    reinterpret_cast<float4*>(p)[0] = a;
-    reinterpret_cast<float4*>(p)[1] = b;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    reinterpret_cast<f32x4*>(p)[0] = f32x4{a.x, a.y, a.z, a.w};
+    reinterpret_cast<f32x4*>(p)[1] = f32x4{b.x, b.y, b.z, b.w};
   }
   __device__ __forceinline__ float dot(const Vec8& o) const {
     float s0 = a.x * o.a.x;
