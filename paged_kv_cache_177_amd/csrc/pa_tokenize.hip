@@ -25,6 +25,9 @@
 //      embeddings are built.
 //   3. Lane l of an accumulator holds output columns 4 (l / 16) .. + 3 of token l % 16: rounded
 //      to bf16 they are 8 contiguous bytes of the token's slot [block][head][slot][dim].
+#include <map>
+#include <mutex>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -40,6 +43,11 @@ constexpr int kWaves = 8;
 constexpr int kMaxDm = 512;      // LDS holds X [kTok][kMaxDm + 8] bf16
 constexpr int kT = 4;            // tiles a wave carries through one pass over the inputs
 constexpr int kEmbedUnroll = 2;  // float4 pieces in flight per thread while embedding
+// With PRE (launches the device holds at once), a wave whose steps number at most kPre requests
+// all their weight fragments at the start, before the embedding, instead of two steps ahead: its
+// products then never wait on a load (the model width 256 gives 8 steps). That takes 254 VGPRs,
+// one workgroup per CU, so larger launches keep the two-step pipeline at two workgroups per CU.
+constexpr int kPre = 8;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -52,6 +60,7 @@ struct Step {
   u32x4_t w[kT];  // the kT tiles' weight fragments for one 32-input step
 };
 
+template <bool PRE>
 __global__ __launch_bounds__(64 * kWaves) void tokenize_kv_kernel(const TokenizeArgs a) {
   __shared__ int s_ids[kTok][3];
   __shared__ __attribute__((aligned(16))) unsigned short s_x[kTok][kMaxDm + 8];
@@ -105,7 +114,16 @@ __global__ __launch_bounds__(64 * kWaves) void tokenize_kv_kernel(const Tokenize
     }
   };
   Step sa, sb;
-  if (steps > 0) {
+  Step pre[PRE ? kPre : 1];
+  bool pre_all = false;  // uniform
+  if constexpr (PRE) {
+    pre_all = steps <= kPre;
+    if (pre_all) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) load_step(pre[j], j);
+    }
+  }
+  if (!pre_all && steps > 0) {
     load_step(sa, 0);
     load_step(sb, 1);
   }
@@ -214,6 +232,14 @@ __global__ __launch_bounds__(64 * kWaves) void tokenize_kv_kernel(const Tokenize
   };
   // two steps in flight: while one computes, the next is already on its way (the step count is
   // padded to even; the padding step is a dummy)
+  if constexpr (PRE) {
+    if (pre_all) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j)
+        if (j < steps) compute_step(pre[j], j);
+      return;
+    }
+  }
   const int steps2 = steps + (steps & 1);
   for (int j = 0; j < steps2; j += 2) {
     compute_step(sa, j);
@@ -246,10 +272,35 @@ __global__ __launch_bounds__(256) void pack_projection_kernel(const u32x4_t* __r
 
 int tokenize_max_model_dim() { return kMaxDm; }
 
+// Workgroups of the prefetching instance the current device holds at once (0 if unknown), cached
+// per device.
+static int resident_prefetching() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(tokenize_kv_kernel<true>), 64 * kWaves, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cache[dev] = per_cu * cus;
+  return per_cu * cus;
+}
+
 hipError_t launch_tokenize(const TokenizeArgs& a, hipStream_t stream) {
   if (a.batch <= 0 || a.max_events <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.max_events + kTok - 1) / kTok), (unsigned)a.batch);
-  hipLaunchKernelGGL(tokenize_kv_kernel, grid, dim3(64 * kWaves), 0, stream, a);
+  const long long wgs = (long long)grid.x * grid.y;
+  const int resident = resident_prefetching();
+  if (resident > 0 && wgs <= resident)
+    hipLaunchKernelGGL((tokenize_kv_kernel<true>), grid, dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tokenize_kv_kernel<false>), grid, dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

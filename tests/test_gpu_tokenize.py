@@ -139,3 +139,30 @@ def test_tokenize_shapes(model_dim, num_heads, head_dim):
     log(f"[tokenize] Dm={model_dim} H={num_heads} dh={head_dim} events={int(c.offsets[-1])}")
     pool = _run(c)
     _check(c, pool)
+
+
+def test_tokenize_launch_larger_than_the_device_holds():
+    """40 rows of ~800 events: about 560 workgroups, more than the device holds at once, so the
+    launch takes the instance that keeps two weight steps in flight (smaller launches request all
+    of a wave's steps up front). Its writes are held to the same bound, and the first three rows,
+    tokenized alone by the other instance into the same pool, get the same bits."""
+    import dataclasses
+
+    c = W.mq_tokenizer(seed=12, batch=40)
+    log(f"[tokenize] B={c.batch} events={int(c.offsets[-1])} (large launch)")
+    pool = _run(c)
+    _check(c, pool)
+    kg, vg = to_numpy(pool.k, "bf16"), to_numpy(pool.v, "bf16")
+    e3 = int(c.offsets[3])
+    small = dataclasses.replace(c, offsets=c.offsets[:4].copy(), neuron_ids=c.neuron_ids[:e3],
+                                time_bins=c.time_bins[:e3], value_ids=c.value_ids[:e3],
+                                block_tables=c.block_tables[:3].copy())
+    pool3 = _run(small)
+    k3, v3 = to_numpy(pool3.k, "bf16"), to_numpy(pool3.v, "bf16")
+    for b in range(3):
+        n = int(c.offsets[b + 1] - c.offsets[b])
+        for t in range(0, n, 16):
+            blk = c.block_tables[b][t // 16]
+            m = min(16, n - t)
+            np.testing.assert_array_equal(k3[blk, :, :m], kg[blk, :, :m], err_msg=f"row {b}")
+            np.testing.assert_array_equal(v3[blk, :, :m], vg[blk, :, :m], err_msg=f"row {b}")
