@@ -620,10 +620,15 @@ def b16_protocol_timing(plan, reps: int = 3):
                                         scale, out=out, query_workspace=True)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
 
+    # every step's views, sliced before the timed runs (slicing in the loop is host time that
+    # would pace the back-to-back steps)
+    views = [(bt_d[s], pos_d[s], k_all[s], v_all[s], q_all[s], len_d[s]) for s in range(steps)]
+
     def step(s):
-        B.pa_append_decode_attention(pool.pool, bt_d[s], stride, pos_d[s], None, k_all[s],
-                                     v_all[s], q_all[s], q_rot, H_q, len_d[s], 16, max_len, scale,
-                                     workspace=ws, out=out, lse=lse)
+        bt_s, pos_s, k_s, v_s, q_s, len_s = views[s]
+        B.pa_append_decode_attention(pool.pool, bt_s, stride, pos_s, None, k_s, v_s, q_s, q_rot,
+                                     H_q, len_s, 16, max_len, scale, workspace=ws, out=out,
+                                     lse=lse)
 
     def ev():
         e = torch.cuda.Event(enable_timing=True)
