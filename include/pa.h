@@ -164,7 +164,7 @@ pa_status pa_append_kv_qk_norm(const pa_pool* pool, const int32_t* block_tables,
  * Workspace: with workspace_needed != NULL the call only writes the bytes it needs for these
  * arguments there and launches nothing; otherwise workspace must hold that many bytes and be
  * 256-byte aligned (it may be NULL when none are needed). A workspace must be zero-filled before
- * its first use: it starts with counters that every call leaves at zero again, the work counter of
+ * its first use: it starts with counters that every call leaves at zero again, the work counters of
  * the split kernels (256 bytes) and one finished-split count per (row, query head) (4 * batch *
  * num_q_heads bytes, rounded up to 256), with the partial results after them. Calls may share a
  * workspace while batch * num_q_heads stays the same (their split counts may differ); after a

@@ -358,7 +358,7 @@ extern "C" pa_status pa_decode_attention(const pa_pool* pool, const void* q, int
 // library runs on its own copy, which lives until the process ends. In host code its name is only a
 // stand-in for the symbol, never a device address: the address is looked up once per device with
 // hipGetSymbolAddress (with that device current) and kept in g_scratch[device]. Layout: the
-// persistent kernel's work counter (256 bytes), a fixed reservation for the finished-split counts
+// work counters (256 bytes), a fixed reservation for the finished-split counts
 // (the same offsets for every batch, so calls of any size follow one another with no clearing),
 // then the partials. The counters must be zero before a call, and every completed call leaves them
 // at zero; they are cleared by a fill kernel on a device's first call and after a failed launch.

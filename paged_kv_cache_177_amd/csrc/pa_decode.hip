@@ -62,6 +62,11 @@
 #ifndef PA_DECODE_GRID_MERGE
 #define PA_DECODE_GRID_MERGE 1
 #endif
+// 1 = a bf16 split grid larger than the device holds hands out its last chunks by tickets (see
+// take_ticket); 0 = every chunk has a fixed workgroup.
+#ifndef PA_DECODE_TICKETS
+#define PA_DECODE_TICKETS 1
+#endif
 
 namespace pa {
 namespace {
@@ -73,6 +78,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;  // log2 units
 constexpr int kWaves = PA_DECODE_WAVES;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kTicketExtraRows = 32;  // ticketed grid rows beyond the chunks they share
 
 // ---- cross-lane helpers -----------------------------------------------------------------------
 template <int CTRL>
@@ -1167,6 +1173,27 @@ constexpr int grid_min_wg() {
   return sizeof(T) == 2 && G <= 4 && PA_DECODE_MIN_WG_PER_CU > 0 ? PA_DECODE_MIN_WG_PER_CU : 1;
 }
 
+// Ticket of a workgroup of the ticketed split grid (the workgroups of grid rows >= ticket_y): the
+// count of such workgroups that asked before it. The counter (bytes 8-15 of the workspace) holds
+// the tickets handed out in its low half and the workgroups that asked in its high half; every
+// ticketed workgroup asks exactly once, so the last to ask re-arms it to zero for the next call.
+// A workgroup on an XCD that runs ahead starts its ticketed workgroups sooner and so takes more of
+// the last chunks; the ones left on a slower XCD find none and exit.
+__device__ __forceinline__ int take_ticket(const DecodeArgs& a, int y) {
+  __shared__ int s_ticket;
+  if (threadIdx.x == 0) {
+    unsigned long long* ctr = reinterpret_cast<unsigned long long*>(a.counter) + 1;
+    const unsigned long long old = __hip_atomic_fetch_add(
+        ctr, (1ull << 32) | 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned asking = (gridDim.y - (unsigned)a.ticket_y) * gridDim.x;
+    if ((unsigned)(old >> 32) == asking - 1)
+      __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ticket = (int)(unsigned)old;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_ticket);
+}
+
 // RING = 3: the bf16 worker's three-fragment ring (run_blocks3), for split grids the device holds
 // at once.
 template <typename T, int D, int G, bool PADDED, bool COMPACT, int RING = 2>
@@ -1212,12 +1239,28 @@ __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vec
     gap_shift = __builtin_amdgcn_readlane(gsh_l, row);
     split = full ? k - (__builtin_amdgcn_readlane(fi, row) - __builtin_amdgcn_readlane(f, row))
                  : n / chunk;
-  } else {
+  } else if (a.ticket_y == 0) {
     g = blockIdx.x;
     row = blockIdx.y;
     // the highest splits go first: they exist only for the longest rows, so the launch ends with
     // the splits every row has (a shorter drain than ending on long rows' late full chunks)
     split = (int)gridDim.z - 1 - (int)blockIdx.z;
+  } else {
+    // ticketed grid: grid rows y < ticket_y hold the same fixed chunks, in the same order, as the
+    // plain grid's (y = row + batch * (s_max - 1 - split)); past them, each workgroup takes the
+    // next of the remaining split-0 chunks from a counter, or exits when none is left
+    const int y = (int)blockIdx.y;
+    if (y < a.ticket_y) {
+      g = blockIdx.x;
+      row = y % a.batch;
+      split = a.s_max - 1 - y / a.batch;
+    } else {
+      const int c = take_ticket(a, y) + (a.ticket_y - a.batch * (a.s_max - 1)) * a.H_kv;
+      if (c >= a.batch * a.H_kv) return;
+      row = c / a.H_kv;
+      g = c - row * a.H_kv;
+      split = 0;
+    }
   }
   // issued before the row length is known, so their latency overlaps the length load
   int ids = w.load_ids(row, split * chunk);
@@ -1774,6 +1817,16 @@ hipError_t launch_layout(const DecodeArgs& args, hipStream_t stream, bool* merge
     const int resident = resident_workgroups(reinterpret_cast<const void*>(ring), ring_pad);
     if (resident > 0 && items <= resident) {
       hipLaunchKernelGGL(ring, grid, dim3(64 * kWaves), ring_pad, stream, a);
+      return hipGetLastError();
+    }
+    // A grid larger than the device holds ends with a drain whose length differs between the
+    // XCDs (each runs the workgroups the dispatcher hands it in turn). The last 3/8 of the split-0
+    // chunks are therefore handed out by tickets, to kTicketExtraRows more grid rows than they
+    // need: an XCD that runs ahead takes more of them. Same chunks, same bits.
+    const long long rows = (long long)a.batch * a.s_max + kTicketExtraRows;
+    if (PA_DECODE_TICKETS && a.s_max > 1 && a.counter != nullptr && rows <= 65535) {
+      a.ticket_y = a.batch * (a.s_max - 1) + a.batch * 5 / 8;
+      hipLaunchKernelGGL(kern, dim3(a.H_kv, (unsigned)rows), dim3(64 * kWaves), pad, stream, a);
       return hipGetLastError();
     }
     hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), pad, stream, a);

@@ -81,6 +81,7 @@ struct DecodeArgs {
   int* counter;     // work counter of the persistent decode kernel (0 between calls), or NULL
   int* merge_counts;  // [batch][H_kv] finished splits per (row, KV head) when the split grid
                      // merges its own partials (0 between calls), else NULL
+  int ticket_y;     // split grid: first grid row whose workgroups take tickets (0: a plain grid)
   int mq_tiles;     // multi-query path: 16-row query tiles per (row, KV head)
   // block-sparse multi-query path: keep flags [batch][ceil(n_q / 16)][mask_kv_blocks], or NULL
   const uint8_t* block_mask;
@@ -105,13 +106,14 @@ struct DecodeArgs {
 };
 
 // Workspace of a decode call (0 bytes when no row can split):
-//   [256 B: work counter (int) of the persistent kernel; must be 0 before the first call, each call
-//    leaves it 0] [split partial outputs, fp32] [split partial log-sum-exps, fp32]
+//   [256 B: work counters, 0 before the first call, each call leaves them 0: bytes 0-3 the
+//    persistent kernel's, bytes 8-15 the ticketed split grid's] [split partial outputs, fp32]
+//   [split partial log-sum-exps, fp32]
 constexpr size_t kCounterBytes = 256;
-// Workspace of a decode with splits, in this order: the persistent kernel's work counter (256
-// bytes), one finished-split count per (row, query head) (a bound of the split grid's per (row,
-// KV head) counts, 256-byte rounded; reserved for every call so that partials never land there),
-// the partial outputs and their log-sum-exp. The counters lead, at offsets that depend on batch x
+// Workspace of a decode with splits, in this order: the work counters (256 bytes), one
+// finished-split count per (row, query head) (a bound of the split grid's per (row, KV head)
+// counts, 256-byte rounded; reserved for every call so that partials never land there), the
+// partial outputs and their log-sum-exp. The counters lead, at offsets that depend on batch x
 // H_q only, so calls of other split counts can share a workspace: every call leaves them at zero.
 inline size_t merge_count_bytes(int batch, int H_q) {
   return ((size_t)batch * (size_t)H_q * sizeof(int) + 255) & ~(size_t)255;

@@ -242,7 +242,9 @@ def test_compact_grid_at_its_64_row_limit():
 
 def test_grid_merge_repeated_calls_and_shared_workspace():
     """The split grid merges a (row, KV head)'s splits in its own launch, through finished-split
-    counts in the workspace that every call leaves at zero. 40 calls in a row give the same bits;
+    counts in the workspace that every call leaves at zero; at this size (9,216 workgroups, more
+    than the device holds) it also hands out its last split-0 chunks by tickets, from a counter
+    the last ticketed workgroup re-arms. 40 calls in a row give the same bits;
     two batches of other split counts (same rows and heads) that take turns on one workspace give
     the bits of fresh workspaces; the first call agrees with the oracle."""
     rng = np.random.default_rng(90)
