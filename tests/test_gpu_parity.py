@@ -240,6 +240,38 @@ def test_compact_grid_at_its_64_row_limit():
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+@pytest.mark.parametrize("H_q,H_kv,D", [(8, 1, 64), (16, 2, 128), (16, 4, 32)])
+def test_ticketed_grid_head_layouts(H_q, H_kv, D):
+    """A bf16 split grid larger than the device holds (here at least 2,000 workgroups, against at
+    most 3 per CU of 256 CUs) hands out the last 3/8 of its split-0 chunks by tickets, with spare
+    grid rows. Head layouts other than B128's (one, two and four KV heads; D = 64, 128, 32) with
+    edge lengths: every row against the oracle; three more calls on the same workspace give the
+    same bits (the ticket counter re-arms after each call); rows decoded alone (a grid the device
+    holds, without tickets) give the same bits as in the batch."""
+    seed = 300 + D + H_kv
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 15, 16, 1023, 1024, 1025, 2048, 5999]
+    n_rows = 2000 // (H_kv * 6) + 1
+    n = np.concatenate([edge, rng.integers(0, 6000, n_rows - len(edge))])
+    case = W.make_paged_case(f"ticketed-{H_q}-{H_kv}-{D}", seed, n, H_q, H_kv, D, "bf16")
+    assert case.batch * H_kv * 6 >= 2000
+    r, _, _ = run_and_check_paged(case, check_pool=False)
+    out, lse = r.out.clone(), r.lse.clone()
+    for _ in range(3):
+        r.out.zero_()
+        r.lse.zero_()
+        r.decode()
+        torch.cuda.synchronize()
+        assert torch.equal(r.out, out) and torch.equal(r.lse, lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in list(range(len(edge))) + [n_rows - 1]:
+        rb = PagedStep(_single_row(case, b))
+        rb.step()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out[b], err_msg=f"row {b}")
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse[b], err_msg=f"row {b}")
+
+
 def test_grid_merge_repeated_calls_and_shared_workspace():
     """The split grid merges a (row, KV head)'s splits in its own launch, through finished-split
     counts in the workspace that every call leaves at zero; at this size (9,216 workgroups, more
