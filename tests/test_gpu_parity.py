@@ -246,14 +246,16 @@ def test_ticketed_grid_head_layouts(H_q, H_kv, D):
     most 3 per CU of 256 CUs) hands out the last 3/8 of its split-0 chunks by tickets, with spare
     grid rows. Head layouts other than B128's (one, two and four KV heads; D = 64, 128, 32) with
     edge lengths: every row against the oracle; three more calls on the same workspace give the
-    same bits (the ticket counter re-arms after each call); rows decoded alone (a grid the device
-    holds, without tickets) give the same bits as in the batch."""
+    same bits (the ticket counter re-arms after each call), and so does the fused append + decode
+    (in one-chunk rows the ticketed workgroup of split 0 stores the new token); rows decoded alone
+    (a grid the device holds, without tickets) give the same bits as in the batch."""
     seed = 300 + D + H_kv
     rng = np.random.default_rng(seed)
     edge = [0, 1, 15, 16, 1023, 1024, 1025, 2048, 5999]
     n_rows = 2000 // (H_kv * 6) + 1
     n = np.concatenate([edge, rng.integers(0, 6000, n_rows - len(edge))])
-    case = W.make_paged_case(f"ticketed-{H_q}-{H_kv}-{D}", seed, n, H_q, H_kv, D, "bf16")
+    case = W.make_paged_case(f"ticketed-{H_q}-{H_kv}-{D}", seed, n, H_q, H_kv, D, "bf16",
+                             rope_theta=1e4)
     assert case.batch * H_kv * 6 >= 2000
     r, _, _ = run_and_check_paged(case, check_pool=False)
     out, lse = r.out.clone(), r.lse.clone()
@@ -263,6 +265,17 @@ def test_ticketed_grid_head_layouts(H_q, H_kv, D):
         r.decode()
         torch.cuda.synchronize()
         assert torch.equal(r.out, out) and torch.equal(r.lse, lse)
+    # bit patterns: the pool's unused slots hold NaN poison
+    k_bits, v_bits = r.kv.k.view(torch.int16).clone(), r.kv.v.view(torch.int16).clone()
+    q_bits = r.q_rot.clone()
+    r.out.zero_()
+    r.q_rot.zero_()
+    r.fused_step()  # the same tokens to the same slots, the queries rotated in registers
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, out) and torch.equal(r.lse, lse)
+    assert torch.equal(r.kv.k.view(torch.int16), k_bits)
+    assert torch.equal(r.kv.v.view(torch.int16), v_bits)
+    assert torch.equal(r.q_rot, q_bits)  # stored by the workgroups of split 0
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     for b in list(range(len(edge))) + [n_rows - 1]:
         rb = PagedStep(_single_row(case, b))
