@@ -1789,13 +1789,18 @@ hipError_t launch_layout(const DecodeArgs& args, hipStream_t stream, bool* merge
                        dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
   }
-  if (decode_vector_is_persistent(a)) {
-    auto kern = decode_persistent_kernel<T, D, G, PADDED>;
-    const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
-    if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits)) {
-      const int grid = (int)(items < resident ? items : resident);
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), 0, stream, a);
-      return hipGetLastError();
+  // fp32 at D = 128, G = 8: the persistent kernel's chunk loop does not fit in 256 registers and
+  // would spill (80-104 bytes per lane), so that instance is not built and its rows take the split
+  // grid below, which cuts the same chunks
+  if constexpr (!(sizeof(T) == 4 && D == 128 && G == 8)) {
+    if (decode_vector_is_persistent(a)) {
+      auto kern = decode_persistent_kernel<T, D, G, PADDED>;
+      const int resident = resident_workgroups(reinterpret_cast<const void*>(kern), 0);
+      if (resident > 0 && (PA_DECODE_PERSISTENT == 2 || a.s_max >= kPersistentMinSplits)) {
+        const int grid = (int)(items < resident ? items : resident);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+        return hipGetLastError();
+      }
     }
   }
   if (PA_DECODE_GRID_MERGE && args.merge_counts != nullptr && a.s_max > 1 &&

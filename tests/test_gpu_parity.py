@@ -218,6 +218,27 @@ def test_wide_batch_with_long_rows_runs_the_persistent_kernel(D):
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+def test_fp32_d128_g8_wide_batch_with_long_rows():
+    """fp32 at D = 128 with groups of 8 query heads, more than 64 rows and long ones: the launch
+    the other instances give to the persistent kernel. That instance would spill, so these rows
+    take the split grid (merged by lse_reduce_kernel past 16 splits), with the same chunks: every
+    row against the oracle, and rows decoded alone (the compact grid for the long ones) give the
+    same bits."""
+    chunk = 1024
+    rng = np.random.default_rng(77)
+    n = np.concatenate([[20 * chunk + 3, 17 * chunk], rng.integers(0, 400, 68)])
+    case = W.make_paged_case("wide-long-f32-D128-G8", 78, n, 16, 2, 128, "f32")
+    r, _, _ = run_and_check_paged(case)
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    for b in [0, 1, 5]:
+        rb = PagedStep(_single_row(case, b))
+        rb.kv = r.kv
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b])
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
+
+
 def test_compact_grid_at_its_64_row_limit():
     """Exactly 64 rows with long ones on the first and the last lane of the row scan, lengths on
     and next to chunk multiples, and empty rows: the compact grid's widest batch. The oracle checks
