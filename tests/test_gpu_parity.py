@@ -239,6 +239,30 @@ def test_fp32_d128_g8_wide_batch_with_long_rows():
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b])
 
 
+@pytest.mark.parametrize("wide", [False, True])
+def test_rows_of_the_longest_lengths(wide):
+    """The longest rows: 131 073 tokens (the top of the long-context length range, 129 chunks) and
+    300 000 tokens (293 chunks: past 256, where the merge gives each of its 8 waves ceil(ns / 8)
+    splits), with a 6-token row; as a 3-row batch (the compact grid) or with 63 more short rows
+    (66 rows: the persistent kernel). Every row against the oracle; the long rows decoded alone
+    give the same bits."""
+    rng = np.random.default_rng(90 + wide)
+    n = [131072, 299999, 5]
+    if wide:
+        n = n + list(rng.integers(0, 300, 63))
+    case = W.make_paged_case(f"longest-{'wide' if wide else 'compact'}", 91 + wide, n, 8, 2, 64,
+                             "bf16")
+    r, _, _ = run_and_check_paged(case, check_pool=False)
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    for b in [0, 1]:
+        rb = PagedStep(_single_row(case, b))
+        rb.kv = r.kv
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b], err_msg=f"row {b}")
+        np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b], err_msg=f"row {b}")
+
+
 def test_compact_grid_at_its_64_row_limit():
     """Exactly 64 rows with long ones on the first and the last lane of the row scan, lengths on
     and next to chunk multiples, and empty rows: the compact grid's widest batch. The oracle checks
