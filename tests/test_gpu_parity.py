@@ -138,13 +138,17 @@ def test_sharp_softmax_and_large_scores():
     run_and_check_paged(case)
 
 
-def _single_row(c, b):
+def _row_range(c, lo, hi):
     return W.PagedCase(**{**c.__dict__,
-                          "n_ctx": c.n_ctx[b:b + 1], "positions": c.positions[b:b + 1],
-                          "dest": c.dest[b:b + 1], "kv_lens": c.kv_lens[b:b + 1],
-                          "block_tables": c.block_tables[b:b + 1],
-                          "k_new": c.k_new[b:b + 1], "v_new": c.v_new[b:b + 1],
-                          "q": c.q[b:b + 1]})
+                          "n_ctx": c.n_ctx[lo:hi], "positions": c.positions[lo:hi],
+                          "dest": c.dest[lo:hi], "kv_lens": c.kv_lens[lo:hi],
+                          "block_tables": c.block_tables[lo:hi],
+                          "k_new": c.k_new[lo:hi], "v_new": c.v_new[lo:hi],
+                          "q": c.q[lo:hi]})
+
+
+def _single_row(c, b):
+    return _row_range(c, b, b + 1)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -261,6 +265,33 @@ def test_rows_of_the_longest_lengths(wide):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(rb.out.cpu().numpy()[0], out_b[b], err_msg=f"row {b}")
         np.testing.assert_array_equal(rb.lse.cpu().numpy()[0], lse_b[b], err_msg=f"row {b}")
+
+
+@pytest.mark.parametrize("batch,n_long", [(65535, 0), (16384, 8)])
+def test_largest_batches(batch, n_long):
+    """The largest batches: 65 535 rows of 1..41 tokens (the most rows a call takes: they go to a
+    grid dimension), and 16 384 such rows with 8 of 3 000..4 000 tokens (4 chunks), where the
+    ticketed grid would need more than 65 535 grid rows and the plain split grid runs. Sampled rows
+    (every 61st, the first and last, and the long ones) against the oracle; every row's bits equal
+    those of the same row decoded in a batch a quarter the size."""
+    rng = np.random.default_rng(95)
+    n = rng.integers(0, 41, batch)
+    long_rows = rng.choice(batch, n_long, replace=False) if n_long else np.array([], int)
+    n[long_rows] = rng.integers(3000, 4000, n_long)
+    case = W.make_paged_case(f"largest-{batch}", 96, n, 4, 1, 32, "bf16")
+    sample = sorted(set(range(0, batch, 61)) | {batch - 1} | set(long_rows.tolist()))
+    r, _, _ = run_and_check_paged(case, rows=sample, check_pool=False)
+    out_b, lse_b = r.out.cpu().numpy(), r.lse.cpu().numpy()
+    q = (batch + 3) // 4
+    for lo in range(0, batch, q):
+        hi = min(lo + q, batch)
+        rb = PagedStep(_row_range(case, lo, hi))
+        rb.kv = r.kv  # the already-appended pool
+        rb.decode()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rb.out.cpu().numpy(), out_b[lo:hi], err_msg=f"rows {lo}..")
+        np.testing.assert_array_equal(rb.lse.cpu().numpy(), lse_b[lo:hi], err_msg=f"rows {lo}..")
+        del rb
 
 
 def test_compact_grid_at_its_64_row_limit():
