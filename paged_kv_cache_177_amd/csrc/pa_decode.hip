@@ -1177,9 +1177,9 @@ constexpr int grid_min_wg() {
 // count of such workgroups that asked before it. The counter (bytes 8-15 of the workspace) holds
 // the tickets handed out in its low half and the workgroups that asked in its high half; every
 // ticketed workgroup asks exactly once, so the last to ask re-arms it to zero for the next call.
-// A workgroup on an XCD that runs ahead starts its ticketed workgroups sooner and so takes more of
-// the last chunks; the ones left on a slower XCD find none and exit.
-__device__ __forceinline__ int take_ticket(const DecodeArgs& a, int y) {
+// An XCD that runs ahead starts its ticketed workgroups sooner and so takes more of the last
+// chunks; the ticketed workgroups left on a slower XCD find none and exit.
+__device__ __forceinline__ int take_ticket(const DecodeArgs& a) {
   __shared__ int s_ticket;
   if (threadIdx.x == 0) {
     unsigned long long* ctr = reinterpret_cast<unsigned long long*>(a.counter) + 1;
@@ -1255,7 +1255,7 @@ __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vec
       row = y % a.batch;
       split = a.s_max - 1 - y / a.batch;
     } else {
-      const int c = take_ticket(a, y) + (a.ticket_y - a.batch * (a.s_max - 1)) * a.H_kv;
+      const int c = take_ticket(a) + (a.ticket_y - a.batch * (a.s_max - 1)) * a.H_kv;
       if (c >= a.batch * a.H_kv) return;
       row = c / a.H_kv;
       g = c - row * a.H_kv;
