@@ -387,7 +387,9 @@ struct Worker {
   // The new token's index t (dest, or positions when dest is NULL) clamped as the append kernel
   // clamps it: into the row's block table (paged) or the row's columns (padded).
   __device__ __forceinline__ int fused_index(int row) const {
-    const int t = a.dest != nullptr ? a.dest[row] : a.positions[row];
+    return fused_clamp(a.dest != nullptr ? a.dest[row] : a.positions[row]);
+  }
+  __device__ __forceinline__ int fused_clamp(int t) const {
     return PADDED ? clampi(t, 0, a.seq_cap - 1) : clampi(t, 0, a.bt_stride * kBlock - 1);
   }
 
@@ -1025,25 +1027,36 @@ struct DecodeWorker<__bf16, D, G, PADDED> {
                                   Worker<__bf16, D, G, PADDED>>;
 };
 
-// Valid tokens of a row (and, padded, its gap start and width), lengths clamped to the bounds.
+// Valid tokens of a row (and, padded, its gap start and width), lengths clamped to the bounds,
+// from the row's loaded values: l0 = gap_start[row] and l1 = gap_end[row] (padded), or l0 =
+// kv_lens[row] (positions[row] for a lockstep step; l1 unused).
 template <bool PADDED>
-__device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_s, int* gap_shift) {
+__device__ __forceinline__ int row_valid_raw(const DecodeArgs& a, int l0, int l1, int* gap_s,
+                                             int* gap_shift) {
   if constexpr (PADDED) {
     const int cols = a.kv_cols;
-    const int gs = clampi(a.gap_start[row], 0, cols);
-    const int ge = clampi(a.gap_end[row], gs, cols);
+    const int gs = clampi(l0, 0, cols);
+    const int ge = clampi(l1, gs, cols);
     *gap_s = gs;
     *gap_shift = ge - gs;
     return cols - (ge - gs);
   } else {
     *gap_s = 0;
     *gap_shift = 0;
-    if (a.kv_from_positions) {  // kv_len = position + 1
-      const int p = a.positions[row];
-      return p < 0 ? 0 : (p >= a.max_kv_len ? a.max_kv_len : p + 1);
-    }
-    return clampi(a.kv_lens[row], 0, a.max_kv_len);
+    if (a.kv_from_positions)  // kv_len = position + 1
+      return l0 < 0 ? 0 : (l0 >= a.max_kv_len ? a.max_kv_len : l0 + 1);
+    return clampi(l0, 0, a.max_kv_len);
   }
+}
+
+// The same, loading the row's values.
+template <bool PADDED>
+__device__ __forceinline__ int row_valid(const DecodeArgs& a, int row, int* gap_s, int* gap_shift) {
+  if constexpr (PADDED)
+    return row_valid_raw<true>(a, a.gap_start[row], a.gap_end[row], gap_s, gap_shift);
+  else
+    return row_valid_raw<false>(a, a.kv_from_positions ? a.positions[row] : a.kv_lens[row], 0,
+                                gap_s, gap_shift);
 }
 
 // Lockstep step: the row's position for the next step, written once per row (by the workgroup of
@@ -1265,13 +1278,32 @@ __global__ __launch_bounds__(64 * kWaves, (grid_min_wg<T, G>())) void decode_vec
   // issued before the row length is known, so their latency overlaps the length load
   int ids = w.load_ids(row, split * chunk);
   w.load_queries(row, g);
-  // fused append: the row's position (a table row, clamped) for the rotations, and where its new
-  // token goes
+  // The row's scalars: its length (or gap) and, for the fused append, its position (a table row,
+  // clamped) for the rotations and where its new token goes. They are loaded together, with no
+  // branch between the loads (one a call does not need re-reads the length), so one wait covers
+  // them; behind a branch, each had waited for every load issued before it.
   const bool fused = a.k_new != nullptr;
-  const int pos = fused && a.cos != nullptr ? clampi(a.positions[row], 0, a.rope_max_pos - 1) : 0;
-  const int t_new = fused ? w.fused_index(row) : 0;
+  const int32_t* lp = PADDED ? a.gap_start : (a.kv_from_positions ? a.positions : a.kv_lens);
+  const int32_t* ep = PADDED ? a.gap_end : lp;
+  const int32_t* tp = fused ? (a.dest != nullptr ? a.dest : a.positions) : lp;
+  const int32_t* pp = fused && a.cos != nullptr ? a.positions : lp;
+  // The pointers are opaque to the compiler, which would otherwise turn a load it can prove equal
+  // to another back into a branch around a load; the four values then pass through one empty asm
+  // before any is used, so they are loaded together (left to itself, the compiler waits for the
+  // length alone, for the early exit below, and issues the others after it: a second round trip)
+  asm("" : "+s"(lp), "+s"(ep), "+s"(tp), "+s"(pp));
+  typedef const __attribute__((address_space(1))) int32_t gint;
+  int v_l0 = ((gint*)lp)[row], v_l1 = ((gint*)ep)[row];
+  int v_t = ((gint*)tp)[row], v_p = ((gint*)pp)[row];
+  asm volatile("" : "+v"(v_l0), "+v"(v_l1), "+v"(v_t), "+v"(v_p));
+  const int l0 = __builtin_amdgcn_readfirstlane(v_l0);
+  const int l1 = __builtin_amdgcn_readfirstlane(v_l1);
+  const int t_raw = __builtin_amdgcn_readfirstlane(v_t);
+  const int p_raw = __builtin_amdgcn_readfirstlane(v_p);
+  const int pos = fused && a.cos != nullptr ? clampi(p_raw, 0, a.rope_max_pos - 1) : 0;
+  const int t_new = fused ? w.fused_clamp(t_raw) : 0;
   Vec8<T> kx, kp, vx;
-  if constexpr (!COMPACT) n = row_valid<PADDED>(a, row, &gap_s, &gap_shift);
+  if constexpr (!COMPACT) n = row_valid_raw<PADDED>(a, l0, l1, &gap_s, &gap_shift);
   const Chunk ch = make_chunk(row, g, split, n, gap_s, gap_shift, chunk);
   if (split >= ch.ns) return;
   advance_position(a, ch);
